@@ -1,0 +1,186 @@
+"""fp64 CPU oracle for the exact attention forward pass.
+
+TEST INFRASTRUCTURE. Only the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package. The product path (the
+HIP library and its Python binding) never imports, links or falls back to it, and
+the two share no code.
+
+The arithmetic lives in ``attn_oracle.c`` (plain C, OpenMP over query rows, IEEE
+double, no fast-math); this module compiles it with gcc when the shared object is
+missing or older than the source, and marshals numpy arrays through ctypes.
+
+What it computes is standard attention written out as a definition -- scores
+S = scale * Q K^T, O = softmax(S) V -- following the section "The quadratic
+bottleneck in standard attention" of the page "FlashAttention: The Algorithm That
+Made Long-Context AI Possible". The tiled method reaches the same result exactly in
+real arithmetic (abstract of "FlashAttention: Fast and Memory-Efficient Exact
+Attention with IO-Awareness"), so no tiling or online softmax appears here.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_SO = os.path.join(_HERE, "liboracle.so")
+_LOCK = threading.Lock()
+_LIB = None
+
+DTYPE_CODES = {"f16": 0, "bf16": 1, "e4m3": 2}
+
+
+def build(force: bool = False) -> str:
+    """Compile attn_oracle.c into liboracle.so with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+        tmp = _SO + f".tmp{os.getpid()}"
+        subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99", "-Wall",
+                        "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def load(path: str):
+    """Load a compiled oracle shared object and declare its C signatures."""
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    i64p = ctypes.POINTER(ctypes.c_int64)
+    lib.oracle_decode.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_double, dp]
+    lib.oracle_decode.restype = ctypes.c_int
+    lib.oracle_attn_fwd_f64.argtypes = [dp, dp, dp, dp, dp] + [ctypes.c_int] * 6 + [ctypes.c_double]
+    lib.oracle_attn_fwd_f64.restype = ctypes.c_int
+    lib.oracle_attn_rows_f64.argtypes = ([dp, ctypes.c_int, dp, dp] + [ctypes.c_int] * 6 +
+                                         [ctypes.c_double, ctypes.c_int64, i64p, dp, dp])
+    lib.oracle_attn_rows_f64.restype = ctypes.c_int
+    lib.oracle_attn_probs_f64.argtypes = ([dp, dp] + [ctypes.c_int] * 6 + [ctypes.c_double] +
+                                          [ctypes.c_int, ctypes.c_int, dp])
+    lib.oracle_attn_probs_f64.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
+    return lib
+
+
+def _lib():
+    global _LIB
+    with _LOCK:
+        if _LIB is None:
+            _LIB = load(build())
+    return _LIB
+
+
+def _dptr(a: np.ndarray):
+    assert a.dtype == np.float64 and a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle uses (OMP_NUM_THREADS, else all available)."""
+    return int(_lib().oracle_num_threads())
+
+
+def decode(raw: np.ndarray, dtype: str, mult: float = 1.0) -> np.ndarray:
+    """Exact fp64 value of every stored element (bit patterns: uint16 for f16/bf16,
+    uint8 for e4m3), multiplied by `mult` (the tensor's descale for e4m3)."""
+    want = np.uint8 if dtype == "e4m3" else np.uint16
+    raw = np.ascontiguousarray(raw)
+    if raw.dtype != want:
+        raise TypeError(f"{dtype} expects {want} bit patterns, got {raw.dtype}")
+    out = np.empty(raw.shape, dtype=np.float64)
+    rc = _lib().oracle_decode(DTYPE_CODES[dtype], raw.ctypes.data, raw.size, float(mult), _dptr(out))
+    if rc:
+        raise ValueError("oracle_decode rejected its arguments")
+    return out
+
+
+def _shape(q: np.ndarray, k: np.ndarray, v: np.ndarray):
+    if q.ndim != 4 or k.ndim != 4 or k.shape != v.shape:
+        raise ValueError("q is [B,N,H,d]; k and v are [B,N,Hkv,d]")
+    B, N, H, d = q.shape
+    if k.shape[0] != B or k.shape[1] != N or k.shape[3] != d:
+        raise ValueError("k/v shape does not match q")
+    return B, N, H, k.shape[2], d
+
+
+def attn_fwd_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: float):
+    """Attention forward on fp64 inputs. q [B,N,H,d], k/v [B,N,Hkv,d].
+    Returns (o [B,N,H,d] float64, lse [B,H,N] float64)."""
+    q, k, v = (np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v))
+    B, N, H, Hkv, d = _shape(q, k, v)
+    o = np.empty_like(q)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    rc = _lib().oracle_attn_fwd_f64(_dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(lse),
+                                    B, H, Hkv, N, d, int(bool(causal)), float(scale))
+    if rc:
+        raise ValueError(f"oracle_attn_fwd_f64 failed ({rc})")
+    return o, lse
+
+
+def attn_rows_f64(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, H: int, rows: np.ndarray,
+                  causal: bool, scale: float):
+    """Selected query rows only. q_rows [R,d] are the fp64 query vectors of the rows
+    rows[r] = (b, h, i); k/v [B,N,Hkv,d]. Returns (o_rows [R,d], lse_rows [R])."""
+    q_rows = np.ascontiguousarray(q_rows, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+    B, N, Hkv, d = k.shape
+    R = rows.shape[0]
+    if q_rows.shape != (R, d):
+        raise ValueError("q_rows must be [len(rows), d]")
+    o = np.empty((R, d), dtype=np.float64)
+    lse = np.empty((R,), dtype=np.float64)
+    rc = _lib().oracle_attn_rows_f64(_dptr(q_rows), 1, _dptr(k), _dptr(v), B, H, Hkv, N, d,
+                                     int(bool(causal)), float(scale), R,
+                                     rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                     _dptr(o), _dptr(lse))
+    if rc:
+        raise ValueError(f"oracle_attn_rows_f64 failed ({rc})")
+    return o, lse
+
+
+def attn_probs_f64(q: np.ndarray, k: np.ndarray, b: int, h: int, causal: bool, scale: float):
+    """Softmax probability matrix [N,N] of one (b, h); zeros where masked. Small N only."""
+    q = np.ascontiguousarray(q, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    B, N, H, d = q.shape
+    Hkv = k.shape[2]
+    p = np.empty((N, N), dtype=np.float64)
+    rc = _lib().oracle_attn_probs_f64(_dptr(q), _dptr(k), B, H, Hkv, N, d, int(bool(causal)),
+                                      float(scale), int(b), int(h), _dptr(p))
+    if rc:
+        raise ValueError(f"oracle_attn_probs_f64 failed ({rc})")
+    return p
+
+
+def attn_fwd(q_raw: np.ndarray, k_raw: np.ndarray, v_raw: np.ndarray, dtype: str, causal: bool,
+             scale: float, descale=None):
+    """Attention forward on the stored inputs exactly as handed to the GPU library:
+    bit patterns of dtype `dtype` ("f16", "bf16" or "e4m3"); for e4m3, `descale` is the
+    (q, k, v) per-tensor factors that multiply the decoded elements."""
+    if dtype == "e4m3":
+        if descale is None or len(descale) != 3:
+            raise ValueError("e4m3 needs three descale factors")
+        dq, dk, dv = (float(x) for x in descale)
+    else:
+        dq = dk = dv = 1.0
+    return attn_fwd_f64(decode(q_raw, dtype, dq), decode(k_raw, dtype, dk), decode(v_raw, dtype, dv),
+                        causal, scale)
+
+
+def attn_rows(q_raw: np.ndarray, k_raw: np.ndarray, v_raw: np.ndarray, dtype: str, causal: bool,
+              scale: float, rows: np.ndarray, descale=None):
+    """Selected rows (b, h, i) of the forward on stored inputs, decoding only the query
+    rows it needs. Returns (o_rows [R,d], lse_rows [R])."""
+    if dtype == "e4m3":
+        dq, dk, dv = (float(x) for x in descale)
+    else:
+        dq = dk = dv = 1.0
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+    B, N, H, d = q_raw.shape
+    q_sel = q_raw[rows[:, 0], rows[:, 2], rows[:, 1], :]
+    return attn_rows_f64(decode(q_sel, dtype, dq), decode(k_raw, dtype, dk), decode(v_raw, dtype, dv),
+                         H, rows, causal, scale)

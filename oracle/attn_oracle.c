@@ -1,0 +1,223 @@
+/*
+ * attn_oracle.c -- plain, slow, fp64 CPU oracle for the exact attention forward pass.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg may load or call this file. The product path (the HIP library)
+ * never links, imports or falls back to it, and this file shares no code, header,
+ * table or helper with that library.
+ *
+ * What it computes. Standard attention as written out on the page "FlashAttention:
+ * The Algorithm That Made Long-Context AI Possible" (section "The quadratic
+ * bottleneck in standard attention"): a score matrix S = Q K^T and the output
+ * O = softmax(S) V. The tiled method of the FlashAttention pages (abstract of
+ * "FlashAttention: Fast and Memory-Efficient Exact Attention with IO-Awareness";
+ * section "What tiling changes" of the page above) reaches exactly this result in
+ * real arithmetic, so the oracle is the definition itself: no tiling, no online
+ * softmax, two passes per query row, everything in IEEE double.
+ *
+ * Readings where the pages are silent (each is also listed in the design notes):
+ *   - scores are multiplied by `scale` before the softmax;
+ *   - causal masking keeps key j for query i iff j <= i (square, no offset);
+ *   - grouped-query attention maps query head h to key/value head h / (H / Hkv);
+ *   - lse is the natural log of the softmax denominator over the scaled scores,
+ *     lse = m + ln(sum_j exp(s_j - m)), so that P_ij = exp(s_ij - lse_i);
+ *   - the inputs are the exact values of the bf16 / f16 / e4m3 elements handed to
+ *     the GPU library; an e4m3 element is multiplied by its tensor's descale.
+ *
+ * Layouts (row-major, contiguous): q, o [B][N][H][d]; k, v [B][N][Hkv][d];
+ * lse [B][H][N].
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC (no fast-math: the order of every sum is
+ * the ascending index order written below).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- element decoders (exact conversion of a storage format to double) ---- */
+
+/* IEEE 754 binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+double oracle_decode_f16(uint16_t h) {
+  int sign = (h >> 15) & 1, e = (h >> 10) & 0x1f, f = h & 0x3ff;
+  double mag;
+  if (e == 0) mag = ldexp((double)f, -24);                  /* subnormal: f * 2^-14 * 2^-10 */
+  else if (e == 31) mag = f ? NAN : INFINITY;
+  else mag = ldexp((double)(1024 + f), e - 25);              /* (1 + f/1024) * 2^(e-15) */
+  return sign ? -mag : mag;
+}
+
+/* bfloat16: the upper half of an IEEE binary32. */
+double oracle_decode_bf16(uint16_t h) {
+  int sign = (h >> 15) & 1, e = (h >> 7) & 0xff, f = h & 0x7f;
+  double mag;
+  if (e == 0) mag = ldexp((double)f, -133);                 /* f * 2^-126 * 2^-7 */
+  else if (e == 255) mag = f ? NAN : INFINITY;
+  else mag = ldexp((double)(128 + f), e - 134);              /* (1 + f/128) * 2^(e-127) */
+  return sign ? -mag : mag;
+}
+
+/* OCP 8-bit E4M3 ("fn"): 1 sign, 4 exponent (bias 7), 3 fraction bits, no
+ * infinities, S.1111.111 is NaN, largest finite magnitude 448. */
+double oracle_decode_e4m3(uint8_t x) {
+  int sign = (x >> 7) & 1, e = (x >> 3) & 0xf, f = x & 7;
+  double mag;
+  if (e == 15 && f == 7) mag = NAN;
+  else if (e == 0) mag = ldexp((double)f, -9);              /* f/8 * 2^-6 */
+  else mag = ldexp((double)(8 + f), e - 10);                 /* (1 + f/8) * 2^(e-7) */
+  return sign ? -mag : mag;
+}
+
+/* dtype codes: 0 = f16, 1 = bf16, 2 = e4m3. Writes n doubles: decode(src[i]) * mult. */
+int oracle_decode(int dtype, const void* src, int64_t n, double mult, double* dst) {
+  if (n < 0 || (n > 0 && (!src || !dst))) return 1;
+  for (int64_t i = 0; i < n; ++i) {
+    double x;
+    if (dtype == 0) x = oracle_decode_f16(((const uint16_t*)src)[i]);
+    else if (dtype == 1) x = oracle_decode_bf16(((const uint16_t*)src)[i]);
+    else if (dtype == 2) x = oracle_decode_e4m3(((const uint8_t*)src)[i]);
+    else return 1;
+    dst[i] = x * mult;
+  }
+  return 0;
+}
+
+/* ---- one query row ---- */
+
+/* Scores, max, exponentials, denominator and output for one query row `qi` of batch b
+ * against key/value head hk, with the mask applied for query position i. `s` is
+ * caller scratch of N doubles. Writes o_row[0..d) and *lse. */
+static void attn_row(const double* qi, const double* k, const double* v, int Hkv, int N, int d,
+                     int causal, double scale, int b, int hk, int i, double* s, double* o_row,
+                     double* lse) {
+  const int nkeys = causal ? i + 1 : N;                      /* keys j <= i under the mask */
+
+  /* pass 1: s_j = scale * <q_i, k_j>, and the row maximum */
+  double m = -INFINITY;
+  for (int j = 0; j < nkeys; ++j) {
+    const double* kj = k + (((size_t)b * N + j) * Hkv + hk) * d;
+    double dot = 0.0;
+    for (int t = 0; t < d; ++t) dot += qi[t] * kj[t];
+    s[j] = scale * dot;
+    if (s[j] > m) m = s[j];
+  }
+  /* pass 2: e_j = exp(s_j - m), l = sum_j e_j, o = sum_j e_j v_j / l */
+  for (int t = 0; t < d; ++t) o_row[t] = 0.0;
+  double l = 0.0;
+  for (int j = 0; j < nkeys; ++j) {
+    const double e = exp(s[j] - m);
+    const double* vj = v + (((size_t)b * N + j) * Hkv + hk) * d;
+    l += e;
+    for (int t = 0; t < d; ++t) o_row[t] += e * vj[t];
+  }
+  for (int t = 0; t < d; ++t) o_row[t] /= l;
+  *lse = m + log(l);
+}
+
+static int check_shape(int B, int H, int Hkv, int N, int d) {
+  if (B < 1 || H < 1 || Hkv < 1 || N < 1 || d < 1) return 1;
+  if (Hkv > H || H % Hkv != 0) return 1;
+  return 0;
+}
+
+/* Full forward over every (b, h, i). Returns 0 on success, 1 on bad arguments,
+ * 2 if scratch allocation failed. */
+int oracle_attn_fwd_f64(const double* q, const double* k, const double* v, double* o, double* lse,
+                        int B, int H, int Hkv, int N, int d, int causal, double scale) {
+  if (check_shape(B, H, Hkv, N, d) || !q || !k || !v || !o || !lse) return 1;
+  const int64_t rows = (int64_t)B * H * N;
+  const int group = H / Hkv;                                 /* grouped-query head map h -> h / group */
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)N);
+    if (!s) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 8)
+    for (int64_t r = 0; r < rows; ++r) {
+      if (!s) continue;
+      const int i = (int)(r % N), h = (int)((r / N) % H), b = (int)(r / ((int64_t)N * H));
+      const size_t qo = (((size_t)b * N + i) * H + h) * d;
+      attn_row(q + qo, k, v, Hkv, N, d, causal, scale, b, h / group, i, s, o + qo,
+               lse + ((size_t)b * H + h) * N + i);
+    }
+    free(s);
+  }
+  return failed ? 2 : 0;
+}
+
+/* Selected rows only: rows[3r], rows[3r+1], rows[3r+2] = (b, h, i). o_rows is
+ * [nrows][d], lse_rows [nrows]. q is either a full [B][N][H][d] tensor
+ * (q_is_rows = 0) or the selected query rows gathered as [nrows][d] (q_is_rows = 1),
+ * so that a caller need not decode a whole large Q to check a sample. */
+int oracle_attn_rows_f64(const double* q, int q_is_rows, const double* k, const double* v,
+                         int B, int H, int Hkv, int N, int d, int causal, double scale,
+                         int64_t nrows, const int64_t* rows, double* o_rows, double* lse_rows) {
+  if (check_shape(B, H, Hkv, N, d) || !q || !k || !v || !rows || !o_rows || !lse_rows) return 1;
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+    if (b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= N) return 1;
+  }
+  const int group = H / Hkv;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)N);
+    if (!s) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+      if (!s) continue;
+      const int b = (int)rows[3 * r], h = (int)rows[3 * r + 1], i = (int)rows[3 * r + 2];
+      const double* qi = q_is_rows ? q + (size_t)r * d : q + (((size_t)b * N + i) * H + h) * d;
+      attn_row(qi, k, v, Hkv, N, d, causal, scale, b, h / group, i, s, o_rows + (size_t)r * d,
+               lse_rows + r);
+    }
+    free(s);
+  }
+  return failed ? 2 : 0;
+}
+
+/* Softmax probabilities of one (b, h) as an N x N matrix (row i, key j), zero where
+ * masked. For small N only: used to check that rows sum to one. */
+int oracle_attn_probs_f64(const double* q, const double* k, int B, int H, int Hkv, int N, int d,
+                          int causal, double scale, int b, int h, double* p) {
+  if (check_shape(B, H, Hkv, N, d) || !q || !k || !p || b < 0 || b >= B || h < 0 || h >= H)
+    return 1;
+  const int hk = h / (H / Hkv);
+  for (int i = 0; i < N; ++i) {
+    const double* qi = q + (((size_t)b * N + i) * H + h) * d;
+    double* pi = p + (size_t)i * N;
+    const int nkeys = causal ? i + 1 : N;
+    double m = -INFINITY, l = 0.0;
+    for (int j = 0; j < N; ++j) pi[j] = 0.0;
+    for (int j = 0; j < nkeys; ++j) {
+      const double* kj = k + (((size_t)b * N + j) * Hkv + hk) * d;
+      double dot = 0.0;
+      for (int t = 0; t < d; ++t) dot += qi[t] * kj[t];
+      pi[j] = scale * dot;
+      if (pi[j] > m) m = pi[j];
+    }
+    for (int j = 0; j < nkeys; ++j) {
+      pi[j] = exp(pi[j] - m);
+      l += pi[j];
+    }
+    for (int j = 0; j < nkeys; ++j) pi[j] /= l;
+  }
+  return 0;
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}

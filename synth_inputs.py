@@ -1,0 +1,132 @@
+"""Seeded synthetic inputs for the attention forward workloads.
+
+This module draws random tensors and rounds them to the storage format handed to
+the GPU library. It holds none of the attention arithmetic and is the only code
+shared by the oracle side and the HIP side (both receive the same bit patterns).
+
+Recipe (per tensor, in the order Q, K, V):
+  * ``numpy.random.Generator(PCG64(seed))`` draws float32 standard normals in
+    memory order [B, N, heads, d];
+  * for the e4m3 workload, the same generator then draws U(0,1) per element and
+    multiplies the entries with U < outlier_frac (0.1%) by outlier_mult (20);
+  * f16 / bf16: round to nearest even (torch CPU casts);
+  * e4m3: per-tensor scale = amax(|x|) / 448 (float32), x / scale clamped to
+    [-448, 448], rounded to nearest even in OCP E4M3 (torch ``float8_e4m3fn``);
+    the descale handed to the library is that scale.
+Arrays are returned as bit patterns: uint16 for f16 / bf16, uint8 for e4m3.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, replace
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    N: int
+    d: int
+    causal: bool
+    dtype: str          # "f16", "bf16" or "e4m3"
+    seed: int
+    scale: float
+    outlier_frac: float = 0.0
+    outlier_mult: float = 20.0
+
+    @property
+    def flops(self) -> float:
+        """4*B*H*N^2*d, halved under the causal mask (query heads H)."""
+        f = 4.0 * self.B * self.H * self.N * self.N * self.d
+        return f / 2 if self.causal else f
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+def _w(name, B, H, Hkv, N, d, causal, dtype, seed, **kw):
+    return Workload(name, B, H, Hkv, N, d, causal, dtype, seed, 1.0 / math.sqrt(d), **kw)
+
+
+# The five workloads: a tiny fp16 case, bf16 multi-head, bf16 causal long sequence,
+# bf16 causal grouped-query, and e4m3 with outliers.
+WORKLOADS = {
+    w.name: w for w in [
+        _w("tiny_f16_b1_h2_n128_d64", 1, 2, 2, 128, 64, False, "f16", 1001),
+        _w("mha_bf16_b16_h16_n2048_d128", 16, 16, 16, 2048, 128, False, "bf16", 1002),
+        _w("causal_bf16_b1_h16_n16384_d128", 1, 16, 16, 16384, 128, True, "bf16", 1003),
+        _w("gqa_causal_bf16_b4_h32_kv8_n8192_d128", 4, 32, 8, 8192, 128, True, "bf16", 1004),
+        _w("fp8_e4m3_b8_h16_n4096_d128", 8, 16, 16, 4096, 128, False, "e4m3", 1005,
+           outlier_frac=1e-3, outlier_mult=20.0),
+    ]
+}
+
+E4M3_MAX = 448.0
+
+
+def _round_bits(x: np.ndarray, dtype: str) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    if dtype == "bf16":
+        return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if dtype == "f16":
+        return t.to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    raise ValueError(dtype)
+
+
+def quantize_e4m3(x: np.ndarray):
+    """Per-tensor e4m3 quantisation. Returns (uint8 bit patterns, descale float)."""
+    amax = float(np.max(np.abs(x))) if x.size else 0.0
+    scale = np.float32(amax / E4M3_MAX) if amax > 0 else np.float32(1.0)
+    y = np.clip(x.astype(np.float32) / scale, -E4M3_MAX, E4M3_MAX)
+    bits = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return bits, float(scale)
+
+
+def draw(shape, rng: np.random.Generator, outlier_frac: float = 0.0, outlier_mult: float = 20.0):
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if outlier_frac > 0:
+        u = rng.random(size=shape, dtype=np.float32)
+        x = np.where(u < outlier_frac, x * np.float32(outlier_mult), x).astype(np.float32)
+    return x
+
+
+def make_inputs(B: int, H: int, Hkv: int, N: int, d: int, dtype: str, seed: int,
+                outlier_frac: float = 0.0, outlier_mult: float = 20.0, keep_f32: bool = False):
+    """Draw Q [B,N,H,d], K and V [B,N,Hkv,d] and round them to `dtype`.
+
+    Returns a dict with "q", "k", "v" (bit patterns), "descale" ((dq, dk, dv) for
+    e4m3, else None) and, with keep_f32, the unrounded float32 draws "q32", "k32",
+    "v32"."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {}
+    raw = {}
+    for name, heads in (("q", H), ("k", Hkv), ("v", Hkv)):
+        raw[name] = draw((B, N, heads, d), rng, outlier_frac, outlier_mult)
+    if dtype == "e4m3":
+        ds = []
+        for name in ("q", "k", "v"):
+            bits, s = quantize_e4m3(raw[name])
+            out[name] = bits
+            ds.append(s)
+        out["descale"] = tuple(ds)
+    else:
+        for name in ("q", "k", "v"):
+            out[name] = _round_bits(raw[name], dtype)
+        out["descale"] = None
+    if keep_f32:
+        for name in ("q", "k", "v"):
+            out[name + "32"] = raw[name]
+    return out
+
+
+def workload_inputs(w: Workload, keep_f32: bool = False, **overrides):
+    """Inputs of a named workload (optionally with some sizes overridden)."""
+    if overrides:
+        w = w.with_(**overrides)
+    return make_inputs(w.B, w.H, w.Hkv, w.N, w.d, w.dtype, w.seed, w.outlier_frac,
+                       w.outlier_mult, keep_f32=keep_f32)

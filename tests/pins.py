@@ -1,0 +1,331 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself:
+brute force in 50-digit arithmetic, an independent library implementation, closed
+forms, invariants of softmax attention and the storage-format definitions.
+
+The pages describe attention as S = Q K^T, O = softmax(S) V (section "The quadratic
+bottleneck in standard attention" of "FlashAttention: The Algorithm That Made
+Long-Context AI Possible") and state that the tiled method is exact (abstract of
+"FlashAttention: Fast and Memory-Efficient Exact Attention with IO-Awareness"). They
+print no worked example, so every pin here is derived from that definition.
+
+Each pin is a function that raises AssertionError on failure. The same battery runs
+against deliberately broken copies of the oracle (test_oracle_mutants.py) to show
+that a plausible mistake anywhere in it fails at least one pin.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import mpmath
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _qkv(rng, B, N, H, Hkv, d):
+    return (rng.standard_normal((B, N, H, d)), rng.standard_normal((B, N, Hkv, d)),
+            rng.standard_normal((B, N, Hkv, d)))
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    err = np.max(np.abs(a - b) / np.maximum(1.0, np.abs(b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max scaled error {err:.3e} > {tol:.1e}"
+
+
+# P1 -- brute force in 50 significant digits on tiny inputs.
+def pin_mpmath_bruteforce():
+    rng = np.random.default_rng(11)
+    mpmath.mp.dps = 50
+    cases = [(1, 1, 1, 1, False), (2, 1, 3, 4, True), (2, 2, 5, 8, False), (2, 1, 8, 4, True),
+             (1, 1, 17, 8, False), (2, 2, 2, 1, True), (4, 2, 6, 3, True)]
+    for H, Hkv, N, d, causal in cases:
+        q, k, v = _qkv(rng, 1, N, H, Hkv, d)
+        scale = 0.37
+        o, lse = oracle.attn_fwd_f64(q, k, v, causal, scale)
+        for h in range(H):
+            hk = h // (H // Hkv)
+            for i in range(N):
+                J = range(i + 1) if causal else range(N)
+                s = [mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(q[0, i, h, t]) * mpmath.mpf(k[0, j, hk, t])
+                                                     for t in range(d)) for j in J]
+                L = mpmath.log(mpmath.fsum(mpmath.exp(x) for x in s))
+                w = [mpmath.exp(x - L) for x in s]
+                ref_o = [float(mpmath.fsum(w[n] * mpmath.mpf(v[0, j, hk, t]) for n, j in enumerate(J)))
+                         for t in range(d)]
+                _close(o[0, i, h], ref_o, 1e-13, f"mpmath O (H{H} Hkv{Hkv} N{N} d{d} c{causal}) h{h} i{i}")
+                _close(lse[0, h, i], float(L), 1e-13, f"mpmath lse h{h} i{i}")
+
+
+def _sdpa_lse(q, k, causal, scale, H, Hkv):
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3).repeat_interleave(H // Hkv, dim=1)
+    s = torch.matmul(tq, tk.transpose(-1, -2).contiguous()) * scale
+    if causal:
+        N = q.shape[1]
+        s = s.masked_fill(torch.ones(N, N, dtype=torch.bool).triu(1), float("-inf"))
+    return torch.logsumexp(s, dim=-1).numpy()
+
+
+# P2 -- an independent library implementation (torch CPU scaled_dot_product_attention, float64).
+def pin_torch_sdpa():
+    rng = np.random.default_rng(12)
+    for B, H, Hkv, N, d, causal in [(1, 2, 2, 128, 64, False), (2, 4, 2, 67, 16, True),
+                                    (1, 4, 1, 33, 8, False), (1, 2, 2, 130, 128, True)]:
+        q, k, v = _qkv(rng, B, N, H, Hkv, d)
+        scale = 1.0 / math.sqrt(d)
+        o, lse = oracle.attn_fwd_f64(q, k, v, causal, scale)
+        t = lambda x: torch.from_numpy(x).permute(0, 2, 1, 3)
+        ref = F.scaled_dot_product_attention(t(q), t(k), t(v), is_causal=causal, scale=scale,
+                                             enable_gqa=(H != Hkv)).permute(0, 2, 1, 3).numpy()
+        _close(o, ref, 1e-12, f"sdpa O B{B} H{H} Hkv{Hkv} N{N} d{d} causal={causal}")
+        _close(lse, _sdpa_lse(q, k, causal, scale, H, Hkv), 1e-12, "logsumexp of scores")
+
+
+# P3 -- Q = 0: every score is 0, so O_i is the mean of the visible V rows and lse_i = ln|J_i|.
+def pin_zero_query():
+    rng = np.random.default_rng(13)
+    for causal in (False, True):
+        B, N, H, Hkv, d = 2, 37, 4, 2, 8
+        _, k, v = _qkv(rng, B, N, H, Hkv, d)
+        q = np.zeros((B, N, H, d))
+        o, lse = oracle.attn_fwd_f64(q, k, v, causal, 0.7)
+        for h in range(H):
+            hk = h // (H // Hkv)
+            if causal:
+                ref = np.cumsum(v[:, :, hk, :], axis=1) / np.arange(1, N + 1)[None, :, None]
+                ref_lse = np.log(np.arange(1, N + 1))[None, :].repeat(B, 0)
+            else:
+                ref = np.repeat(v[:, :, hk, :].mean(axis=1, keepdims=True), N, axis=1)
+                ref_lse = np.full((B, N), math.log(N))
+            _close(o[:, :, h, :], ref, 1e-13, f"Q=0 mean of V (causal={causal}) h{h}")
+            _close(lse[:, h, :], ref_lse, 1e-13, f"Q=0 lse=ln|J| (causal={causal})")
+
+
+# P4 -- one key: O = V_0 and lse = scale * <q, k_0>.
+def pin_single_key():
+    rng = np.random.default_rng(14)
+    q, k, v = _qkv(rng, 3, 1, 4, 2, 5)
+    for causal in (False, True):
+        o, lse = oracle.attn_fwd_f64(q, k, v, causal, 0.3)
+        for h in range(4):
+            hk = h // 2
+            _close(o[:, 0, h, :], v[:, 0, hk, :], 1e-15, "N=1 O=V0")
+            _close(lse[:, h, 0], 0.3 * np.einsum("bt,bt->b", q[:, 0, h, :], k[:, 0, hk, :]), 1e-14,
+                   "N=1 lse=scale*q.k")
+
+
+# P5 -- two keys: weights are logistic functions of the score difference.
+def pin_two_keys():
+    rng = np.random.default_rng(15)
+    q, k, v = _qkv(rng, 1, 2, 1, 1, 6)
+    scale = 0.45
+    o, lse = oracle.attn_fwd_f64(q, k, v, False, scale)
+    s = [scale * float(np.dot(q[0, 0, 0], k[0, j, 0])) for j in range(2)]
+    sig = lambda x: 1.0 / (1.0 + math.exp(-x))
+    ref = sig(s[0] - s[1]) * v[0, 0, 0] + sig(s[1] - s[0]) * v[0, 1, 0]
+    _close(o[0, 0, 0], ref, 1e-14, "two-key logistic form")
+    _close(lse[0, 0, 0], np.logaddexp(s[0], s[1]), 1e-14, "two-key lse=logaddexp")
+    # causal: the first query sees only key 0
+    o, lse = oracle.attn_fwd_f64(q, k, v, True, scale)
+    _close(o[0, 0, 0], v[0, 0, 0], 1e-15, "causal row 0 sees key 0 only")
+    _close(lse[0, 0, 0], s[0], 1e-14, "causal row 0 lse")
+
+
+# P6 -- rows of P sum to one and are nonnegative: constant V gives a constant output
+# and O is affine in V.
+def pin_affine_in_v():
+    rng = np.random.default_rng(16)
+    B, N, H, Hkv, d = 2, 29, 2, 1, 7
+    q, k, v = _qkv(rng, B, N, H, Hkv, d)
+    for causal in (False, True):
+        c = rng.standard_normal(d)
+        o, _ = oracle.attn_fwd_f64(q, k, np.broadcast_to(c, v.shape).copy(), causal, 0.5)
+        _close(o, np.broadcast_to(c, o.shape), 1e-14, "constant V")
+        o1, l1 = oracle.attn_fwd_f64(q, k, v, causal, 0.5)
+        o2, l2 = oracle.attn_fwd_f64(q, k, 2.5 * v - 1.25, causal, 0.5)
+        _close(o2, 2.5 * o1 - 1.25, 1e-13, "O(aV+b)=aO(V)+b")
+        _close(l2, l1, 0.0, "lse does not depend on V")
+
+
+# P7 -- probability rows: nonnegative, sum to one, zero above the diagonal when causal,
+# and the output is those rows applied to V.
+def pin_probability_rows():
+    rng = np.random.default_rng(17)
+    B, N, H, Hkv, d = 1, 23, 2, 2, 4
+    q, k, v = _qkv(rng, B, N, H, Hkv, d)
+    for causal in (False, True):
+        o, lse = oracle.attn_fwd_f64(q, k, v, causal, 0.8)
+        for h in range(H):
+            p = oracle.attn_probs_f64(q, k, 0, h, causal, 0.8)
+            assert np.all(p >= 0), "negative probability"
+            _close(p.sum(axis=1), np.ones(N), 1e-14, "rows sum to 1")
+            if causal:
+                assert np.all(np.triu(p, 1) == 0), "mass above the diagonal"
+            _close(o[0, :, h, :], p @ v[0, :, h, :], 1e-13, "O = P V")
+            s = 0.8 * q[0, :, h, :] @ k[0, :, h, :].T
+            with np.errstate(divide="ignore"):
+                _close(np.where(p > 0, np.log(np.where(p > 0, p, 1)) + lse[0, h, :, None], 0),
+                       np.where(p > 0, s, 0), 1e-12, "P_ij = exp(s_ij - lse_i)")
+
+
+# P8 -- without the mask, permuting key/value rows together changes nothing.
+def pin_key_permutation():
+    rng = np.random.default_rng(18)
+    B, N, H, Hkv, d = 2, 41, 4, 2, 6
+    q, k, v = _qkv(rng, B, N, H, Hkv, d)
+    o, lse = oracle.attn_fwd_f64(q, k, v, False, 0.6)
+    perm = rng.permutation(N)
+    o2, lse2 = oracle.attn_fwd_f64(q, k[:, perm], v[:, perm], False, 0.6)
+    _close(o2, o, 1e-13, "key permutation O")
+    _close(lse2, lse, 1e-13, "key permutation lse")
+
+
+# P9 -- adding w to every key shifts every score of row i by scale*<q_i, w>: O is
+# unchanged and lse_i moves by exactly that amount.
+def pin_key_shift():
+    rng = np.random.default_rng(19)
+    B, N, H, Hkv, d = 1, 31, 2, 1, 5
+    q, k, v = _qkv(rng, B, N, H, Hkv, d)
+    w = rng.standard_normal(d)
+    for causal in (False, True):
+        o, lse = oracle.attn_fwd_f64(q, k, v, causal, 0.9)
+        o2, lse2 = oracle.attn_fwd_f64(q, k + w, v, causal, 0.9)
+        _close(o2, o, 1e-12, "key shift O")
+        shift = 0.9 * np.einsum("bnhd,d->bhn", q, w)
+        _close(lse2, lse + shift, 1e-12, "key shift lse")
+
+
+# P10 -- grouped-query attention equals multi-head attention with each K/V head
+# repeated for its group of query heads (query head h reads K/V head h // (H/Hkv)).
+def pin_gqa_repeat():
+    rng = np.random.default_rng(20)
+    B, N, H, Hkv, d = 2, 19, 6, 2, 4
+    q, k, v = _qkv(rng, B, N, H, Hkv, d)
+    for causal in (False, True):
+        o, lse = oracle.attn_fwd_f64(q, k, v, causal, 0.5)
+        kr = np.repeat(k, H // Hkv, axis=2)
+        vr = np.repeat(v, H // Hkv, axis=2)
+        o2, lse2 = oracle.attn_fwd_f64(q, kr, vr, causal, 0.5)
+        _close(o, o2, 0.0, "GQA = repeated MHA (O)")
+        _close(lse, lse2, 0.0, "GQA = repeated MHA (lse)")
+
+
+# P11 -- under the mask, row i equals unmasked attention over keys 0..i.
+def pin_causal_prefix():
+    rng = np.random.default_rng(21)
+    B, N, H, Hkv, d = 1, 17, 2, 2, 4
+    q, k, v = _qkv(rng, B, N, H, Hkv, d)
+    o, lse = oracle.attn_fwd_f64(q, k, v, True, 0.7)
+    for i in (0, 1, 5, 16):
+        qq = np.repeat(q[:, i:i + 1], i + 1, axis=1)
+        o2, lse2 = oracle.attn_fwd_f64(qq, k[:, :i + 1], v[:, :i + 1], False, 0.7)
+        _close(o2[:, 0], o[:, i], 1e-13, f"causal row {i} = prefix attention (O)")
+        _close(lse2[:, :, 0], lse[:, :, i], 1e-13, f"causal row {i} = prefix attention (lse)")
+
+
+# P12 -- splitting the keys into two sets: lse merges by logaddexp and O merges with
+# weights exp(lse_part - lse).
+def pin_split_merge():
+    rng = np.random.default_rng(22)
+    B, N, H, Hkv, d = 1, 24, 2, 1, 6
+    q, k, v = _qkv(rng, B, N, H, Hkv, d)
+    o, lse = oracle.attn_fwd_f64(q, k, v, False, 0.55)
+    a = 10
+    # queries attend separately to keys [0,a) and [a,N): pad each part to N rows by
+    # evaluating each query against the part (rows of q are independent)
+    def part(ks, vs):
+        n = ks.shape[1]
+        oo = np.empty((B, N, H, d))
+        ll = np.empty((B, H, N))
+        for i in range(N):
+            qq = np.repeat(q[:, i:i + 1], n, axis=1)
+            o_, l_ = oracle.attn_fwd_f64(qq, ks, vs, False, 0.55)
+            oo[:, i] = o_[:, 0]
+            ll[:, :, i] = l_[:, :, 0]
+        return oo, ll
+    oa, la = part(k[:, :a], v[:, :a])
+    ob, lb = part(k[:, a:], v[:, a:])
+    lm = np.logaddexp(la, lb)
+    _close(lm, lse, 1e-13, "lse = logaddexp(lse_A, lse_B)")
+    wa = np.exp(la - lm).transpose(0, 2, 1)[..., None]
+    wb = np.exp(lb - lm).transpose(0, 2, 1)[..., None]
+    _close(wa * oa + wb * ob, o, 1e-13, "O = sum of parts weighted by exp(lse_part - lse)")
+
+
+# P13 -- large score gaps: the output is the value row of the best key and lse the best
+# score; scores of magnitude ~1e3 stay finite (the row maximum is subtracted).
+def pin_hardmax_and_range():
+    rng = np.random.default_rng(23)
+    B, N, H, Hkv, d = 1, 9, 1, 1, 3
+    k = rng.standard_normal((B, N, Hkv, d))
+    v = rng.standard_normal((B, N, Hkv, d))
+    q = np.zeros((B, N, H, d))
+    best = 4
+    k[0, best, 0] = np.array([50.0, 0.0, 0.0])
+    k[0, :best, 0, 0] = np.linspace(-5, 5, best)
+    k[0, best + 1:, 0, 0] = np.linspace(-5, 9, N - best - 1)
+    q[0, :, 0] = np.array([1.0, 0.0, 0.0])
+    o, lse = oracle.attn_fwd_f64(q, k, v, False, 1.0)
+    _close(o[0, :, 0], np.repeat(v[0, best:best + 1, 0], N, axis=0), 1e-15, "hardmax O")
+    assert np.all(np.abs(lse[0, 0] - 50.0) < 1e-13), "hardmax lse = best score"
+    for mag in (300.0, 1000.0):
+        o, lse = oracle.attn_fwd_f64(q, k * (mag / 50.0), v, True, 1.0)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), f"non-finite at score magnitude {mag}"
+        _close(o[0, best:, 0], np.repeat(v[0, best:best + 1, 0], N - best, axis=0), 1e-15,
+               f"hardmax under the mask at magnitude {mag}")
+
+
+# P14 -- storage formats decode to the values their definitions give, checked against
+# independent decoders (numpy binary16, torch bfloat16 and float8_e4m3fn).
+def pin_decoders():
+    codes16 = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f16 = oracle.decode(codes16, "f16")
+    ref = codes16.view(np.float16).astype(np.float64)
+    fin = np.isfinite(ref)
+    assert np.array_equal(f16[fin], ref[fin]), "f16 decode"
+    assert np.array_equal(np.isnan(f16), np.isnan(ref)) and np.array_equal(np.isinf(f16), np.isinf(ref))
+    bf = oracle.decode(codes16, "bf16")
+    refb = torch.from_numpy(codes16.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    fin = np.isfinite(refb)
+    assert np.array_equal(bf[fin], refb[fin]), "bf16 decode"
+    assert np.array_equal(np.isnan(bf), np.isnan(refb)) and np.array_equal(np.isinf(bf), np.isinf(refb))
+    codes8 = np.arange(256, dtype=np.uint16).astype(np.uint8)
+    e = oracle.decode(codes8, "e4m3")
+    refe = torch.from_numpy(codes8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    fin = np.isfinite(refe)
+    assert np.array_equal(e[fin], refe[fin]), "e4m3 decode"
+    assert np.array_equal(np.isnan(e), np.isnan(refe)), "e4m3 NaN codes"
+    # definition points of OCP E4M3: largest finite, smallest normal, smallest subnormal
+    assert e[0x7E] == 448.0 and e[0x08] == 2.0 ** -6 and e[0x01] == 2.0 ** -9 and e[0xFE] == -448.0
+    assert oracle.decode(np.array([0x38], np.uint8), "e4m3", 0.25)[0] == 0.25, "descale multiplies"
+
+
+# Closed-form fixtures derived by hand (tests/golden/*.json, each with its derivation).
+def pin_golden_fixtures():
+    for name in sorted(os.listdir(GOLDEN)):
+        if not name.endswith(".json"):
+            continue
+        with open(os.path.join(GOLDEN, name)) as f:
+            fx = json.load(f)
+        q = np.array(fx["q"], dtype=np.float64)
+        k = np.array(fx["k"], dtype=np.float64)
+        v = np.array(fx["v"], dtype=np.float64)
+        scale = fx["scale"] if isinstance(fx["scale"], float) else eval(fx["scale"], {"math": math})
+        o, lse = oracle.attn_fwd_f64(q, k, v, fx["causal"], scale)
+        _close(o, np.array(fx["o"]), fx["tol"], f"golden {name} O")
+        _close(lse, np.array(fx["lse"]), fx["tol"], f"golden {name} lse")
+
+
+ALL_PINS = [pin_mpmath_bruteforce, pin_torch_sdpa, pin_zero_query, pin_single_key, pin_two_keys,
+            pin_affine_in_v, pin_probability_rows, pin_key_permutation, pin_key_shift, pin_gqa_repeat,
+            pin_causal_prefix, pin_split_merge, pin_hardmax_and_range, pin_decoders, pin_golden_fixtures]
