@@ -1,0 +1,173 @@
+"""Benchmark of the attention forward hot path on one MI355X.
+
+A step is one attention forward (one fa_fwd launch through the C ABI) over the whole
+workload, inputs resident in HBM. Prints one JSON line with TFLOP/s counted as
+4*B*H*N^2*d (halved under the causal mask), the roofline of the kernel (achieved
+TFLOP/s from HIP events on the launch stream against the dense bf16/f16 MFMA peak) and
+the fp64 CPU oracle timed on the host cores on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --mode copy      # plain device copy of known size, for counter scaling
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+import synth_inputs  # noqa: E402
+
+DEFAULT_WORKLOAD = "mha_bf16_b16_h16_n2048_d128"
+# Dense MFMA peak of MI355X: 256 CUs x 4 SIMDs x 2.4 GHz x (1024 bf16/f16 or 2048 fp8 FLOP/clk/SIMD)
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2}
+KERNEL_SRC = os.path.join(ROOT, "exact_tiled_attention_03_amd", "csrc", "fa_fwd.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+METRIC = "attention fwd TFLOP/s (4*B*H*N^2*d, causal halved) and % MFMA peak, bf16 d=128"
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
+    on this exact kernel source and workload; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = t.get("workloads", {}).get(workload)
+    if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def to_dev(bits, dtype):
+    if dtype == "e4m3":
+        return torch.from_numpy(np.ascontiguousarray(bits)).cuda()
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda()
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
+
+
+def cpu_baseline(w: synth_inputs.Workload, inp: dict, budget_s: float = 12.0):
+    """The fp64 oracle on a bounded sample: whole (batch, GQA group) slices of the same
+    inputs, in order, until about budget_s seconds of wall time on the host cores."""
+    import oracle
+    dq, dk, dv = inp["descale"] if inp["descale"] else (1.0, 1.0, 1.0)
+    g = w.H // w.Hkv
+    per_head = (4.0 * w.N * w.N * w.d) / (2 if w.causal else 1)
+    heads, elapsed = 0, 0.0
+    for b in range(w.B):
+        if elapsed >= budget_s:
+            break
+        q = oracle.decode(inp["q"][b:b + 1], w.dtype, dq)
+        k = oracle.decode(inp["k"][b:b + 1], w.dtype, dk)
+        v = oracle.decode(inp["v"][b:b + 1], w.dtype, dv)
+        for hk in range(w.Hkv):
+            if elapsed >= budget_s:
+                break
+            t0 = time.perf_counter()
+            oracle.attn_fwd_f64(np.ascontiguousarray(q[:, :, hk * g:(hk + 1) * g]), k[:, :, hk:hk + 1],
+                                v[:, :, hk:hk + 1], w.causal, w.scale)
+            elapsed += time.perf_counter() - t0
+            heads += g
+    flops = per_head * heads
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"first {heads} of {w.B * w.H} (batch, head) slices of {w.name} in memory order, "
+                      f"whole slices ({flops / 1e9:.1f} GFLOP, {elapsed:.1f} s in fp64)"}
+
+
+def run_copy():
+    n = 1 << 28  # 2^28 float32 = 1 GiB read, 1 GiB written per copy
+    x = torch.ones(n, device="cuda", dtype=torch.float32)
+    y = torch.empty_like(x)
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy", "bytes_read_per_launch": n * 4, "bytes_written_per_launch": n * 4,
+                      "launches": 5}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(synth_inputs.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", default="attn", choices=["attn", "copy"])
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the attention forward here is a single-GPU kernel "
+              "library with no multi-GPU path; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if args.mode == "copy":
+        run_copy()
+        return
+
+    import exact_tiled_attention_03_amd as fa
+
+    w = synth_inputs.WORKLOADS[args.workload]
+    inp = synth_inputs.workload_inputs(w)
+    q, k, v = (to_dev(inp[x], w.dtype) for x in "qkv")
+    dt = w.dtype if w.dtype == "e4m3" else None
+    o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale, descale=inp["descale"], dtype=dt)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o.float()).all()), "non-finite output"
+
+    for _ in range(args.warmup):
+        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, descale=inp["descale"], dtype=dt, out=o, lse=lse)
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, descale=inp["descale"], dtype=dt, out=o, lse=lse)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+
+    ms_per_step = wall * 1e3 / args.steps
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    achieved = w.flops / (kernel_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) inputs)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   "causal": w.causal, "scale": w.scale, "flop_per_step": w.flops},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name),
+                     "kernel_ms": round(kernel_ms, 5)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,435 @@
+// fa_fwd.hip -- exact tiled attention forward for gfx950 (MI355X), and its C ABI.
+//
+// Method: the I/O-aware exact attention of "FlashAttention: Fast and Memory-Efficient
+// Exact Attention with IO-Awareness" (abstract): key/value tiles stream through on-chip
+// memory (here LDS), the scores of one tile live only in registers, and a running row
+// maximum with a running exponential sum (section "What tiling changes" of "FlashAttention:
+// The Algorithm That Made Long-Context AI Possible") replaces the full-row softmax, so the
+// N x N matrix never reaches HBM. Work partitioning follows the abstract of
+// "FlashAttention-2: Faster Attention with Better Parallelism and Work Partitioning":
+// one workgroup per (batch, head, query tile) so that a single head still spreads over
+// many CUs (item 2), and each wavefront owns disjoint query rows while sharing the
+// workgroup's K/V tiles, so no partial output rows are reduced across wavefronts (item 3).
+// Non-matmul work is kept small (item 1): the scale is folded into one FMA before a
+// base-2 exponential, the output is normalised once at the end, and the accumulator is
+// only rescaled when a row maximum has grown by more than 2^8.
+//
+// gfx950 mapping (one wavefront = 64 lanes, MFMA 32x32x16):
+//   * The score tile is computed transposed, S^T = K Q^T, so that each lane holds one
+//     query (lane % 32) and 16 keys per 32-key block: row max and row sum are lane-local
+//     plus one v_permlane32_swap between lanes l and l^32.
+//   * The output is accumulated transposed, O^T += V^T P^T, so the per-query rescale is
+//     lane-local too. The probabilities leave the S^T accumulator already in the B-operand
+//     layout of the next MFMA (keys are consumed in a permuted order, matched on the V side).
+//   * V^T operands come straight from the row-major V tile with ds_read_b64_tr_b16.
+//   * K/V tiles are double-buffered in LDS with a 16-byte-chunk XOR swizzle; the next
+//     tile's global loads are in flight while the current tile is computed.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa.h"
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kWaves = 8;              // wavefronts per workgroup (two per SIMD)
+constexpr int kBr = 32 * kWaves;       // query rows per workgroup
+constexpr int kBc = 64;                // keys per K/V tile
+constexpr int kThreads = kWave * kWaves;
+constexpr float kRescaleThreshold = 8.0f;  // log2 units: rescale once a max grows by > 2^8
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, Hkv, N;
+  int group;            // H / Hkv
+  int num_qtiles;       // ceil(N / kBr)
+  int total;            // workgroups in the grid: num_qtiles * H * B
+  float c;              // scale * log2(e): score -> base-2 exponent
+};
+
+// Workgroups are handed to the 8 XCDs round-robin (workgroup L runs on XCD L % 8), and
+// each XCD has its own L2. Reorder so that XCD x receives one contiguous range of the
+// logical work list, in which consecutive entries share K/V: the logical order is
+// (batch, K/V head, query tile, query head within the group), query tiles longest first
+// under the causal mask.
+struct TileCoord {
+  int b, h, qt;
+};
+__device__ __forceinline__ TileCoord tile_of_workgroup(const FwdArgs& a, int L, bool causal) {
+  const int xcd = L & 7, slot = L >> 3;
+  const int per = a.total >> 3, rem = a.total & 7;
+  const int logical = xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+  const int gm = logical % a.group;
+  int t = logical / a.group;
+  int qt = t % a.num_qtiles;
+  t /= a.num_qtiles;
+  const int hk = t % a.Hkv;
+  const int b = t / a.Hkv;
+  if (causal) qt = a.num_qtiles - 1 - qt;
+  return {b, hk * a.group + gm, qt};
+}
+
+// ---- element types ----------------------------------------------------------------
+struct Bf16Ops {
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ unsigned pack2(float x, float y) {
+    bf16x2 r = {(__bf16)x, (__bf16)y};  // v_cvt_pk_bf16_f32, round to nearest even
+    return __builtin_bit_cast(unsigned, r);
+  }
+};
+struct F16Ops {
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ unsigned pack2(float x, float y) {
+    f16x2 r = {(_Float16)x, (_Float16)y};  // v_cvt_pk_f16_f32, round to nearest even
+    return __builtin_bit_cast(unsigned, r);
+  }
+};
+
+// ---- LDS tile layout ----------------------------------------------------------------
+// A K or V tile is kBc rows of D 16-bit elements. Row r keeps its 16-byte chunks in
+// XOR-permuted order: logical chunk c sits at physical chunk c ^ swz(r). For D = 128 the
+// permutation gives 16 consecutive rows 16 distinct chunk positions for a fixed logical
+// chunk (the K reads) and makes every aligned group of 4 rows read by ds_read_b64_tr_b16
+// hit disjoint banks.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) {
+    const int x = r & 3;
+    return ((x << 1) ^ (x << 2)) ^ ((r >> 2) & 3);
+  } else {
+    return r & 7;
+  }
+}
+template <int D>
+__device__ __forceinline__ int lds_elem(int row, int col) {  // element offset of (row, col)
+  return row * D + (((col >> 3) ^ swz<D>(row)) << 3) + (col & 7);
+}
+
+__device__ __forceinline__ float pair_max(float x) {  // max over lanes l and l^32
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {  // sum over lanes l and l^32
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---- the forward kernel for 16-bit inputs -------------------------------------------
+template <typename Ops, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
+  constexpr int kChunks = D / 8;                  // 16-byte chunks per row
+  constexpr int kTileChunks = kBc * kChunks;
+  constexpr int kPerThread = kTileChunks / kThreads;
+  constexpr int kKsteps = D / 16;                 // MFMA k-steps over d for S^T
+  constexpr int kDblocks = D / 32;                // 32-row blocks of O^T
+  constexpr int kKb = kBc / 32;                   // 32-key blocks per tile
+  static_assert(kTileChunks % kThreads == 0, "tile must split evenly over the workgroup");
+
+  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kBc * D];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kBc * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+
+  const TileCoord tc = tile_of_workgroup(a, blockIdx.x, CAUSAL);
+  const int b = tc.b, h = tc.h, qt = tc.qt;
+  const int hk = h / a.group;
+  const int N = a.N;
+  const int q0 = qt * kBr;
+  const int qw0 = q0 + wave * 32;                 // this wavefront's first query
+  const int qi = qw0 + l32;                       // this lane's query
+
+  const size_t q_row_stride = (size_t)a.H * D;
+  const size_t kv_row_stride = (size_t)a.Hkv * D;
+  const uint16_t* qp = (const uint16_t*)a.q + ((size_t)b * N) * q_row_stride + (size_t)h * D;
+  const uint16_t* kp = (const uint16_t*)a.k + ((size_t)b * N) * kv_row_stride + (size_t)hk * D;
+  const uint16_t* vp = (const uint16_t*)a.v + ((size_t)b * N) * kv_row_stride + (size_t)hk * D;
+
+  // Q^T operand: lane holds q[qi][ks*16 + hi*8 .. +7] for every k-step
+  // rows past the end are read from row N-1 (in bounds) and never stored
+  u32x4 qreg[kKsteps];
+  const int qi_ld = min(qi, N - 1);
+#pragma unroll
+  for (int ks = 0; ks < kKsteps; ++ks)
+    qreg[ks] = *(const u32x4*)(qp + (size_t)qi_ld * q_row_stride + ks * 16 + hi * 8);
+
+  const int kv_end = CAUSAL ? min(N, q0 + kBr) : N;
+  const int ntiles = (kv_end + kBc - 1) / kBc;
+
+  u32x4 kst[kPerThread], vst[kPerThread];
+  auto load_tile = [&](int j) {
+    const int j0 = j * kBc;
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      const int id = tid + u * kThreads;
+      const int row = id / kChunks, ch = id % kChunks;
+      // keys past the end read row N-1: their scores are masked to -inf, so they add
+      // exp2(-inf) = 0 times a finite V row
+      const int key = min(j0 + row, N - 1);
+      kst[u] = *(const u32x4*)(kp + (size_t)key * kv_row_stride + ch * 8);
+      vst[u] = *(const u32x4*)(vp + (size_t)key * kv_row_stride + ch * 8);
+    }
+  };
+  auto store_tile = [&](int stage) {
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+      const int id = tid + u * kThreads;
+      const int row = id / kChunks, ch = id % kChunks;
+      const int off = lds_elem<D>(row, ch * 8);
+      *(u32x4*)&lds_k[stage][off] = kst[u];
+      *(u32x4*)&lds_v[stage][off] = vst[u];
+    }
+  };
+
+  f32x16 oacc[kDblocks];
+#pragma unroll
+  for (int i = 0; i < kDblocks; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[i][e] = 0.0f;
+  float m_run = -INFINITY;   // running max, base-2 exponent units (score * c)
+  float l_run = 0.0f;        // this lane's part of the running denominator
+
+  load_tile(0);
+  store_tile(0);
+  // Drain every outstanding load here (Q included) so that no wait for Q is left inside
+  // the loop, where it would also wait for the next tile's prefetch.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int j = 0; j < ntiles; ++j) {
+    const int stage = j & 1;
+    const int j0 = j * kBc;
+    if (j + 1 < ntiles) load_tile(j + 1);
+
+    // wavefront-uniform: does any key of this tile lie after every query of this wave?
+    const bool wave_active = !CAUSAL || j0 <= qw0 + 31;
+    if (wave_active) {
+      const uint16_t* kt = lds_k[stage];
+      const uint16_t* vt = lds_v[stage];
+      // ---- S^T = K Q^T ----
+      f32x16 s[kKb];
+#pragma unroll
+      for (int kb = 0; kb < kKb; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[kb][e] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < kKsteps; ++ks) {
+#pragma unroll
+        for (int kb = 0; kb < kKb; ++kb) {
+          const u32x4 ka = *(const u32x4*)&kt[lds_elem<D>(kb * 32 + l32, ks * 16 + hi * 8)];
+          s[kb] = Ops::mfma(ka, qreg[ks], s[kb]);
+        }
+      }
+      // ---- mask (diagonal tiles and the ragged last tile only) ----
+      const bool need_mask = (j0 + kBc > N) || (CAUSAL && j0 + kBc - 1 > qw0);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < kKb; ++kb)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int key = j0 + kb * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
+            const bool dead = key >= N || (CAUSAL && key > qi);
+            s[kb][e] = dead ? -INFINITY : s[kb][e];
+          }
+      }
+      // ---- online softmax ----
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < kKb; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
+      mx = pair_max(mx) * a.c;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleThreshold) != 0) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < kDblocks; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+      }
+      u32x4 p[kKb][2];
+      float lsum = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < kKb; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const int e = hf * 8 + e2 * 2;
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], a.c, -m_run));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e + 1], a.c, -m_run));
+            lsum += p0 + p1;
+            p[kb][hf][e2] = Ops::pack2(p0, p1);
+          }
+      l_run += lsum;
+      // ---- O^T += V^T P^T ----
+#pragma unroll
+      for (int db = 0; db < kDblocks; ++db) {
+#pragma unroll
+        for (int kk = 0; kk < 2 * kKb; ++kk) {
+          const int kb = kk >> 1, hf = kk & 1;
+          const int i16 = lane & 15;
+          const int dim = db * 32 + (lane & 16) + (i16 & 3) * 4;
+          u32x4 va;
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            const int row = kb * 32 + hf * 16 + r * 8 + hi * 4 + (i16 >> 2);
+            const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(vt + lds_elem<D>(row, dim)));
+            const u32x2 tu = __builtin_bit_cast(u32x2, t);
+            va[2 * r] = tu[0];
+            va[2 * r + 1] = tu[1];
+          }
+          oacc[db] = Ops::mfma(va, p[kb][hf], oacc[db]);
+        }
+      }
+    }
+    if (j + 1 < ntiles) store_tile(stage ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalise once, write O and lse ----
+  const float l_tot = pair_sum(l_run);
+  if (qi < N) {
+    const float inv = 1.0f / l_tot;
+    uint16_t* op = (uint16_t*)a.o + ((size_t)b * N + qi) * q_row_stride + (size_t)h * D;
+#pragma unroll
+    for (int db = 0; db < kDblocks; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dim = db * 32 + g * 8 + hi * 4;
+        u32x2 w;
+        w[0] = Ops::pack2(oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv);
+        w[1] = Ops::pack2(oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv);
+        *(u32x2*)(op + dim) = w;
+      }
+    if (hi == 0) a.lse[((size_t)b * a.H + h) * N + qi] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  }
+}
+
+// ---- host side -------------------------------------------------------------------------
+bool aligned(const void* p, size_t n) { return ((uintptr_t)p % n) == 0; }
+
+fa_status check_sizes(int B, int H, int Hkv, int N, int d, int causal, fa_dtype dtype) {
+  if (B < 1 || H < 1 || Hkv < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
+  if (Hkv > H || H % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP8_E4M3)
+    return FA_ERR_INVALID_ARG;
+  const long long q_elems = (long long)B * N * H * d;
+  if (q_elems >= (1LL << 31)) return FA_ERR_INVALID_ARG;
+  const long long grid = ((long long)N + kBr - 1) / kBr * H * B;
+  if (grid > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+template <typename Ops, int D, bool CAUSAL>
+fa_status launch(const FwdArgs& args, hipStream_t stream) {
+  hipLaunchKernelGGL((fa_fwd_kernel<Ops, D, CAUSAL>), dim3(args.total), dim3(kThreads), 0, stream, args);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+template <typename Ops>
+fa_status dispatch(const FwdArgs& args, int d, int causal, hipStream_t stream) {
+  if (d == 128) return causal ? launch<Ops, 128, true>(args, stream) : launch<Ops, 128, false>(args, stream);
+  return causal ? launch<Ops, 64, true>(args, stream) : launch<Ops, 64, false>(args, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int Hkv, int N, int d, int causal, float scale, fa_dtype dtype,
+                 const float* descale_qkv, void* stream) {
+  fa_status st = check_sizes(B, H, Hkv, N, d, causal, dtype);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  if (dtype == FA_DTYPE_FP8_E4M3) {
+    if (!descale_qkv) return FA_ERR_INVALID_ARG;
+    for (int i = 0; i < 3; ++i)
+      if (!std::isfinite(descale_qkv[i]) || !(descale_qkv[i] > 0.0f)) return FA_ERR_INVALID_ARG;
+  } else if (descale_qkv) {
+    return FA_ERR_INVALID_ARG;
+  }
+  FwdArgs args;
+  args.q = q;
+  args.k = k;
+  args.v = v;
+  args.o = o;
+  args.lse = lse;
+  args.B = B;
+  args.H = H;
+  args.Hkv = Hkv;
+  args.N = N;
+  args.group = H / Hkv;
+  args.num_qtiles = (N + kBr - 1) / kBr;
+  args.total = args.num_qtiles * H * B;
+  args.c = (float)((double)scale * 1.4426950408889634);
+  hipStream_t s = (hipStream_t)stream;
+  switch (dtype) {
+    case FA_DTYPE_BF16: return dispatch<Bf16Ops>(args, d, causal, s);
+    case FA_DTYPE_F16: return dispatch<F16Ops>(args, d, causal, s);
+    default: return FA_ERR_UNSUPPORTED;
+  }
+}
+
+fa_status fa_fwd_query(int B, int H, int Hkv, int N, int d, int causal, fa_dtype dtype,
+                       size_t* q_bytes, size_t* kv_bytes, size_t* o_bytes, size_t* lse_bytes,
+                       size_t* workspace_bytes) {
+  fa_status st = check_sizes(B, H, Hkv, N, d, causal, dtype);
+  if (st != FA_OK) return st;
+  const size_t in_size = dtype == FA_DTYPE_FP8_E4M3 ? 1 : 2;
+  if (q_bytes) *q_bytes = (size_t)B * N * H * d * in_size;
+  if (kv_bytes) *kv_bytes = (size_t)B * N * Hkv * d * in_size;
+  if (o_bytes) *o_bytes = (size_t)B * N * H * d * 2;
+  if (lse_bytes) *lse_bytes = (size_t)B * H * N * sizeof(float);
+  if (workspace_bytes) *workspace_bytes = 0;
+  return FA_OK;
+}
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported configuration";
+    case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
+  }
+  return "unknown fa_status";
+}
+
+int fa_version(void) { return 100; }
+
+}  // extern "C"

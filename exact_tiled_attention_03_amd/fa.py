@@ -1,0 +1,120 @@
+"""Python binding of libfa.so (include/fa.h). Argument marshalling only: every step of
+the attention forward runs in the library's gfx950 kernels; torch provides device
+memory and the current stream. There is no fallback path: if the library is missing,
+every call raises."""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libfa.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH = 0, 1, 2, 3
+FA_DTYPE_F16, FA_DTYPE_BF16, FA_DTYPE_FP8_E4M3 = 0, 1, 2
+DTYPE_NAMES = {"f16": FA_DTYPE_F16, "bf16": FA_DTYPE_BF16, "e4m3": FA_DTYPE_FP8_E4M3}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(f"{LIB_PATH} is missing: build it with exact_tiled_attention_03_amd.build.build()")
+            L = ctypes.CDLL(LIB_PATH)
+            c_int, c_float, vp = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+            szp = ctypes.POINTER(ctypes.c_size_t)
+            L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int,
+                                 c_float, c_int, ctypes.POINTER(c_float), vp]
+            L.fa_fwd.restype = c_int
+            L.fa_fwd_query.argtypes = [c_int] * 7 + [szp] * 5
+            L.fa_fwd_query.restype = c_int
+            L.fa_status_string.argtypes = [c_int]
+            L.fa_status_string.restype = ctypes.c_char_p
+            L.fa_version.argtypes = []
+            L.fa_version.restype = c_int
+            _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().fa_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(lib().fa_version())
+
+
+def _check(status: int):
+    if status != FA_OK:
+        raise FaError(status, status_string(status))
+
+
+def fa_fwd(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int, Hkv: int,
+           N: int, d: int, causal: int, scale: float, dtype: int, descale=None, stream: int = 0) -> int:
+    """Direct call of fa_fwd with raw pointers; returns the status code."""
+    ds = (ctypes.c_float * 3)(*descale) if descale is not None else None
+    return int(lib().fa_fwd(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Hkv, N, d, int(causal),
+                            float(scale), int(dtype), ds, stream))
+
+
+def fa_fwd_query(B: int, H: int, Hkv: int, N: int, d: int, causal: int, dtype: int) -> dict:
+    """Byte sizes of q, k/v, o, lse and the workspace (always 0); raises on bad sizes."""
+    out = [ctypes.c_size_t(0) for _ in range(5)]
+    _check(lib().fa_fwd_query(B, H, Hkv, N, d, int(causal), int(dtype), *[ctypes.byref(x) for x in out]))
+    return dict(zip(("q", "kv", "o", "lse", "workspace"), (x.value for x in out)))
+
+
+def _dtype_code(t, dtype):
+    import torch
+    if dtype is not None:
+        return DTYPE_NAMES[dtype]
+    return {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16,
+            torch.float8_e4m3fn: FA_DTYPE_FP8_E4M3}[t.dtype]
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, descale=None, dtype: str | None = None,
+        out=None, lse=None, stream=None):
+    """Attention forward on device tensors.
+
+    q [B,N,H,d], k and v [B,N,Hkv,d], contiguous, on one GPU; element type float16,
+    bfloat16 or float8_e4m3fn (uint8 tensors with dtype="e4m3" are also accepted;
+    e4m3 needs descale=(dq, dk, dv)). Returns (o [B,N,H,d], lse [B,H,N] float32);
+    o has q's type for 16-bit inputs and bfloat16 for e4m3. Enqueues on the current
+    stream (or `stream`) and returns without synchronising."""
+    import torch
+    code = _dtype_code(q, dtype)
+    B, N, H, d = q.shape
+    Hkv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out_dtype = torch.bfloat16 if code == FA_DTYPE_FP8_E4M3 else q.dtype
+    if out is None:
+        out = torch.empty((B, N, H, d), dtype=out_dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    for t in (q, k, v, out, lse):
+        if not t.is_contiguous() or t.device != q.device:
+            raise ValueError("tensors must be contiguous and on the same device")
+    if tuple(k.shape) != (B, N, Hkv, d) or tuple(v.shape) != (B, N, Hkv, d):
+        raise ValueError("k and v must be [B,N,Hkv,d] matching q")
+    if tuple(out.shape) != (B, N, H, d) or out.dtype != out_dtype or tuple(lse.shape) != (B, H, N):
+        raise ValueError("out/lse have the wrong shape or type")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Hkv, N, d,
+                int(bool(causal)), scale, code, descale, stream)
+    _check(st)
+    return out, lse

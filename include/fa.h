@@ -1,0 +1,103 @@
+/*
+ * fa.h -- C ABI of the exact tiled attention forward library (libfa.so, gfx950).
+ *
+ * The operation. For every batch b, query head h and query position i:
+ *     s_ij   = scale * <q_i, k_j>                       (j over the visible keys)
+ *     O_i    = sum_j softmax_j(s_i.) v_j
+ *     lse_i  = ln sum_j exp(s_ij)
+ * This is standard attention as defined on the page "FlashAttention: The Algorithm
+ * That Made Long-Context AI Possible" (section "The quadratic bottleneck in standard
+ * attention"), computed the I/O-aware way described in the abstract of "FlashAttention:
+ * Fast and Memory-Efficient Exact Attention with IO-Awareness" and the section "What
+ * tiling changes" of the first page: key/value tiles stream through on-chip memory, a
+ * running row maximum and running exponential sum replace the full softmax, and the
+ * N x N score matrix never reaches device memory. The work is split over workgroups
+ * per (batch, head, query tile) and, inside a workgroup, per wavefront over disjoint
+ * query rows, as in the abstract of "FlashAttention-2: Faster Attention with Better
+ * Parallelism and Work Partitioning" (items 2 and 3). The pages leave the following
+ * open; the library takes these readings:
+ *   - `scale` multiplies the scores before the softmax;
+ *   - causal masking keeps key j for query i iff j <= i (square, no offset);
+ *   - grouped-query attention: query head h reads key/value head h / (H / Hkv);
+ *   - lse is the natural log of the softmax denominator over the scaled scores;
+ *   - e4m3 inputs (the low-precision mode in the abstract of "FlashAttention-3: Fast
+ *     and Accurate Attention with Asynchrony and Low-precision") carry one descale per
+ *     tensor: the logical value of an element is its e4m3 value times the descale.
+ *
+ * Layouts (row-major, contiguous, element strides implied by the shape):
+ *     q, o : [B][N][H][d]        k, v : [B][N][Hkv][d]        lse : [B][H][N] float32
+ * Element types: F16 -> q, k, v, o are IEEE binary16; BF16 -> bfloat16; FP8_E4M3 ->
+ * q, k, v are OCP E4M3 ("fn", max 448) and o is bfloat16. Accumulation is float32.
+ *
+ * Ownership and execution. The caller owns every buffer (device memory). The library
+ * allocates nothing, frees nothing and never synchronises: fa_fwd validates its
+ * arguments on the host, enqueues one kernel on `stream` (a hipStream_t; NULL is the
+ * null stream) and returns. A fault inside the kernel surfaces at the caller's next
+ * synchronisation. q, k, v are only read; o and lse are fully overwritten; o and lse
+ * must not overlap q, k, v or each other. No workspace is needed: memory use is linear
+ * in N. The library keeps no state and may be called from several threads.
+ *
+ * Errors. Every precondition is checked on the host before any HIP call; on error
+ * nothing is enqueued and the outputs are untouched.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size, bad flag, bad scale */
+  FA_ERR_UNSUPPORTED = 2,   /* valid request the kernels do not implement (e.g. d) */
+  FA_ERR_LAUNCH = 3         /* the HIP runtime rejected the launch */
+} fa_status;
+
+typedef enum {
+  FA_DTYPE_F16 = 0,
+  FA_DTYPE_BF16 = 1,
+  FA_DTYPE_FP8_E4M3 = 2
+} fa_dtype;
+
+/*
+ * Attention forward.
+ *   q, k, v   device pointers, layouts above, 16-byte aligned.
+ *   o         device pointer, [B][N][H][d] of the output type, 16-byte aligned.
+ *   lse       device pointer, [B][H][N] float32, 4-byte aligned.
+ *   B, H, Hkv, N, d   sizes: B >= 1, N >= 1, 1 <= Hkv <= H, H % Hkv == 0,
+ *             d in {64, 128}; every tensor must have fewer than 2^31 elements.
+ *   causal    0 (no mask) or 1 (key j visible to query i iff j <= i).
+ *   scale     finite, > 0; multiplies q.k before the softmax (1/sqrt(d) is usual).
+ *   dtype     element type of q, k, v (see above).
+ *   descale_qkv  FP8_E4M3 only: host pointer to three finite, positive floats
+ *             (descale of q, k, v); must be NULL for the other types.
+ *   stream    hipStream_t to enqueue on (NULL = null stream).
+ * Returns FA_OK once the kernel is enqueued.
+ */
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                 int B, int H, int Hkv, int N, int d, int causal, float scale,
+                 fa_dtype dtype, const float* descale_qkv, void* stream);
+
+/*
+ * Shape query: byte sizes of every buffer fa_fwd reads or writes for these arguments,
+ * after the same size checks fa_fwd makes. Any output pointer may be NULL.
+ * workspace_bytes is always 0 (no scratch memory). Pure host function.
+ */
+fa_status fa_fwd_query(int B, int H, int Hkv, int N, int d, int causal, fa_dtype dtype,
+                       size_t* q_bytes, size_t* kv_bytes, size_t* o_bytes, size_t* lse_bytes,
+                       size_t* workspace_bytes);
+
+/* Static, human-readable text for a status code. */
+const char* fa_status_string(fa_status s);
+
+/* Library version, encoded as major * 10000 + minor * 100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,105 @@
+"""The C-ABI library on the host (CPU only): it loads, exports every function that
+include/fa.h declares, and rejects bad arguments before touching HIP. No call here
+reaches a kernel launch: every fa_fwd call has an argument the host checks reject."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_tiled_attention_03_amd as fa
+from exact_tiled_attention_03_amd import fa as binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+FAKE = 1 << 20     # aligned, non-null host address; only ever paired with an invalid argument
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) >= {"fa_fwd", "fa_fwd_query", "fa_status_string", "fa_version"}
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), f"libfa.so does not export {n}"
+
+
+def test_version_and_status_strings():
+    assert fa.version() >= 100
+    for s in range(4):
+        assert fa.status_string(s).startswith("FA_")
+    assert "unknown" in fa.status_string(99)
+
+
+def test_query_sizes():
+    q = fa.fa_fwd_query(4, 32, 8, 8192, 128, 1, fa.FA_DTYPE_BF16)
+    assert q == {"q": 4 * 8192 * 32 * 128 * 2, "kv": 4 * 8192 * 8 * 128 * 2, "o": 4 * 8192 * 32 * 128 * 2,
+                 "lse": 4 * 32 * 8192 * 4, "workspace": 0}
+    q8 = fa.fa_fwd_query(8, 16, 16, 4096, 128, 0, fa.FA_DTYPE_FP8_E4M3)
+    assert q8["q"] == 8 * 4096 * 16 * 128 and q8["o"] == 2 * q8["q"] and q8["workspace"] == 0
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H=0), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=3), fa.FA_ERR_INVALID_ARG),           # H % Hkv != 0
+    (dict(Hkv=8, H=4), fa.FA_ERR_INVALID_ARG),      # Hkv > H
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=0), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=7), fa.FA_ERR_INVALID_ARG),
+    (dict(B=1 << 20, N=1 << 12), fa.FA_ERR_INVALID_ARG),   # more than 2^31 elements
+])
+def test_query_rejects(args, status):
+    a = dict(B=1, H=4, Hkv=2, N=64, d=128, causal=0, dtype=fa.FA_DTYPE_BF16)
+    a.update(args)
+    with pytest.raises(fa.FaError) as e:
+        fa.fa_fwd_query(a["B"], a["H"], a["Hkv"], a["N"], a["d"], a["causal"], a["dtype"])
+    assert e.value.status == status
+
+
+def _call(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=4, Hkv=2, N=64, d=128, causal=0,
+             scale=0.125, dtype=fa.FA_DTYPE_BF16, descale=None)
+    a.update(over)
+    return fa.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"], a["d"],
+                     a["causal"], a["scale"], a["dtype"], a["descale"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(k=0), fa.FA_ERR_INVALID_ARG),
+    (dict(v=0), fa.FA_ERR_INVALID_ARG),
+    (dict(o=0), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=0), fa.FA_ERR_INVALID_ARG),
+    (dict(q=FAKE + 8), fa.FA_ERR_INVALID_ARG),      # not 16-byte aligned
+    (dict(o=FAKE + 4), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=FAKE + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=fa.FA_DTYPE_FP8_E4M3, descale=None), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=fa.FA_DTYPE_FP8_E4M3, descale=(1.0, 0.0, 1.0)), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=fa.FA_DTYPE_FP8_E4M3, descale=(1.0, float("nan"), 1.0)), fa.FA_ERR_INVALID_ARG),
+    (dict(descale=(1.0, 1.0, 1.0)), fa.FA_ERR_INVALID_ARG),   # descale with a 16-bit type
+    (dict(Hkv=3), fa.FA_ERR_INVALID_ARG),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=-5), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=-1), fa.FA_ERR_INVALID_ARG),
+])
+def test_fwd_rejects_before_launch(over, status):
+    assert _call(**over) == status
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "absent.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.lib()

@@ -1,0 +1,141 @@
+"""Parity of the HIP path with the fp64 oracle on the same seeded inputs (GPU).
+
+Small and ragged shapes are compared element by element over the whole output;
+the full-size workloads are compared on sampled rows the oracle computes one by one,
+in the same launch configuration the benchmark times. Tolerances (elementwise, fp32
+accumulation): |dO| <= 2e-3 (f16), 1e-2 (bf16), 6e-2 (e4m3, bf16 out) times
+max(1, |O_ref|); |dlse| <= 1e-3."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+SMALL = [
+    # dtype, B, H, Hkv, N, d, causal
+    ("f16", 1, 2, 2, 128, 64, False),
+    ("f16", 1, 2, 2, 128, 64, True),
+    ("bf16", 2, 4, 2, 200, 128, False),
+    ("bf16", 2, 4, 2, 200, 128, True),
+    ("bf16", 1, 3, 1, 333, 64, False),
+    ("bf16", 1, 3, 1, 333, 64, True),
+    ("f16", 2, 4, 4, 257, 128, True),
+    ("f16", 1, 2, 1, 300, 128, False),
+    ("bf16", 1, 8, 2, 1024, 128, True),
+    ("bf16", 1, 4, 4, 640, 128, False),
+] + [("bf16", 1, 2, 2, n, d, c) for n in (1, 2, 3, 17, 100, 129) for d in (64, 128) for c in (False, True)]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "-".join(map(str, c)))
+def test_small_full_parity(case):
+    dtype, B, H, Hkv, N, d, causal = case
+    _log(f"[small] {case}")
+    scale = 1.0 / np.sqrt(d)
+    inp = synth_inputs.make_inputs(B, H, Hkv, N, d, dtype, seed=500 + N + d + H)
+    o, lse = gu.host(*gu.run(inp, dtype, causal, scale))
+    o_ref, lse_ref = oracle.attn_fwd(inp["q"], inp["k"], inp["v"], dtype, causal, scale)
+    gu.compare(o, o_ref, lse, lse_ref, dtype, str(case))
+
+
+@pytest.mark.parametrize("name", [n for n in synth_inputs.WORKLOADS if synth_inputs.WORKLOADS[n].dtype != "e4m3"])
+def test_workload_sampled_parity(name):
+    w = synth_inputs.WORKLOADS[name]
+    _log(f"[workload] {name}")
+    inp = synth_inputs.workload_inputs(w)
+    o_d, lse_d = gu.run(inp, w.dtype, w.causal, w.scale)
+    assert bool(torch.isfinite(o_d.float()).all()) and bool(torch.isfinite(lse_d).all())
+    if w.N <= 128:
+        o_ref, lse_ref = oracle.attn_fwd(inp["q"], inp["k"], inp["v"], w.dtype, w.causal, w.scale)
+        o_g, l_g = gu.host(o_d, lse_d)
+        gu.compare(o_g, o_ref, l_g, lse_ref, w.dtype, name)
+        return
+    rows = gu.sample_rows(w.B, w.H, w.N, n_random=40, seed=w.seed)
+    o_ref, lse_ref = oracle.attn_rows(inp["q"], inp["k"], inp["v"], w.dtype, w.causal, w.scale, rows)
+    o_g = o_d[rows[:, 0], rows[:, 2], rows[:, 1]].float().cpu().numpy().astype(np.float64)
+    l_g = lse_d[rows[:, 0], rows[:, 1], rows[:, 2]].cpu().numpy().astype(np.float64)
+    e = gu.compare(o_g, o_ref, l_g, lse_ref, w.dtype, name)
+    _log(f"[workload] {name}: max scaled dO {e[0]:.2e}, max |dO| {e[1]:.2e}, max dlse {e[2]:.2e}")
+
+
+def _dev(x, dtype):
+    bits = synth_inputs._round_bits(np.asarray(x, dtype=np.float32), dtype)
+    return bits, gu.to_dev(bits, dtype)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_query_gives_mean_of_values(causal):
+    B, N, H, Hkv, d = 1, 300, 2, 1, 128
+    inp = synth_inputs.make_inputs(B, H, Hkv, N, d, "bf16", seed=77)
+    inp["q"] = np.zeros_like(inp["q"])
+    o, lse = gu.host(*gu.run(inp, "bf16", causal, 0.1))
+    v = oracle.decode(inp["v"], "bf16")[:, :, 0, :]
+    ref = np.cumsum(v, axis=1) / np.arange(1, N + 1)[None, :, None] if causal else \
+        np.repeat(v.mean(axis=1, keepdims=True), N, axis=1)
+    for h in range(H):
+        gu.compare(o[:, :, h, :], ref, lse[:, h, :],
+                   np.log(np.arange(1, N + 1))[None] if causal else np.full((B, N), np.log(N)), "bf16",
+                   f"Q=0 causal={causal}")
+
+
+def test_constant_values_and_determinism():
+    B, N, H, Hkv, d = 2, 515, 4, 2, 128
+    inp = synth_inputs.make_inputs(B, H, Hkv, N, d, "bf16", seed=78)
+    c = np.linspace(-3, 3, d).astype(np.float32)
+    inp["v"] = synth_inputs._round_bits(np.broadcast_to(c, inp["v"].shape).copy(), "bf16")
+    cref = oracle.decode(inp["v"][0, 0, 0], "bf16")
+    for causal in (False, True):
+        o1, l1 = gu.run(inp, "bf16", causal, 0.09)
+        o2, l2 = gu.run(inp, "bf16", causal, 0.09)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), "two runs differ"
+        o = o1.float().cpu().numpy()
+        assert np.max(np.abs(o - cref) / np.maximum(1, np.abs(cref))) <= gu.TOL["bf16"]
+
+
+def test_gqa_equals_repeated_heads_bitwise():
+    B, N, H, Hkv, d = 1, 389, 8, 2, 128
+    inp = synth_inputs.make_inputs(B, H, Hkv, N, d, "bf16", seed=79)
+    rep = dict(inp)
+    rep["k"] = np.ascontiguousarray(np.repeat(inp["k"], H // Hkv, axis=2))
+    rep["v"] = np.ascontiguousarray(np.repeat(inp["v"], H // Hkv, axis=2))
+    for causal in (False, True):
+        o1, l1 = gu.run(inp, "bf16", causal, 0.088)
+        o2, l2 = gu.run(rep, "bf16", causal, 0.088)
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_key_permutation_invariance():
+    B, N, H, Hkv, d = 1, 256, 2, 2, 128
+    inp = synth_inputs.make_inputs(B, H, Hkv, N, d, "bf16", seed=80)
+    o1, l1 = gu.host(*gu.run(inp, "bf16", False, 0.088))
+    perm = np.random.default_rng(1).permutation(N)
+    p = dict(inp)
+    p["k"] = np.ascontiguousarray(inp["k"][:, perm])
+    p["v"] = np.ascontiguousarray(inp["v"][:, perm])
+    o2, l2 = gu.host(*gu.run(p, "bf16", False, 0.088))
+    assert np.max(np.abs(o1 - o2)) <= 2 * gu.TOL["bf16"] and np.max(np.abs(l1 - l2)) <= gu.LSE_TOL
+
+
+@pytest.mark.parametrize("scale", [2.0, 20.0])
+def test_large_scores_stay_finite_and_exact(scale):
+    # scores of magnitude up to ~1e3: the running maximum must keep exp2 in range
+    B, N, H, Hkv, d = 1, 333, 2, 2, 128
+    inp = synth_inputs.make_inputs(B, H, Hkv, N, d, "bf16", seed=81)
+    for causal in (False, True):
+        o, lse = gu.host(*gu.run(inp, "bf16", causal, scale))
+        o_ref, lse_ref = oracle.attn_fwd(inp["q"], inp["k"], inp["v"], "bf16", causal, scale)
+        # lse tolerance scales with the score magnitude (fp32 rounding of scores ~ |s| * 2^-24 * d)
+        tol_l = max(gu.LSE_TOL, 4e-6 * float(np.max(np.abs(lse_ref))))
+        assert np.all(np.isfinite(o)) and np.max(np.abs(lse - lse_ref)) <= tol_l
+        assert np.max(np.abs(o - o_ref) / np.maximum(1, np.abs(o_ref))) <= gu.TOL["bf16"]
