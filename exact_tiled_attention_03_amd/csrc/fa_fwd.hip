@@ -28,6 +28,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "fa.h"
 
@@ -109,13 +110,18 @@ struct F16Ops {
 };
 
 // ---- LDS tile layout ----------------------------------------------------------------
-// A K or V tile is kBc rows of D 16-bit elements. Row r keeps its 16-byte chunks in
-// XOR-permuted order: logical chunk c sits at physical chunk c ^ swz(r). For D = 128 the
-// permutation gives 16 consecutive rows 16 distinct chunk positions for a fixed logical
-// chunk (the K reads) and makes every aligned group of 4 rows read by ds_read_b64_tr_b16
-// hit disjoint banks.
+// K tile: kBc rows (keys) of D 16-bit elements, row-major like K in memory. Row r keeps
+// its 16-byte chunks in XOR-permuted order, logical chunk c at physical c ^ kswz(r), so
+// that 16 consecutive rows reading the same logical chunk hit 16 different bank groups.
+//
+// V tile: stored transposed as kBc/16 planes, one per group of 16 keys; plane g is D rows
+// (dims) of the group's 16 keys, 32 bytes per row. Inside a row the keys are stored in the
+// order in which a lane of the probability operand holds them: the lane with hi = lane/32
+// holds keys {4hi..4hi+3, 8+4hi..8+4hi+3} of the group, which form the 16-byte chunk hi.
+// The two chunks of row `dim` are swapped when bit 3 of dim is set, so that 16 lanes
+// reading 16 consecutive rows cover all 64 banks once.
 template <int D>
-__device__ __forceinline__ int swz(int r) {
+__device__ __forceinline__ int kswz(int r) {
   if constexpr (D == 128) {
     const int x = r & 3;
     return ((x << 1) ^ (x << 2)) ^ ((r >> 2) & 3);
@@ -123,9 +129,16 @@ __device__ __forceinline__ int swz(int r) {
     return r & 7;
   }
 }
+
 template <int D>
-__device__ __forceinline__ int lds_elem(int row, int col) {  // element offset of (row, col)
-  return row * D + (((col >> 3) ^ swz<D>(row)) << 3) + (col & 7);
+__device__ __forceinline__ int k_byte(int row, int col) {  // byte offset of K(row, col)
+  return row * D * 2 + ((((col >> 3) ^ kswz<D>(row)) << 4) | ((col & 7) << 1));
+}
+// byte offset, inside a V^T tile, of chunk c (stored positions 8c..8c+7) of row `dim` in
+// the plane of key group g
+template <int D>
+__device__ __forceinline__ int vt_byte(int g, int dim, int c) {
+  return g * (D * 32) + dim * 32 + ((c ^ ((dim >> 3) & 1)) << 4);
 }
 
 __device__ __forceinline__ float pair_max(float x) {  // max over lanes l and l^32
@@ -137,19 +150,25 @@ __device__ __forceinline__ float pair_sum(float x) {  // sum over lanes l and l^
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+typedef __attribute__((address_space(3))) unsigned char lds_byte;
+template <typename T>
+__device__ __forceinline__ T lds_load(const lds_byte* base, int byte_off) {
+  return *(const __attribute__((address_space(3))) T*)(base + byte_off);
+}
+template <int V>
+using ic = std::integral_constant<int, V>;
+
 // ---- the forward kernel for 16-bit inputs -------------------------------------------
 template <typename Ops, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
-  constexpr int kChunks = D / 8;                  // 16-byte chunks per row
-  constexpr int kTileChunks = kBc * kChunks;
-  constexpr int kPerThread = kTileChunks / kThreads;
+  constexpr int kChunks = D / 8;                  // 16-byte chunks per K row
   constexpr int kKsteps = D / 16;                 // MFMA k-steps over d for S^T
   constexpr int kDblocks = D / 32;                // 32-row blocks of O^T
   constexpr int kKb = kBc / 32;                   // 32-key blocks per tile
-  static_assert(kTileChunks % kThreads == 0, "tile must split evenly over the workgroup");
+  constexpr int kTileBytes = kBc * D * 2;
+  constexpr int kStageBytes = 2 * kTileBytes;     // K tile then V^T tile
 
-  __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kBc * D];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kBc * D];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kStageBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -171,8 +190,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
   const uint16_t* kp = (const uint16_t*)a.k + ((size_t)b * N) * kv_row_stride + (size_t)hk * D;
   const uint16_t* vp = (const uint16_t*)a.v + ((size_t)b * N) * kv_row_stride + (size_t)hk * D;
 
-  // Q^T operand: lane holds q[qi][ks*16 + hi*8 .. +7] for every k-step
-  // rows past the end are read from row N-1 (in bounds) and never stored
+  // Q^T operand: lane holds q[qi][ks*16 + hi*8 .. +7] for every k-step; rows past the
+  // end are read from row N-1 (in bounds) and never stored
   u32x4 qreg[kKsteps];
   const int qi_ld = min(qi, N - 1);
 #pragma unroll
@@ -182,28 +201,78 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
   const int kv_end = CAUSAL ? min(N, q0 + kBr) : N;
   const int ntiles = (kv_end + kBc - 1) / kBc;
 
-  u32x4 kst[kPerThread], vst[kPerThread];
+  // per-lane LDS byte offsets of the MFMA operands (stage 0, key block 0); the key block,
+  // the half and the stage only add compile-time constants
+  int koff[kKsteps];
+#pragma unroll
+  for (int ks = 0; ks < kKsteps; ++ks) koff[ks] = k_byte<D>(l32, ks * 16 + hi * 8);
+  int voff[kDblocks];
+#pragma unroll
+  for (int db = 0; db < kDblocks; ++db) voff[db] = kTileBytes + vt_byte<D>(0, db * 32 + l32, hi);
+
+  // Staging of the next tile. Wavefront w stages keys [8w, 8w+8) of the tile:
+  //   K: rows 8w.., each lane one 16-byte chunk per instruction (kKRows rows per
+  //      instruction), kept in memory order;
+  //   V: the 8 keys of stored chunk (w&1) of key group w>>1, i.e. keys
+  //      16(w>>1) + 4(w&1) + {0,1,2,3,8,9,10,11}; lane l holds dims 2l and 2l+1 of each
+  //      and transposes them into two 16-byte V^T chunks (one per dim).
+  // Row addresses are wavefront-uniform (scalar); only the last, ragged tile clamps rows
+  // past the end to row N-1 per lane.
+  constexpr int kKRows = kWave / kChunks;         // K rows per wavefront load
+  constexpr int kKLoads = 8 / kKRows;             // K loads per lane per tile
+  static_assert(kBc == 8 * kWaves, "each wavefront stages 8 keys");
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  // per-lane byte offsets from a wavefront-uniform row address (unsigned 32-bit, so the
+  // loads take the scalar-base form)
+  const unsigned k_lane_off = (unsigned)(lane / kChunks) * (unsigned)(kv_row_stride * 2) +
+                              (unsigned)(lane % kChunks) * 16u;
+  const unsigned v_lane_off = (unsigned)min(2 * lane, D - 2) * 2u;  // lanes past D/2 repeat
+  u32x4 kst[kKLoads];
+  unsigned vst[8];
   auto load_tile = [&](int j) {
     const int j0 = j * kBc;
+    if (j0 + kBc <= N) {
 #pragma unroll
-    for (int u = 0; u < kPerThread; ++u) {
-      const int id = tid + u * kThreads;
-      const int row = id / kChunks, ch = id % kChunks;
+      for (int u = 0; u < kKLoads; ++u) {
+        const char* rowp = (const char*)(kp + (size_t)(j0 + 8 * wv + u * kKRows) * kv_row_stride);
+        kst[u] = *(const u32x4*)(rowp + k_lane_off);
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int key = j0 + 16 * (wv >> 1) + 4 * (wv & 1) + (r & 3) + (r >> 2) * 8;
+        const char* rowp = (const char*)(vp + (size_t)key * kv_row_stride);
+        vst[r] = *(const unsigned*)(rowp + v_lane_off);
+      }
+    } else {
       // keys past the end read row N-1: their scores are masked to -inf, so they add
       // exp2(-inf) = 0 times a finite V row
-      const int key = min(j0 + row, N - 1);
-      kst[u] = *(const u32x4*)(kp + (size_t)key * kv_row_stride + ch * 8);
-      vst[u] = *(const u32x4*)(vp + (size_t)key * kv_row_stride + ch * 8);
+#pragma unroll
+      for (int u = 0; u < kKLoads; ++u) {
+        const int key = min(j0 + 8 * wv + u * kKRows + lane / kChunks, N - 1);
+        kst[u] = *(const u32x4*)(kp + (size_t)key * kv_row_stride + (lane % kChunks) * 8);
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int key = min(j0 + 16 * (wv >> 1) + 4 * (wv & 1) + (r & 3) + (r >> 2) * 8, N - 1);
+        const char* rowp = (const char*)(vp + (size_t)key * kv_row_stride);
+        vst[r] = *(const unsigned*)(rowp + v_lane_off);
+      }
     }
   };
   auto store_tile = [&](int stage) {
+    unsigned char* st = lds + stage * kStageBytes;
 #pragma unroll
-    for (int u = 0; u < kPerThread; ++u) {
-      const int id = tid + u * kThreads;
-      const int row = id / kChunks, ch = id % kChunks;
-      const int off = lds_elem<D>(row, ch * 8);
-      *(u32x4*)&lds_k[stage][off] = kst[u];
-      *(u32x4*)&lds_v[stage][off] = vst[u];
+    for (int u = 0; u < kKLoads; ++u)
+      *(u32x4*)(st + k_byte<D>(8 * wv + u * kKRows + lane / kChunks, (lane % kChunks) * 8)) = kst[u];
+    if (2 * lane < D) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const unsigned sel = e ? 0x07060302u : 0x05040100u;
+        u32x4 t;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) t[q] = __builtin_amdgcn_perm(vst[2 * q + 1], vst[2 * q], sel);
+        *(u32x4*)(st + kTileBytes + vt_byte<D>(wv >> 1, 2 * lane + e, wv & 1)) = t;
+      }
     }
   };
 
@@ -222,16 +291,15 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int stage = j & 1;
+  auto tile = [&](auto stage_c, int j) {
+    constexpr int stage = decltype(stage_c)::value;
     const int j0 = j * kBc;
     if (j + 1 < ntiles) load_tile(j + 1);
 
     // wavefront-uniform: does any key of this tile lie after every query of this wave?
     const bool wave_active = !CAUSAL || j0 <= qw0 + 31;
     if (wave_active) {
-      const uint16_t* kt = lds_k[stage];
-      const uint16_t* vt = lds_v[stage];
+      const lds_byte* st = (const lds_byte*)lds + stage * kStageBytes;
       // ---- S^T = K Q^T ----
       f32x16 s[kKb];
 #pragma unroll
@@ -242,7 +310,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
       for (int ks = 0; ks < kKsteps; ++ks) {
 #pragma unroll
         for (int kb = 0; kb < kKb; ++kb) {
-          const u32x4 ka = *(const u32x4*)&kt[lds_elem<D>(kb * 32 + l32, ks * 16 + hi * 8)];
+          const u32x4 ka = lds_load<u32x4>(st, koff[ks] + kb * 32 * D * 2);
           s[kb] = Ops::mfma(ka, qreg[ks], s[kb]);
         }
       }
@@ -290,31 +358,25 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
             p[kb][hf][e2] = Ops::pack2(p0, p1);
           }
       l_run += lsum;
-      // ---- O^T += V^T P^T ----
+      // ---- O^T += V^T P^T: the V^T operand of key group (kb, hf) is one 16-byte read ----
 #pragma unroll
       for (int db = 0; db < kDblocks; ++db) {
 #pragma unroll
         for (int kk = 0; kk < 2 * kKb; ++kk) {
           const int kb = kk >> 1, hf = kk & 1;
-          const int i16 = lane & 15;
-          const int dim = db * 32 + (lane & 16) + (i16 & 3) * 4;
-          u32x4 va;
-#pragma unroll
-          for (int r = 0; r < 2; ++r) {
-            const int row = kb * 32 + hf * 16 + r * 8 + hi * 4 + (i16 >> 2);
-            const s16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(vt + lds_elem<D>(row, dim)));
-            const u32x2 tu = __builtin_bit_cast(u32x2, t);
-            va[2 * r] = tu[0];
-            va[2 * r + 1] = tu[1];
-          }
+          const u32x4 va = lds_load<u32x4>(st, voff[db] + kk * (D * 32));
           oacc[db] = Ops::mfma(va, p[kb][hf], oacc[db]);
         }
       }
     }
     if (j + 1 < ntiles) store_tile(stage ^ 1);
     __syncthreads();
+  };
+  for (int j = 0; j < ntiles; j += 2) {
+    tile(ic<0>(), j);
+    if (j + 1 < ntiles) tile(ic<1>(), j + 1);
   }
+
 
   // ---- epilogue: normalise once, write O and lse ----
   const float l_tot = pair_sum(l_run);
