@@ -48,9 +48,10 @@ constexpr int kWaves = 8;              // wavefronts per workgroup (two per SIMD
 constexpr int kBr = 32 * kWaves;       // query rows per workgroup
 constexpr int kBc = 64;                // keys per K/V tile
 constexpr int kThreads = kWave * kWaves;
-constexpr float kRescaleThreshold = 8.0f;  // log2 units: rescale once a max grows by > 2^8
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+// word 3 of a raw buffer descriptor on gfx9-family GPUs: 32-bit data format, no swizzle
+constexpr int kBufferWord3 = 0x00020000;
 
 struct FwdArgs {
   const void* q;
@@ -89,6 +90,7 @@ __device__ __forceinline__ TileCoord tile_of_workgroup(const FwdArgs& a, int L, 
 
 // ---- element types ----------------------------------------------------------------
 struct Bf16Ops {
+  static constexpr float kPMax = 32768.0f;   // bound on stored probabilities (bf16 range is wider)
   static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -99,6 +101,7 @@ struct Bf16Ops {
   }
 };
 struct F16Ops {
+  static constexpr float kPMax = 32768.0f;   // below the largest finite f16, 65504
   static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
@@ -148,6 +151,44 @@ __device__ __forceinline__ float pair_max(float x) {  // max over lanes l and l^
 __device__ __forceinline__ float pair_sum(float x) {  // sum over lanes l and l^32
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Reductions over a lane's scores written as balanced trees: a single wavefront runs the
+// softmax on its SIMD while the other issues MFMAs, so dependent-issue latency, not
+// throughput, bounds these chains.
+template <int KB>
+__device__ __forceinline__ float tree_max(const f32x16 (&x)[KB]) {
+  float t[KB * 16];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) t[kb * 16 + e] = x[kb][e];
+  int n = KB * 16;
+#pragma unroll
+  for (int lvl = 0; lvl < 6; ++lvl) {
+    if (n <= 1) break;
+    int m = 0;
+#pragma unroll
+    for (int i = 0; i + 2 < n; i += 3) t[m++] = fmaxf(fmaxf(t[i], t[i + 1]), t[i + 2]);
+    const int rem = n % 3;
+    if (rem == 1) t[m++] = t[n - 1];
+    if (rem == 2) t[m++] = fmaxf(t[n - 2], t[n - 1]);
+    n = m;
+  }
+  return t[0];
+}
+template <int KB>
+__device__ __forceinline__ float tree_sum(const f32x16 (&x)[KB]) {
+  float t[KB * 16];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) t[kb * 16 + e] = x[kb][e];
+#pragma unroll
+  for (int w = KB * 8; w >= 1; w >>= 1)
+#pragma unroll
+    for (int i = 0; i < w; ++i) t[i] = t[i] + t[i + w];
+  return t[0];
 }
 
 typedef __attribute__((address_space(3))) unsigned char lds_byte;
@@ -210,60 +251,66 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int db = 0; db < kDblocks; ++db) voff[db] = kTileBytes + vt_byte<D>(0, db * 32 + l32, hi);
 
-  // Staging of the next tile. Wavefront w stages keys [8w, 8w+8) of the tile:
-  //   K: rows 8w.., each lane one 16-byte chunk per instruction (kKRows rows per
-  //      instruction), kept in memory order;
+  // ---- staging of one LDS slot ----------------------------------------------------------
+  // Slot j holds the K tile of key tile j and the V^T tile of key tile j-1 (see the
+  // schedule below). Wavefront w stages keys [8w, 8w+8) of each tile:
+  //   K: rows 8w.., each lane one 16-byte chunk per load (kKRows rows per load), kept in
+  //      memory order;
   //   V: the 8 keys of stored chunk (w&1) of key group w>>1, i.e. keys
   //      16(w>>1) + 4(w&1) + {0,1,2,3,8,9,10,11}; lane l holds dims 2l and 2l+1 of each
   //      and transposes them into two 16-byte V^T chunks (one per dim).
-  // Row addresses are wavefront-uniform (scalar); only the last, ragged tile clamps rows
-  // past the end to row N-1 per lane.
+  // Row addresses are wavefront-uniform; only a ragged last tile clamps rows past the end
+  // to row N-1 per lane (such keys are masked to -inf, so they add exp2(-inf) = 0 times a
+  // finite V row).
   constexpr int kKRows = kWave / kChunks;         // K rows per wavefront load
   constexpr int kKLoads = 8 / kKRows;             // K loads per lane per tile
   static_assert(kBc == 8 * kWaves, "each wavefront stages 8 keys");
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  // per-lane byte offsets from a wavefront-uniform row address (unsigned 32-bit, so the
-  // loads take the scalar-base form)
-  const unsigned k_lane_off = (unsigned)(lane / kChunks) * (unsigned)(kv_row_stride * 2) +
-                              (unsigned)(lane % kChunks) * 16u;
+  // K and V of this (batch, K/V head) are read through buffer descriptors (scalar base,
+  // 32-bit lane offset, scalar row offset), so that staging needs no per-lane 64-bit
+  // addresses; the descriptor's extent is exactly N rows, a hardware bound on top of
+  // the row clamping below
+  const unsigned row_bytes = (unsigned)(kv_row_stride * 2);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, (int)(row_bytes * (unsigned)N), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vp, 0, (int)(row_bytes * (unsigned)N), kBufferWord3);
+  const int k_lane_row = lane / kChunks;
+  const unsigned k_lane_col = (unsigned)(lane % kChunks) * 16u;
+  const unsigned k_lane_off = (unsigned)k_lane_row * row_bytes + k_lane_col;
   const unsigned v_lane_off = (unsigned)min(2 * lane, D - 2) * 2u;  // lanes past D/2 repeat
   u32x4 kst[kKLoads];
   unsigned vst[8];
-  auto load_tile = [&](int j) {
+  auto load_k = [&](int j) __attribute__((always_inline)) {
     const int j0 = j * kBc;
     if (j0 + kBc <= N) {
 #pragma unroll
-      for (int u = 0; u < kKLoads; ++u) {
-        const char* rowp = (const char*)(kp + (size_t)(j0 + 8 * wv + u * kKRows) * kv_row_stride);
-        kst[u] = *(const u32x4*)(rowp + k_lane_off);
-      }
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int key = j0 + 16 * (wv >> 1) + 4 * (wv & 1) + (r & 3) + (r >> 2) * 8;
-        const char* rowp = (const char*)(vp + (size_t)key * kv_row_stride);
-        vst[r] = *(const unsigned*)(rowp + v_lane_off);
-      }
+      for (int u = 0; u < kKLoads; ++u)
+        kst[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_lane_off, (j0 + 8 * wv + u * kKRows) * row_bytes, 0);
     } else {
-      // keys past the end read row N-1: their scores are masked to -inf, so they add
-      // exp2(-inf) = 0 times a finite V row
 #pragma unroll
       for (int u = 0; u < kKLoads; ++u) {
-        const int key = min(j0 + 8 * wv + u * kKRows + lane / kChunks, N - 1);
-        kst[u] = *(const u32x4*)(kp + (size_t)key * kv_row_stride + (lane % kChunks) * 8);
-      }
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int key = min(j0 + 16 * (wv >> 1) + 4 * (wv & 1) + (r & 3) + (r >> 2) * 8, N - 1);
-        const char* rowp = (const char*)(vp + (size_t)key * kv_row_stride);
-        vst[r] = *(const unsigned*)(rowp + v_lane_off);
+        const int key = min(j0 + 8 * wv + u * kKRows + k_lane_row, N - 1);
+        kst[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, (unsigned)key * row_bytes + k_lane_col, 0, 0);
       }
     }
   };
-  auto store_tile = [&](int stage) {
-    unsigned char* st = lds + stage * kStageBytes;
+  auto load_v = [&](int j) __attribute__((always_inline)) {
+    const int j0 = j * kBc;
+    const bool full = j0 + kBc <= N;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      int key = j0 + 16 * (wv >> 1) + 4 * (wv & 1) + (r & 3) + (r >> 2) * 8;
+      if (!full) key = min(key, N - 1);
+      vst[r] = __builtin_amdgcn_raw_buffer_load_b32(vrs, v_lane_off, key * row_bytes, 0);
+    }
+  };
+  auto store_k = [&](int buf) __attribute__((always_inline)) {
+    unsigned char* st = lds + buf * kStageBytes;
 #pragma unroll
     for (int u = 0; u < kKLoads; ++u)
       *(u32x4*)(st + k_byte<D>(8 * wv + u * kKRows + lane / kChunks, (lane % kChunks) * 8)) = kst[u];
+  };
+  auto store_v = [&](int buf) __attribute__((always_inline)) {
+    unsigned char* st = lds + buf * kStageBytes;
     if (2 * lane < D) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
@@ -276,107 +323,185 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
     }
   };
 
+  // ---- per-wavefront state ----------------------------------------------------------------
   f32x16 oacc[kDblocks];
 #pragma unroll
   for (int i = 0; i < kDblocks; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[i][e] = 0.0f;
+  f32x16 s[kKb];             // S^T of the tile between its MFMA block and its softmax block
+  u32x4 p[kKb][2];           // probabilities of the tile between its softmax and its P.V
+#pragma unroll
+  for (int kb = 0; kb < kKb; ++kb)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) p[kb][hf] = u32x4{0u, 0u, 0u, 0u};
   float m_run = -INFINITY;   // running max, base-2 exponent units (score * c)
   float l_run = 0.0f;        // this lane's part of the running denominator
 
-  load_tile(0);
-  store_tile(0);
-  // Drain every outstanding load here (Q included) so that no wait for Q is left inside
-  // the loop, where it would also wait for the next tile's prefetch.
+  // wavefront-uniform: key tile j has a key visible to some query of this wavefront
+  auto wave_active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || j * kBc <= qw0 + 31; };
+
+  // MFMA block of step j: O^T += V^T(j-1) P^T(j-1), then S^T(j) = K(j) Q^T. Both read slot j.
+  auto pv_part = [&](const lds_byte* st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < 2 * kKb; ++kk) {
+#pragma unroll
+      for (int db = 0; db < kDblocks; ++db) {
+        const u32x4 va = lds_load<u32x4>(st, voff[db] + kk * (D * 32));
+        oacc[db] = Ops::mfma(va, p[kk >> 1][kk & 1], oacc[db]);
+      }
+    }
+  };
+  auto s_part = [&](const lds_byte* st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < kKb; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[kb][e] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < kKsteps; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < kKb; ++kb) {
+        const u32x4 ka = lds_load<u32x4>(st, koff[ks] + kb * 32 * D * 2);
+        s[kb] = Ops::mfma(ka, qreg[ks], s[kb]);
+      }
+    }
+  };
+  // One variant only, so that the register allocator sees a single path: the first step
+  // (j = 0) multiplies the zero probabilities by the zero-filled V^T region of slot 0, and
+  // the last step (j = T) computes an S^T from stale K that nothing reads. A wavefront with
+  // no visible key in tile j-1 has none in tile j either and skips the block.
+  auto mfma_block = [&](auto buf_c, int j) __attribute__((always_inline)) {
+    constexpr int buf = decltype(buf_c)::value;
+    const lds_byte* st = (const lds_byte*)lds + buf * kStageBytes;
+    if (j <= ntiles && wave_active(j - 1)) {
+      s_part(st);
+      pv_part(st);
+      // keep operand reads kLead MFMAs ahead of their use: this wavefront is the only one
+      // issuing MFMAs on its SIMD during the step, so LDS latency must be hidden inside it
+      constexpr int kOps = kDblocks * 2 * kKb + kKsteps * kKb;
+      constexpr int kLead = 8;
+      __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);   // DS reads
+#pragma unroll
+      for (int i = 0; i < kOps - kLead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // one DS read
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kLead, 0);
+    }
+  };
+
+  // softmax block of tile j: mask, running max (lazy rescale of O), exponentials, row sum,
+  // and the probabilities packed as the B operand of the next P.V
+  auto softmax_block = [&](int j) __attribute__((always_inline)) {
+    if (j >= ntiles || !wave_active(j)) return;
+    const int j0 = j * kBc;
+    const bool need_mask = (j0 + kBc > N) || (CAUSAL && j0 + kBc - 1 > qw0);
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < kKb; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = j0 + kb * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
+          const bool dead = key >= N || (CAUSAL && key > qi);
+          s[kb][e] = dead ? -INFINITY : s[kb][e];
+        }
+    }
+    // Probabilities against the running maximum m_run as it stands. Every p is at most this
+    // lane's partial sum, so while that sum is <= Ops::kPMax no p can overflow the storage
+    // type of P and no rescale is needed (exact in real arithmetic for any m_run). Otherwise
+    // (a score grew past m_run by more than log2(kPMax), or m_run is still -inf on the
+    // first tile, which makes the sum inf or NaN) take the tile's true maximum, rescale the
+    // accumulators and recompute.
+    f32x16 pe[kKb];
+    auto exponentials = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int kb = 0; kb < kKb; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) pe[kb][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], a.c, -m_run));
+      return tree_sum<kKb>(pe);
+    };
+    float lsum = exponentials();
+    if (__builtin_amdgcn_ballot_w64(!(lsum <= Ops::kPMax)) != 0) {
+      const float mx = pair_max(tree_max<kKb>(s)) * a.c;
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < kDblocks; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+      lsum = exponentials();
+    }
+#pragma unroll
+    for (int kb = 0; kb < kKb; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int e = hf * 8 + e2 * 2;
+          p[kb][hf][e2] = Ops::pack2(pe[kb][e], pe[kb][e + 1]);
+        }
+    l_run += lsum;
+  };
+
+  // ---- schedule ------------------------------------------------------------------------
+  // The two halves of the workgroup (wavefronts 0-3 and 4-7, one of each per SIMD) run half
+  // a step apart, so that on every SIMD one wavefront issues MFMAs while the other
+  // computes the softmax. Step t (0 <= t < 2T+2, T key tiles) for a wavefront of half g:
+  //   u = t - g; u even: MFMA block of j = u/2 (P.V of tile j-1, S of tile j);
+  //              u odd:  softmax block of tile j = u/2;
+  // every step ends with a workgroup barrier. Slot j (LDS buffer j&1) is read at steps 2j
+  // and 2j+1; it is loaded from global memory at step 2j-2 and written to LDS at the end
+  // of step 2j-1, after the last reader of slot j-2 (same buffer) has finished.
+  const int half = wv >> 2;
+  load_k(0);
+  store_k(0);
+  {  // the V^T region of slot 0 (no tile -1) is zero, so step 0's P.V adds 0 * 0
+    unsigned char* vz = lds + kTileBytes;
+    for (int i = tid; i < kTileBytes / 16; i += kThreads) *(u32x4*)(vz + i * 16) = u32x4{0u, 0u, 0u, 0u};
+  }
+  // drain every outstanding load (Q included) so that no wait for Q is left inside the
+  // loop, where it would also wait for the prefetch in flight
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  auto tile = [&](auto stage_c, int j) {
-    constexpr int stage = decltype(stage_c)::value;
-    const int j0 = j * kBc;
-    if (j + 1 < ntiles) load_tile(j + 1);
-
-    // wavefront-uniform: does any key of this tile lie after every query of this wave?
-    const bool wave_active = !CAUSAL || j0 <= qw0 + 31;
-    if (wave_active) {
-      const lds_byte* st = (const lds_byte*)lds + stage * kStageBytes;
-      // ---- S^T = K Q^T ----
-      f32x16 s[kKb];
-#pragma unroll
-      for (int kb = 0; kb < kKb; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[kb][e] = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < kKsteps; ++ks) {
-#pragma unroll
-        for (int kb = 0; kb < kKb; ++kb) {
-          const u32x4 ka = lds_load<u32x4>(st, koff[ks] + kb * 32 * D * 2);
-          s[kb] = Ops::mfma(ka, qreg[ks], s[kb]);
-        }
-      }
-      // ---- mask (diagonal tiles and the ragged last tile only) ----
-      const bool need_mask = (j0 + kBc > N) || (CAUSAL && j0 + kBc - 1 > qw0);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < kKb; ++kb)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int key = j0 + kb * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
-            const bool dead = key >= N || (CAUSAL && key > qi);
-            s[kb][e] = dead ? -INFINITY : s[kb][e];
-          }
-      }
-      // ---- online softmax ----
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < kKb; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[kb][e]);
-      mx = pair_max(mx) * a.c;
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleThreshold) != 0) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < kDblocks; ++i)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
-      }
-      u32x4 p[kKb][2];
-      float lsum = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < kKb; ++kb)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const int e = hf * 8 + e2 * 2;
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], a.c, -m_run));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e + 1], a.c, -m_run));
-            lsum += p0 + p1;
-            p[kb][hf][e2] = Ops::pack2(p0, p1);
-          }
-      l_run += lsum;
-      // ---- O^T += V^T P^T: the V^T operand of key group (kb, hf) is one 16-byte read ----
-#pragma unroll
-      for (int db = 0; db < kDblocks; ++db) {
-#pragma unroll
-        for (int kk = 0; kk < 2 * kKb; ++kk) {
-          const int kb = kk >> 1, hf = kk & 1;
-          const u32x4 va = lds_load<u32x4>(st, voff[db] + kk * (D * 32));
-          oacc[db] = Ops::mfma(va, p[kb][hf], oacc[db]);
-        }
-      }
+  // the halves run separate copies of the step loop, so that inside each copy the kind of
+  // block of every step is a compile-time fact (no state is merged across branches)
+  auto step = [&](auto phase_c, auto half_c, int t) __attribute__((always_inline)) {
+    constexpr int phase = decltype(phase_c)::value;      // t % 4
+    constexpr int hf = decltype(half_c)::value;          // this wavefront's half
+    if constexpr (hf == (phase & 1)) {
+      mfma_block(ic<(phase >> 1) & 1>(), (t - hf) >> 1);
+    } else {
+      if (t - hf >= 0) softmax_block((t - hf) >> 1);
     }
-    if (j + 1 < ntiles) store_tile(stage ^ 1);
+    // the next slot's global loads go out after this step's block, so that the MFMA
+    // wavefront starts its MFMAs at once; they land during the next step
+    if constexpr ((phase & 1) == 0) {
+      const int jn = t / 2 + 1;                           // slot to fill
+      if (jn < ntiles) load_k(jn);
+      if (jn <= ntiles) load_v(jn - 1);
+    }
+    if constexpr ((phase & 1) == 1) {
+      const int jn = (t + 1) / 2;                         // slot filled at step t-1
+      constexpr int buf = phase == 1 ? 1 : 0;             // == jn & 1
+      if (jn < ntiles) store_k(buf);
+      if (jn <= ntiles) store_v(buf);
+    }
     __syncthreads();
   };
-  for (int j = 0; j < ntiles; j += 2) {
-    tile(ic<0>(), j);
-    if (j + 1 < ntiles) tile(ic<1>(), j + 1);
-  }
-
+  auto run = [&](auto half_c) __attribute__((always_inline)) {
+    const int nsteps = 2 * ntiles + 2;
+    for (int t = 0; t < nsteps; t += 4) {
+      step(ic<0>(), half_c, t);
+      step(ic<1>(), half_c, t + 1);
+      step(ic<2>(), half_c, t + 2);
+      step(ic<3>(), half_c, t + 3);
+    }
+  };
+  if (half == 0) run(ic<0>());
+  else run(ic<1>());
 
   // ---- epilogue: normalise once, write O and lse ----
   const float l_tot = pair_sum(l_run);
