@@ -32,17 +32,50 @@ def host(o: torch.Tensor, lse: torch.Tensor):
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-def compare(o, o_ref, lse, lse_ref, dtype: str, what: str = ""):
-    """Assert the parity bound; return (max scaled dO, max |dO|, max |dlse|)."""
+def compare(o, o_ref, lse, lse_ref, dtype: str, what: str = "", extra_bound=None):
+    """Assert the parity bound; return (max scaled dO, max |dO|, max |dlse|). With
+    `extra_bound` (an elementwise array), an element also passes when |dO| is within it."""
     assert np.all(np.isfinite(o)), f"{what}: non-finite output"
     assert np.all(np.isfinite(lse)), f"{what}: non-finite lse"
     scaled = np.abs(o - o_ref) / np.maximum(1.0, np.abs(o_ref))
     e_o = float(scaled.max()) if scaled.size else 0.0
     e_abs = float(np.abs(o - o_ref).max()) if o.size else 0.0
     e_l = float(np.abs(lse - lse_ref).max()) if lse.size else 0.0
-    assert e_o <= TOL[dtype], f"{what}: max scaled |dO| {e_o:.3e} > {TOL[dtype]} (abs {e_abs:.3e})"
+    if extra_bound is None:
+        assert e_o <= TOL[dtype], f"{what}: max scaled |dO| {e_o:.3e} > {TOL[dtype]} (abs {e_abs:.3e})"
+    else:
+        ok = (scaled <= TOL[dtype]) | (np.abs(o - o_ref) <= extra_bound)
+        assert np.all(ok), f"{what}: {int((~ok).sum())} elements outside both bounds (max scaled {e_o:.3e})"
     assert e_l <= LSE_TOL, f"{what}: max |dlse| {e_l:.3e} > {LSE_TOL}"
     return e_o, e_abs, e_l
+
+
+def fp8_quantization_bound(inp: dict, causal: bool, scale: float, o_ref: np.ndarray) -> np.ndarray:
+    """Per-element bound on |O_gpu - O_ref| from rounding the probabilities to e4m3.
+
+    The kernel stores p~_j = p_j (1 + d_j), |d_j| <= u = 2^-4 (round to nearest, 3 fraction
+    bits), and normalises by the sum of the stored values, so O_gpu = sum_j w~_j v_j with
+    w~_j = w_j (1 + d_j) / (1 + sum_k w_k d_k). Since sum_j (w~_j - w_j) = 0,
+      |O_gpu - O_ref| = |sum_j (w~_j - w_j) (v_j - O_ref)| <= 2u/(1-u) * sum_j w_j |v_j - O_ref|.
+    Added: bf16 output rounding (2^-8 |O|, twice the half-ulp) and 2e-3 for float32
+    accumulation and probabilities below the e4m3 normal range. Small shapes only (uses the
+    oracle's N x N probabilities)."""
+    import oracle
+    dq, dk, dv = inp["descale"]
+    q = oracle.decode(inp["q"], "e4m3", dq)
+    k = oracle.decode(inp["k"], "e4m3", dk)
+    v = oracle.decode(inp["v"], "e4m3", dv)
+    B, N, H, d = q.shape
+    g = H // k.shape[2]
+    u = 2.0 ** -4
+    bound = np.empty_like(o_ref)
+    for b in range(B):
+        for h in range(H):
+            w = oracle.attn_probs_f64(q, k, b, h, causal, scale)          # [N, N]
+            vh = v[b, :, h // g, :]                                       # [N, d]
+            dev = np.abs(vh[None, :, :] - o_ref[b, :, h, None, :])        # [N(i), N(j), d]
+            bound[b, :, h, :] = (2 * u / (1 - u)) * np.einsum("ij,ijt->it", w, dev)
+    return bound + 2.0 ** -8 * np.abs(o_ref) + 2e-3
 
 
 def sample_rows(B: int, H: int, N: int, n_random: int, seed: int, br: int = 128) -> np.ndarray:
