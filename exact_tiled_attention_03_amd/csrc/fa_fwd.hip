@@ -453,8 +453,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
   //   u = t - g; u even: MFMA block of j = u/2 (P.V of tile j-1, S of tile j);
   //              u odd:  softmax block of tile j = u/2;
   // every step ends with a workgroup barrier. Slot j (LDS buffer j&1) is read at steps 2j
-  // and 2j+1; it is loaded from global memory at step 2j-2 and written to LDS at the end
-  // of step 2j-1, after the last reader of slot j-2 (same buffer) has finished.
+  // and 2j+1; its global loads go out at the end of step 2j-3 and it is written to LDS at
+  // the end of step 2j-1, after the last reader of slot j-2 (same buffer) has finished.
   const int half = wv >> 2;
   load_k(0);
   store_k(0);
@@ -465,6 +465,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
   // drain every outstanding load (Q included) so that no wait for Q is left inside the
   // loop, where it would also wait for the prefetch in flight
   __builtin_amdgcn_s_waitcnt(0);
+  if (1 < ntiles) load_k(1);
+  if (1 <= ntiles) load_v(0);
   __syncthreads();
 
   // the halves run separate copies of the step loop, so that inside each copy the kind of
@@ -477,18 +479,16 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
     } else {
       if (t - hf >= 0) softmax_block((t - hf) >> 1);
     }
-    // the next slot's global loads go out after this step's block, so that the MFMA
-    // wavefront starts its MFMAs at once; they land during the next step
-    if constexpr ((phase & 1) == 0) {
-      const int jn = t / 2 + 1;                           // slot to fill
-      if (jn < ntiles) load_k(jn);
-      if (jn <= ntiles) load_v(jn - 1);
-    }
+    // At the end of every odd step t the staged slot jn = (t+1)/2 goes to LDS and the
+    // global loads of slot jn+1 go out at once, so that they have the next two blocks to
+    // land (slot jn+1 is stored at the end of step t+2).
     if constexpr ((phase & 1) == 1) {
-      const int jn = (t + 1) / 2;                         // slot filled at step t-1
+      const int jn = (t + 1) / 2;
       constexpr int buf = phase == 1 ? 1 : 0;             // == jn & 1
       if (jn < ntiles) store_k(buf);
       if (jn <= ntiles) store_v(buf);
+      if (jn + 1 < ntiles) load_k(jn + 1);
+      if (jn + 1 <= ntiles) load_v(jn);
     }
     __syncthreads();
   };
@@ -772,6 +772,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
     for (int i = tid; i < kTileV / 16; i += kThreads) *(u32x4*)(vz + i * 16) = u32x4{0u, 0u, 0u, 0u};
   }
   __builtin_amdgcn_s_waitcnt(0);
+  if (1 < ntiles) load_k(1);
+  if (1 <= ntiles) load_v(0);
   __syncthreads();
 
   auto step = [&](auto phase_c, auto half_c, int t) __attribute__((always_inline)) {
@@ -782,16 +784,13 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
     } else {
       if (t - hf >= 0) softmax_block((t - hf) >> 1);
     }
-    if constexpr ((phase & 1) == 0) {
-      const int jn = t / 2 + 1;
-      if (jn < ntiles) load_k(jn);
-      if (jn <= ntiles) load_v(jn - 1);
-    }
-    if constexpr ((phase & 1) == 1) {
+    if constexpr ((phase & 1) == 1) {   // store slot jn, then load slot jn+1 (see above)
       const int jn = (t + 1) / 2;
       constexpr int buf = phase == 1 ? 1 : 0;
       if (jn < ntiles) store_k(buf);
       if (jn <= ntiles) store_v(buf);
+      if (jn + 1 < ntiles) load_k(jn + 1);
+      if (jn + 1 <= ntiles) load_v(jn);
     }
     __syncthreads();
   };
