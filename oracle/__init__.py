@@ -59,6 +59,15 @@ def load(path: str):
     lib.oracle_attn_probs_f64.argtypes = ([dp, dp] + [ctypes.c_int] * 6 + [ctypes.c_double] +
                                           [ctypes.c_int, ctypes.c_int, dp])
     lib.oracle_attn_probs_f64.restype = ctypes.c_int
+    lib.oracle_attn_fwd_local_f64.argtypes = ([dp, dp, dp, dp, dp] + [ctypes.c_int] * 8 +
+                                              [ctypes.c_double])
+    lib.oracle_attn_fwd_local_f64.restype = ctypes.c_int
+    lib.oracle_attn_rows_local_f64.argtypes = ([dp, ctypes.c_int, dp, dp] + [ctypes.c_int] * 8 +
+                                               [ctypes.c_double, ctypes.c_int64, i64p, dp, dp])
+    lib.oracle_attn_rows_local_f64.restype = ctypes.c_int
+    lib.oracle_attn_probs_local_f64.argtypes = ([dp, dp] + [ctypes.c_int] * 8 + [ctypes.c_double] +
+                                                [ctypes.c_int, ctypes.c_int, dp])
+    lib.oracle_attn_probs_local_f64.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -105,22 +114,31 @@ def _shape(q: np.ndarray, k: np.ndarray, v: np.ndarray):
     return B, N, H, k.shape[2], d
 
 
-def attn_fwd_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: float):
-    """Attention forward on fp64 inputs. q [B,N,H,d], k/v [B,N,Hkv,d].
+def _window(window):
+    left, right = (-1, -1) if window is None else (int(window[0]), int(window[1]))
+    return max(left, -1), max(right, -1)
+
+
+def attn_fwd_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: float,
+                 window=None):
+    """Attention forward on fp64 inputs. q [B,N,H,d], k/v [B,N,Hkv,d]. `window` =
+    (left, right) keeps keys i-left <= j <= i+right for query i (negative: unbounded).
     Returns (o [B,N,H,d] float64, lse [B,H,N] float64)."""
     q, k, v = (np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v))
     B, N, H, Hkv, d = _shape(q, k, v)
+    left, right = _window(window)
     o = np.empty_like(q)
     lse = np.empty((B, H, N), dtype=np.float64)
-    rc = _lib().oracle_attn_fwd_f64(_dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(lse),
-                                    B, H, Hkv, N, d, int(bool(causal)), float(scale))
+    rc = _lib().oracle_attn_fwd_local_f64(_dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(lse),
+                                          B, H, Hkv, N, d, int(bool(causal)), left, right,
+                                          float(scale))
     if rc:
         raise ValueError(f"oracle_attn_fwd_f64 failed ({rc})")
     return o, lse
 
 
 def attn_rows_f64(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, H: int, rows: np.ndarray,
-                  causal: bool, scale: float):
+                  causal: bool, scale: float, window=None):
     """Selected query rows only. q_rows [R,d] are the fp64 query vectors of the rows
     rows[r] = (b, h, i); k/v [B,N,Hkv,d]. Returns (o_rows [R,d], lse_rows [R])."""
     q_rows = np.ascontiguousarray(q_rows, dtype=np.float64)
@@ -133,8 +151,9 @@ def attn_rows_f64(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, H: int, rows
         raise ValueError("q_rows must be [len(rows), d]")
     o = np.empty((R, d), dtype=np.float64)
     lse = np.empty((R,), dtype=np.float64)
-    rc = _lib().oracle_attn_rows_f64(_dptr(q_rows), 1, _dptr(k), _dptr(v), B, H, Hkv, N, d,
-                                     int(bool(causal)), float(scale), R,
+    left, right = _window(window)
+    rc = _lib().oracle_attn_rows_local_f64(_dptr(q_rows), 1, _dptr(k), _dptr(v), B, H, Hkv, N, d,
+                                           int(bool(causal)), left, right, float(scale), R,
                                      rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
                                      _dptr(o), _dptr(lse))
     if rc:
@@ -142,22 +161,24 @@ def attn_rows_f64(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, H: int, rows
     return o, lse
 
 
-def attn_probs_f64(q: np.ndarray, k: np.ndarray, b: int, h: int, causal: bool, scale: float):
+def attn_probs_f64(q: np.ndarray, k: np.ndarray, b: int, h: int, causal: bool, scale: float,
+                   window=None):
     """Softmax probability matrix [N,N] of one (b, h); zeros where masked. Small N only."""
     q = np.ascontiguousarray(q, dtype=np.float64)
     k = np.ascontiguousarray(k, dtype=np.float64)
     B, N, H, d = q.shape
     Hkv = k.shape[2]
     p = np.empty((N, N), dtype=np.float64)
-    rc = _lib().oracle_attn_probs_f64(_dptr(q), _dptr(k), B, H, Hkv, N, d, int(bool(causal)),
-                                      float(scale), int(b), int(h), _dptr(p))
+    left, right = _window(window)
+    rc = _lib().oracle_attn_probs_local_f64(_dptr(q), _dptr(k), B, H, Hkv, N, d, int(bool(causal)),
+                                            left, right, float(scale), int(b), int(h), _dptr(p))
     if rc:
         raise ValueError(f"oracle_attn_probs_f64 failed ({rc})")
     return p
 
 
 def attn_fwd(q_raw: np.ndarray, k_raw: np.ndarray, v_raw: np.ndarray, dtype: str, causal: bool,
-             scale: float, descale=None):
+             scale: float, descale=None, window=None):
     """Attention forward on the stored inputs exactly as handed to the GPU library:
     bit patterns of dtype `dtype` ("f16", "bf16" or "e4m3"); for e4m3, `descale` is the
     (q, k, v) per-tensor factors that multiply the decoded elements."""
@@ -168,11 +189,11 @@ def attn_fwd(q_raw: np.ndarray, k_raw: np.ndarray, v_raw: np.ndarray, dtype: str
     else:
         dq = dk = dv = 1.0
     return attn_fwd_f64(decode(q_raw, dtype, dq), decode(k_raw, dtype, dk), decode(v_raw, dtype, dv),
-                        causal, scale)
+                        causal, scale, window)
 
 
 def attn_rows(q_raw: np.ndarray, k_raw: np.ndarray, v_raw: np.ndarray, dtype: str, causal: bool,
-              scale: float, rows: np.ndarray, descale=None):
+              scale: float, rows: np.ndarray, descale=None, window=None):
     """Selected rows (b, h, i) of the forward on stored inputs, decoding only the query
     rows it needs. Returns (o_rows [R,d], lse_rows [R])."""
     if dtype == "e4m3":
@@ -183,4 +204,4 @@ def attn_rows(q_raw: np.ndarray, k_raw: np.ndarray, v_raw: np.ndarray, dtype: st
     B, N, H, d = q_raw.shape
     q_sel = q_raw[rows[:, 0], rows[:, 2], rows[:, 1], :]
     return attn_rows_f64(decode(q_sel, dtype, dq), decode(k_raw, dtype, dk), decode(v_raw, dtype, dv),
-                         H, rows, causal, scale)
+                         H, rows, causal, scale, window)

@@ -18,6 +18,10 @@
  * Readings where the pages are silent (each is also listed in the design notes):
  *   - scores are multiplied by `scale` before the softmax;
  *   - causal masking keeps key j for query i iff j <= i (square, no offset);
+ *   - a key window (the sliding-window patterns that the section "Why context lengths
+ *     exploded after 2022" of the long-context page above names without defining) keeps
+ *     i - left <= j <= i + right on top of the mask, a negative bound meaning no limit
+ *     on that side; every query keeps at least its own key, so no row is empty;
  *   - grouped-query attention maps query head h to key/value head h / (H / Hkv);
  *   - lse is the natural log of the softmax denominator over the scaled scores,
  *     lse = m + ln(sum_j exp(s_j - m)), so that P_ij = exp(s_ij - lse_i);
@@ -88,16 +92,14 @@ int oracle_decode(int dtype, const void* src, int64_t n, double mult, double* ds
 /* ---- one query row ---- */
 
 /* Scores, max, exponentials, denominator and output for one query row `qi` of batch b
- * against key/value head hk, with the mask applied for query position i. `s` is
- * caller scratch of N doubles. Writes o_row[0..d) and *lse. */
+ * against key/value head hk over the visible keys jlo <= j <= jhi (a non-empty range).
+ * `s` is caller scratch of N doubles. Writes o_row[0..d) and *lse. */
 static void attn_row(const double* qi, const double* k, const double* v, int Hkv, int N, int d,
-                     int causal, double scale, int b, int hk, int i, double* s, double* o_row,
+                     int jlo, int jhi, double scale, int b, int hk, double* s, double* o_row,
                      double* lse) {
-  const int nkeys = causal ? i + 1 : N;                      /* keys j <= i under the mask */
-
   /* pass 1: s_j = scale * <q_i, k_j>, and the row maximum */
   double m = -INFINITY;
-  for (int j = 0; j < nkeys; ++j) {
+  for (int j = jlo; j <= jhi; ++j) {
     const double* kj = k + (((size_t)b * N + j) * Hkv + hk) * d;
     double dot = 0.0;
     for (int t = 0; t < d; ++t) dot += qi[t] * kj[t];
@@ -107,7 +109,7 @@ static void attn_row(const double* qi, const double* k, const double* v, int Hkv
   /* pass 2: e_j = exp(s_j - m), l = sum_j e_j, o = sum_j e_j v_j / l */
   for (int t = 0; t < d; ++t) o_row[t] = 0.0;
   double l = 0.0;
-  for (int j = 0; j < nkeys; ++j) {
+  for (int j = jlo; j <= jhi; ++j) {
     const double e = exp(s[j] - m);
     const double* vj = v + (((size_t)b * N + j) * Hkv + hk) * d;
     l += e;
@@ -115,6 +117,16 @@ static void attn_row(const double* qi, const double* k, const double* v, int Hkv
   }
   for (int t = 0; t < d; ++t) o_row[t] /= l;
   *lse = m + log(l);
+}
+
+/* Visible keys of query i: causal keeps j <= i; a key window keeps i - left <= j <= i + right
+ * (a negative bound means no limit on that side). */
+static void key_range(int i, int N, int causal, int left, int right, int* jlo, int* jhi) {
+  int lo = 0, hi = causal ? i : N - 1;
+  if (left >= 0 && i - left > lo) lo = i - left;
+  if (right >= 0 && i + right < hi) hi = i + right;
+  *jlo = lo;
+  *jhi = hi;
 }
 
 static int check_shape(int B, int H, int Hkv, int N, int d) {
@@ -125,8 +137,9 @@ static int check_shape(int B, int H, int Hkv, int N, int d) {
 
 /* Full forward over every (b, h, i). Returns 0 on success, 1 on bad arguments,
  * 2 if scratch allocation failed. */
-int oracle_attn_fwd_f64(const double* q, const double* k, const double* v, double* o, double* lse,
-                        int B, int H, int Hkv, int N, int d, int causal, double scale) {
+int oracle_attn_fwd_local_f64(const double* q, const double* k, const double* v, double* o,
+                              double* lse, int B, int H, int Hkv, int N, int d, int causal,
+                              int left, int right, double scale) {
   if (check_shape(B, H, Hkv, N, d) || !q || !k || !v || !o || !lse) return 1;
   const int64_t rows = (int64_t)B * H * N;
   const int group = H / Hkv;                                 /* grouped-query head map h -> h / group */
@@ -143,7 +156,9 @@ int oracle_attn_fwd_f64(const double* q, const double* k, const double* v, doubl
       if (!s) continue;
       const int i = (int)(r % N), h = (int)((r / N) % H), b = (int)(r / ((int64_t)N * H));
       const size_t qo = (((size_t)b * N + i) * H + h) * d;
-      attn_row(q + qo, k, v, Hkv, N, d, causal, scale, b, h / group, i, s, o + qo,
+      int jlo, jhi;
+      key_range(i, N, causal, left, right, &jlo, &jhi);
+      attn_row(q + qo, k, v, Hkv, N, d, jlo, jhi, scale, b, h / group, s, o + qo,
                lse + ((size_t)b * H + h) * N + i);
     }
     free(s);
@@ -151,13 +166,20 @@ int oracle_attn_fwd_f64(const double* q, const double* k, const double* v, doubl
   return failed ? 2 : 0;
 }
 
+/* Full forward without a key window. */
+int oracle_attn_fwd_f64(const double* q, const double* k, const double* v, double* o, double* lse,
+                        int B, int H, int Hkv, int N, int d, int causal, double scale) {
+  return oracle_attn_fwd_local_f64(q, k, v, o, lse, B, H, Hkv, N, d, causal, -1, -1, scale);
+}
+
 /* Selected rows only: rows[3r], rows[3r+1], rows[3r+2] = (b, h, i). o_rows is
  * [nrows][d], lse_rows [nrows]. q is either a full [B][N][H][d] tensor
  * (q_is_rows = 0) or the selected query rows gathered as [nrows][d] (q_is_rows = 1),
  * so that a caller need not decode a whole large Q to check a sample. */
-int oracle_attn_rows_f64(const double* q, int q_is_rows, const double* k, const double* v,
-                         int B, int H, int Hkv, int N, int d, int causal, double scale,
-                         int64_t nrows, const int64_t* rows, double* o_rows, double* lse_rows) {
+int oracle_attn_rows_local_f64(const double* q, int q_is_rows, const double* k, const double* v,
+                               int B, int H, int Hkv, int N, int d, int causal, int left,
+                               int right, double scale, int64_t nrows, const int64_t* rows,
+                               double* o_rows, double* lse_rows) {
   if (check_shape(B, H, Hkv, N, d) || !q || !k || !v || !rows || !o_rows || !lse_rows) return 1;
   for (int64_t r = 0; r < nrows; ++r) {
     const int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
@@ -177,7 +199,9 @@ int oracle_attn_rows_f64(const double* q, int q_is_rows, const double* k, const 
       if (!s) continue;
       const int b = (int)rows[3 * r], h = (int)rows[3 * r + 1], i = (int)rows[3 * r + 2];
       const double* qi = q_is_rows ? q + (size_t)r * d : q + (((size_t)b * N + i) * H + h) * d;
-      attn_row(qi, k, v, Hkv, N, d, causal, scale, b, h / group, i, s, o_rows + (size_t)r * d,
+      int jlo, jhi;
+      key_range(i, N, causal, left, right, &jlo, &jhi);
+      attn_row(qi, k, v, Hkv, N, d, jlo, jhi, scale, b, h / group, s, o_rows + (size_t)r * d,
                lse_rows + r);
     }
     free(s);
@@ -185,33 +209,47 @@ int oracle_attn_rows_f64(const double* q, int q_is_rows, const double* k, const 
   return failed ? 2 : 0;
 }
 
+int oracle_attn_rows_f64(const double* q, int q_is_rows, const double* k, const double* v,
+                         int B, int H, int Hkv, int N, int d, int causal, double scale,
+                         int64_t nrows, const int64_t* rows, double* o_rows, double* lse_rows) {
+  return oracle_attn_rows_local_f64(q, q_is_rows, k, v, B, H, Hkv, N, d, causal, -1, -1, scale,
+                                    nrows, rows, o_rows, lse_rows);
+}
+
 /* Softmax probabilities of one (b, h) as an N x N matrix (row i, key j), zero where
  * masked. For small N only: used to check that rows sum to one. */
-int oracle_attn_probs_f64(const double* q, const double* k, int B, int H, int Hkv, int N, int d,
-                          int causal, double scale, int b, int h, double* p) {
+int oracle_attn_probs_local_f64(const double* q, const double* k, int B, int H, int Hkv, int N,
+                                int d, int causal, int left, int right, double scale, int b, int h,
+                                double* p) {
   if (check_shape(B, H, Hkv, N, d) || !q || !k || !p || b < 0 || b >= B || h < 0 || h >= H)
     return 1;
   const int hk = h / (H / Hkv);
   for (int i = 0; i < N; ++i) {
     const double* qi = q + (((size_t)b * N + i) * H + h) * d;
     double* pi = p + (size_t)i * N;
-    const int nkeys = causal ? i + 1 : N;
+    int jlo, jhi;
+    key_range(i, N, causal, left, right, &jlo, &jhi);
     double m = -INFINITY, l = 0.0;
     for (int j = 0; j < N; ++j) pi[j] = 0.0;
-    for (int j = 0; j < nkeys; ++j) {
+    for (int j = jlo; j <= jhi; ++j) {
       const double* kj = k + (((size_t)b * N + j) * Hkv + hk) * d;
       double dot = 0.0;
       for (int t = 0; t < d; ++t) dot += qi[t] * kj[t];
       pi[j] = scale * dot;
       if (pi[j] > m) m = pi[j];
     }
-    for (int j = 0; j < nkeys; ++j) {
+    for (int j = jlo; j <= jhi; ++j) {
       pi[j] = exp(pi[j] - m);
       l += pi[j];
     }
-    for (int j = 0; j < nkeys; ++j) pi[j] /= l;
+    for (int j = jlo; j <= jhi; ++j) pi[j] /= l;
   }
   return 0;
+}
+
+int oracle_attn_probs_f64(const double* q, const double* k, int B, int H, int Hkv, int N, int d,
+                          int causal, double scale, int b, int h, double* p) {
+  return oracle_attn_probs_local_f64(q, k, B, H, Hkv, N, d, causal, -1, -1, scale, b, h, p);
 }
 
 int oracle_num_threads(void) {

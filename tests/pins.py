@@ -321,11 +321,116 @@ def pin_golden_fixtures():
         k = np.array(fx["k"], dtype=np.float64)
         v = np.array(fx["v"], dtype=np.float64)
         scale = fx["scale"] if isinstance(fx["scale"], float) else eval(fx["scale"], {"math": math})
-        o, lse = oracle.attn_fwd_f64(q, k, v, fx["causal"], scale)
+        o, lse = oracle.attn_fwd_f64(q, k, v, fx["causal"], scale, fx.get("window"))
         _close(o, np.array(fx["o"]), fx["tol"], f"golden {name} O")
         _close(lse, np.array(fx["lse"]), fx["tol"], f"golden {name} lse")
 
 
+# Key windows. The long-context page names sliding-window patterns (section "Why
+# context lengths exploded after 2022") without defining them; the reading pinned here
+# keeps key j for query i iff i - left <= j <= i + right (negative bound: unbounded),
+# intersected with the causal mask.
+def _window_mask(N, causal, left, right):
+    """Boolean [N, N] visibility built from the offset matrix j - i (an implementation
+    independent of the oracle's per-row range arithmetic)."""
+    off = np.subtract.outer(np.arange(N), np.arange(N)).T       # off[i, j] = j - i
+    keep = np.ones((N, N), dtype=bool)
+    if causal:
+        keep &= off <= 0
+    if left >= 0:
+        keep &= off >= -left
+    if right >= 0:
+        keep &= off <= right
+    return keep
+
+
+WINDOW_CASES = [(False, 0, 0), (False, 1, 2), (False, 2, 1), (False, 3, -1), (False, -1, 4),
+                (True, 2, -1), (True, 0, 3), (True, 5, 7), (False, 40, 40), (True, -1, -1)]
+
+
+# P15 -- windows against brute force in 50 digits and against torch's attention with an
+# explicit boolean mask (float64, CPU).
+def pin_window_bruteforce_and_sdpa():
+    rng = np.random.default_rng(31)
+    mpmath.mp.dps = 50
+    N, H, Hkv, d = 9, 2, 1, 3
+    q, k, v = _qkv(rng, 1, N, H, Hkv, d)
+    for causal, left, right in WINDOW_CASES:
+        o, lse = oracle.attn_fwd_f64(q, k, v, causal, 0.6, (left, right))
+        keep = _window_mask(N, causal, left, right)
+        for h in range(H):
+            for i in range(N):
+                J = [j for j in range(N) if keep[i, j]]
+                s = [mpmath.mpf(0.6) * mpmath.fsum(mpmath.mpf(q[0, i, h, t]) * mpmath.mpf(k[0, j, 0, t])
+                                                   for t in range(d)) for j in J]
+                L = mpmath.log(mpmath.fsum(mpmath.exp(x) for x in s))
+                ref = [float(mpmath.fsum(mpmath.exp(x - L) * mpmath.mpf(v[0, j, 0, t]) for x, j in zip(s, J)))
+                       for t in range(d)]
+                _close(o[0, i, h], ref, 1e-13, f"window ({causal},{left},{right}) mpmath O h{h} i{i}")
+                _close(lse[0, h, i], float(L), 1e-13, f"window ({causal},{left},{right}) mpmath lse")
+    B, N, H, Hkv, d = 2, 70, 4, 2, 16
+    q, k, v = _qkv(rng, B, N, H, Hkv, d)
+    t = lambda x: torch.from_numpy(x).permute(0, 2, 1, 3)
+    for causal, left, right in WINDOW_CASES:
+        o, lse = oracle.attn_fwd_f64(q, k, v, causal, 0.25, (left, right))
+        mask = torch.from_numpy(_window_mask(N, causal, left, right))
+        ref = F.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=mask, scale=0.25,
+                                             enable_gqa=True).permute(0, 2, 1, 3).numpy()
+        _close(o, ref, 1e-12, f"window ({causal},{left},{right}) vs sdpa with mask")
+
+
+# P16 -- windows in closed form: with Q = 0 row i is the mean of its visible V rows and
+# lse_i = ln(count); a window of width zero gives O_i = V_i and lse_i = scale <q_i, k_i>.
+def pin_window_closed_forms():
+    rng = np.random.default_rng(32)
+    B, N, H, Hkv, d = 1, 23, 2, 1, 5
+    _, k, v = _qkv(rng, B, N, H, Hkv, d)
+    q0 = np.zeros((B, N, H, d))
+    for causal, left, right in WINDOW_CASES:
+        o, lse = oracle.attn_fwd_f64(q0, k, v, causal, 0.9, (left, right))
+        keep = _window_mask(N, causal, left, right).astype(np.float64)
+        count = keep.sum(axis=1)
+        for h in range(H):
+            _close(o[0, :, h], keep @ v[0, :, 0] / count[:, None], 1e-13,
+                   f"window ({causal},{left},{right}) Q=0 local mean")
+            _close(lse[0, h], np.log(count), 1e-13, f"window ({causal},{left},{right}) Q=0 ln(count)")
+    q, k, v = _qkv(rng, B, N, H, Hkv, d)
+    for causal in (False, True):
+        o, lse = oracle.attn_fwd_f64(q, k, v, causal, 0.4, (0, 0))
+        for h in range(H):
+            _close(o[0, :, h], v[0, :, 0], 1e-15, "window (0,0): O_i = V_i")
+            _close(lse[0, h], 0.4 * np.einsum("nt,nt->n", q[0, :, h], k[0, :, 0]), 1e-14,
+                   "window (0,0): lse_i = scale <q_i, k_i>")
+
+
+# P17 -- windows reduce to the unwindowed cases: a window wider than the sequence is
+# the full (or causal) attention, and right = 0 without the mask is the causal mask.
+def pin_window_reductions():
+    rng = np.random.default_rng(33)
+    B, N, H, Hkv, d = 1, 31, 2, 2, 4
+    q, k, v = _qkv(rng, B, N, H, Hkv, d)
+    for causal in (False, True):
+        o, lse = oracle.attn_fwd_f64(q, k, v, causal, 0.5)
+        for w in ((N, N), (N - 1, N - 1), (-1, -1), (10 * N, -1)):
+            o2, lse2 = oracle.attn_fwd_f64(q, k, v, causal, 0.5, w)
+            assert np.array_equal(o, o2) and np.array_equal(lse, lse2), f"wide window {w} (causal={causal})"
+    oc, lc = oracle.attn_fwd_f64(q, k, v, True, 0.5)
+    o2, l2 = oracle.attn_fwd_f64(q, k, v, False, 0.5, (-1, 0))
+    assert np.array_equal(oc, o2) and np.array_equal(lc, l2), "right = 0 is the causal mask"
+    # a causal window is a row-wise suffix of the causal prefix: row i with left = L is
+    # the unmasked attention of query i over keys max(0, i-L) .. i
+    L = 4
+    o, lse = oracle.attn_fwd_f64(q, k, v, True, 0.5, (L, -1))
+    for i in (0, 3, 4, 17, 30):
+        lo = max(0, i - L)
+        n = i + 1 - lo
+        o2, l2 = oracle.attn_fwd_f64(np.repeat(q[:, i:i + 1], n, axis=1), k[:, lo:i + 1], v[:, lo:i + 1],
+                                     False, 0.5)
+        _close(o2[:, 0], o[:, i], 1e-13, f"causal window row {i} = slice attention (O)")
+        _close(l2[:, :, 0], lse[:, :, i], 1e-13, f"causal window row {i} = slice attention (lse)")
+
+
 ALL_PINS = [pin_mpmath_bruteforce, pin_torch_sdpa, pin_zero_query, pin_single_key, pin_two_keys,
             pin_affine_in_v, pin_probability_rows, pin_key_permutation, pin_key_shift, pin_gqa_repeat,
-            pin_causal_prefix, pin_split_merge, pin_hardmax_and_range, pin_decoders, pin_golden_fixtures]
+            pin_causal_prefix, pin_split_merge, pin_hardmax_and_range, pin_decoders, pin_golden_fixtures,
+            pin_window_bruteforce_and_sdpa, pin_window_closed_forms, pin_window_reductions]

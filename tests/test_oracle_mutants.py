@@ -16,8 +16,17 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")
 
 MUTANTS = {
     "gqa_map_modulo": ("h / group", "h % Hkv"),
-    "causal_excludes_diagonal": ("causal ? i + 1 : N", "causal ? i : N"),
-    "causal_one_extra_key": ("causal ? i + 1 : N", "causal ? (i + 2 < N ? i + 2 : N) : N"),
+    "causal_excludes_diagonal": ("hi = causal ? i : N - 1;", "hi = causal ? i - 1 : N - 1;"),
+    "causal_one_extra_key": ("hi = causal ? i : N - 1;", "hi = causal ? (i + 1 < N ? i + 1 : i) : N - 1;"),
+    "window_left_off_by_one": ("if (left >= 0 && i - left > lo) lo = i - left;",
+                               "if (left >= 0 && i - left + 1 > lo) lo = i - left + 1;"),
+    "window_right_one_extra": ("if (right >= 0 && i + right < hi) hi = i + right;",
+                               "if (right >= 0 && i + right + 1 < hi) hi = i + right + 1;"),
+    "window_sides_swapped": ("if (left >= 0 && i - left > lo) lo = i - left;",
+                             "if (right >= 0 && i - right > lo) lo = i - right;"),
+    "window_right_ignored": ("if (right >= 0 && i + right < hi) hi = i + right;", ""),
+    "window_overrides_causal": ("if (right >= 0 && i + right < hi) hi = i + right;",
+                                "if (right >= 0) hi = i + right < N - 1 ? i + right : N - 1;"),
     "scale_dropped": ("s[j] = scale * dot;", "s[j] = dot;"),
     "scale_squared": ("s[j] = scale * dot;", "s[j] = scale * scale * dot;"),
     "max_not_subtracted": ("const double e = exp(s[j] - m);", "const double e = exp(s[j]);"),
@@ -28,7 +37,7 @@ MUTANTS = {
     "dot_drops_last_dim": ("for (int t = 0; t < d; ++t) dot += qi[t] * kj[t];",
                            "for (int t = 0; t + 1 < d; ++t) dot += qi[t] * kj[t];"),
     "v_rows_reversed": ("const double* vj = v + (((size_t)b * N + j) * Hkv + hk) * d;",
-                        "const double* vj = v + (((size_t)b * N + (nkeys - 1 - j)) * Hkv + hk) * d;"),
+                        "const double* vj = v + (((size_t)b * N + (jlo + jhi - j)) * Hkv + hk) * d;"),
     "k_used_for_v": ("const double* vj = v + (((size_t)b * N + j) * Hkv + hk) * d;",
                      "const double* vj = k + (((size_t)b * N + j) * Hkv + hk) * d;"),
     "f16_exponent_bias": ("mag = ldexp((double)(1024 + f), e - 25);", "mag = ldexp((double)(1024 + f), e - 24);"),
