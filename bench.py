@@ -1,8 +1,9 @@
 """Benchmark of the attention forward hot path on one MI355X.
 
-A step is one attention forward (one fa_fwd launch through the C ABI) over the whole
-workload, inputs resident in HBM. Prints one JSON line with TFLOP/s counted as
-4*B*H*N^2*d (halved under the causal mask), the roofline of the kernel (achieved
+A step is one attention forward (one fa_fwd launch through the C ABI, fa_fwd_local for
+a key-window workload) over the whole workload, inputs resident in HBM. Prints one JSON
+line with TFLOP/s counted as 4*B*H*N^2*d (halved under the causal mask; for a key window,
+4*B*H*d times the visible (query, key) pairs), the roofline of the kernel (achieved
 TFLOP/s from HIP events on the launch stream against the dense bf16/f16 MFMA peak) and
 the fp64 CPU oracle timed on the host cores on a bounded sample of the same workload.
 
@@ -66,7 +67,7 @@ def cpu_baseline(w: synth_inputs.Workload, inp: dict, budget_s: float = 12.0):
     import oracle
     dq, dk, dv = inp["descale"] if inp["descale"] else (1.0, 1.0, 1.0)
     g = w.H // w.Hkv
-    per_head = (4.0 * w.N * w.N * w.d) / (2 if w.causal else 1)
+    per_head = w.flops / (w.B * w.H)
     heads, elapsed = 0, 0.0
     for b in range(w.B):
         if elapsed >= budget_s:
@@ -79,7 +80,7 @@ def cpu_baseline(w: synth_inputs.Workload, inp: dict, budget_s: float = 12.0):
                 break
             t0 = time.perf_counter()
             oracle.attn_fwd_f64(np.ascontiguousarray(q[:, :, hk * g:(hk + 1) * g]), k[:, :, hk:hk + 1],
-                                v[:, :, hk:hk + 1], w.causal, w.scale)
+                                v[:, :, hk:hk + 1], w.causal, w.scale, w.window)
             elapsed += time.perf_counter() - t0
             heads += g
     flops = per_head * heads
@@ -123,19 +124,22 @@ def main():
     inp = synth_inputs.workload_inputs(w)
     q, k, v = (to_dev(inp[x], w.dtype) for x in "qkv")
     dt = w.dtype if w.dtype == "e4m3" else None
-    o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale, descale=inp["descale"], dtype=dt)
+    o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale, descale=inp["descale"], dtype=dt,
+                    window=w.window)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o.float()).all()), "non-finite output"
 
     for _ in range(args.warmup):
-        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, descale=inp["descale"], dtype=dt, out=o, lse=lse)
+        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, descale=inp["descale"], dtype=dt, out=o, lse=lse,
+               window=w.window)
     stream = torch.cuda.current_stream()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, descale=inp["descale"], dtype=dt, out=o, lse=lse)
+        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, descale=inp["descale"], dtype=dt, out=o, lse=lse,
+               window=w.window)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -159,7 +163,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic (seeded N(0,1) inputs)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
-                   "causal": w.causal, "scale": w.scale, "flop_per_step": w.flops},
+                   "causal": w.causal, "scale": w.scale, "flop_per_step": w.flops,
+                   **({"window": list(w.window)} if w.window else {})},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name),
                      "kernel_ms": round(kernel_ms, 5)},

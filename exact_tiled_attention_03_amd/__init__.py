@@ -1,8 +1,9 @@
 """Exact tiled attention forward for MI355X (gfx950): a C-ABI HIP library (libfa.so,
 include/fa.h) and its thin Python binding."""
 from .fa import (FA_DTYPE_BF16, FA_DTYPE_F16, FA_DTYPE_FP8_E4M3, FA_ERR_INVALID_ARG, FA_ERR_LAUNCH,
-                 FA_ERR_UNSUPPORTED, FA_OK, FaError, fa_fwd, fa_fwd_query, fwd, status_string, version)
+                 FA_ERR_UNSUPPORTED, FA_OK, FaError, fa_fwd, fa_fwd_local, fa_fwd_query, fwd, status_string,
+                 version)
 
-__all__ = ["fwd", "fa_fwd", "fa_fwd_query", "status_string", "version", "FaError", "FA_OK",
+__all__ = ["fwd", "fa_fwd", "fa_fwd_local", "fa_fwd_query", "status_string", "version", "FaError", "FA_OK",
            "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_LAUNCH", "FA_DTYPE_F16", "FA_DTYPE_BF16",
            "FA_DTYPE_FP8_E4M3"]

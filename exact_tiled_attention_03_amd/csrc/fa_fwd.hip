@@ -65,17 +65,25 @@ struct FwdArgs {
   int total;            // workgroups in the grid: num_qtiles * H * B
   float c;              // scale * log2(e) (times the q and k descales for e4m3)
   float v_scale;        // 1 for 16-bit inputs; the v descale for e4m3
+  int wl, wr;           // key window of the band mask: query i sees keys i-wl .. i+wr
 };
+
+// Masks, one kernel instance each: none; causal (key j visible to query i iff j <= i);
+// band (iff i - wl <= j <= i + wr, the key window, which also covers a causal mask with
+// a window: wr = 0).
+constexpr int kMaskNone = 0;
+constexpr int kMaskCausal = 1;
+constexpr int kMaskBand = 2;
 
 // Workgroups are handed to the 8 XCDs round-robin (workgroup L runs on XCD L % 8), and
 // each XCD has its own L2. Reorder so that XCD x receives one contiguous range of the
 // logical work list, in which consecutive entries share K/V: the logical order is
 // (batch, K/V head, query tile, query head within the group), query tiles longest first
-// under the causal mask.
+// under a mask.
 struct TileCoord {
   int b, h, qt;
 };
-__device__ __forceinline__ TileCoord tile_of_workgroup(const FwdArgs& a, int L, bool causal) {
+__device__ __forceinline__ TileCoord tile_of_workgroup(const FwdArgs& a, int L, bool reverse) {
   const int xcd = L & 7, slot = L >> 3;
   const int per = a.total >> 3, rem = a.total & 7;
   const int logical = xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
@@ -85,7 +93,7 @@ __device__ __forceinline__ TileCoord tile_of_workgroup(const FwdArgs& a, int L, 
   t /= a.num_qtiles;
   const int hk = t % a.Hkv;
   const int b = t / a.Hkv;
-  if (causal) qt = a.num_qtiles - 1 - qt;
+  if (reverse) qt = a.num_qtiles - 1 - qt;
   return {b, hk * a.group + gm, qt};
 }
 
@@ -201,8 +209,10 @@ template <int V>
 using ic = std::integral_constant<int, V>;
 
 // ---- the forward kernel for 16-bit inputs -------------------------------------------
-template <typename Ops, int D, bool CAUSAL>
+template <typename Ops, int D, int MASK>
 __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
+  constexpr bool CAUSAL = MASK == kMaskCausal;
+  constexpr bool BAND = MASK == kMaskBand;
   constexpr int kChunks = D / 8;                  // 16-byte chunks per K row
   constexpr int kKsteps = D / 16;                 // MFMA k-steps over d for S^T
   constexpr int kDblocks = D / 32;                // 32-row blocks of O^T
@@ -218,19 +228,24 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
   const int l32 = lane & 31;
   const int hi = lane >> 5;
 
-  const TileCoord tc = tile_of_workgroup(a, blockIdx.x, CAUSAL);
+  const TileCoord tc = tile_of_workgroup(a, blockIdx.x, MASK != kMaskNone);
   const int b = tc.b, h = tc.h, qt = tc.qt;
   const int hk = h / a.group;
   const int N = a.N;
   const int q0 = qt * kBr;
   const int qw0 = q0 + wave * 32;                 // this wavefront's first query
   const int qi = qw0 + l32;                       // this lane's query
+  // Keys are addressed from kv0, the first key of the first tile this query tile can see
+  // (under the band mask the left end of its first query's window, rounded down to a
+  // tile; else 0); nk keys follow it up to the end of the sequence.
+  const int kv0 = BAND ? max(0, q0 - a.wl) / kBc * kBc : 0;
+  const int nk = N - kv0;
 
   const size_t q_row_stride = (size_t)a.H * D;
   const size_t kv_row_stride = (size_t)a.Hkv * D;
   const uint16_t* qp = (const uint16_t*)a.q + ((size_t)b * N) * q_row_stride + (size_t)h * D;
-  const uint16_t* kp = (const uint16_t*)a.k + ((size_t)b * N) * kv_row_stride + (size_t)hk * D;
-  const uint16_t* vp = (const uint16_t*)a.v + ((size_t)b * N) * kv_row_stride + (size_t)hk * D;
+  const uint16_t* kp = (const uint16_t*)a.k + ((size_t)b * N + kv0) * kv_row_stride + (size_t)hk * D;
+  const uint16_t* vp = (const uint16_t*)a.v + ((size_t)b * N + kv0) * kv_row_stride + (size_t)hk * D;
 
   // Q^T operand: lane holds q[qi][ks*16 + hi*8 .. +7] for every k-step; rows past the
   // end are read from row N-1 (in bounds) and never stored
@@ -240,8 +255,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
   for (int ks = 0; ks < kKsteps; ++ks)
     qreg[ks] = *(const u32x4*)(qp + (size_t)qi_ld * q_row_stride + ks * 16 + hi * 8);
 
-  const int kv_end = CAUSAL ? min(N, q0 + kBr) : N;
-  const int ntiles = (kv_end + kBc - 1) / kBc;
+  const int kv_end = BAND ? min(N, q0 + kBr + a.wr) : CAUSAL ? min(N, q0 + kBr) : N;
+  const int ntiles = (kv_end - kv0 + kBc - 1) / kBc;
 
   // per-lane LDS byte offsets of the MFMA operands (stage 0, key block 0); the key block,
   // the half and the stage only add compile-time constants
@@ -272,8 +287,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
   // addresses; the descriptor's extent is exactly N rows, a hardware bound on top of
   // the row clamping below
   const unsigned row_bytes = (unsigned)(kv_row_stride * 2);
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, (int)(row_bytes * (unsigned)N), kBufferWord3);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vp, 0, (int)(row_bytes * (unsigned)N), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, (int)(row_bytes * (unsigned)nk), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vp, 0, (int)(row_bytes * (unsigned)nk), kBufferWord3);
   const int k_lane_row = lane / kChunks;
   const unsigned k_lane_col = (unsigned)(lane % kChunks) * 16u;
   const unsigned k_lane_off = (unsigned)k_lane_row * row_bytes + k_lane_col;
@@ -282,25 +297,25 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
   unsigned vst[8];
   auto load_k = [&](int j) __attribute__((always_inline)) {
     const int j0 = j * kBc;
-    if (j0 + kBc <= N) {
+    if (j0 + kBc <= nk) {
 #pragma unroll
       for (int u = 0; u < kKLoads; ++u)
         kst[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_lane_off, (j0 + 8 * wv + u * kKRows) * row_bytes, 0);
     } else {
 #pragma unroll
       for (int u = 0; u < kKLoads; ++u) {
-        const int key = min(j0 + 8 * wv + u * kKRows + k_lane_row, N - 1);
+        const int key = min(j0 + 8 * wv + u * kKRows + k_lane_row, nk - 1);
         kst[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, (unsigned)key * row_bytes + k_lane_col, 0, 0);
       }
     }
   };
   auto load_v = [&](int j) __attribute__((always_inline)) {
     const int j0 = j * kBc;
-    const bool full = j0 + kBc <= N;
+    const bool full = j0 + kBc <= nk;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       int key = j0 + 16 * (wv >> 1) + 4 * (wv & 1) + (r & 3) + (r >> 2) * 8;
-      if (!full) key = min(key, N - 1);
+      if (!full) key = min(key, nk - 1);
       vst[r] = __builtin_amdgcn_raw_buffer_load_b32(vrs, v_lane_off, key * row_bytes, 0);
     }
   };
@@ -336,11 +351,22 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
   for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) p[kb][hf] = u32x4{0u, 0u, 0u, 0u};
-  float m_run = -INFINITY;   // running max, base-2 exponent units (score * c)
+  // running max, base-2 exponent units (score * c); it starts at -FLT_MAX rather than
+  // -inf so that a row whose keys in a tile are all masked gets exp2(-inf - m) = 0, never
+  // exp2(-inf + inf)
+  float m_run = -__FLT_MAX__;
   float l_run = 0.0f;        // this lane's part of the running denominator
 
-  // wavefront-uniform: key tile j has a key visible to some query of this wavefront
-  auto wave_active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || j * kBc <= qw0 + 31; };
+  // wavefront-uniform: key tile j has a key visible to some query of this wavefront; the
+  // tiles for which this holds are consecutive
+  auto wave_active = [&](int j) __attribute__((always_inline)) {
+    if constexpr (BAND) {
+      const int k0 = kv0 + j * kBc;
+      return j >= 0 && j < ntiles && k0 <= qw0 + 31 + a.wr && k0 + kBc - 1 >= qw0 - a.wl;
+    } else {
+      return !CAUSAL || j * kBc <= qw0 + 31;
+    }
+  };
 
   // MFMA block of step j: O^T += V^T(j-1) P^T(j-1), then S^T(j) = K(j) Q^T. Both read slot j.
   auto pv_part = [&](const lds_byte* st) __attribute__((always_inline)) {
@@ -370,11 +396,13 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
   // One variant only, so that the register allocator sees a single path: the first step
   // (j = 0) multiplies the zero probabilities by the zero-filled V^T region of slot 0, and
   // the last step (j = T) computes an S^T from stale K that nothing reads. A wavefront with
-  // no visible key in tile j-1 has none in tile j either and skips the block.
+  // no visible key in tile j-1 has none in tile j either and skips the block; under the
+  // band mask it may see keys of tile j only, and then multiplies its probabilities, still
+  // the initial zeros, by the V^T of tile j-1.
   auto mfma_block = [&](auto buf_c, int j) __attribute__((always_inline)) {
     constexpr int buf = decltype(buf_c)::value;
     const lds_byte* st = (const lds_byte*)lds + buf * kStageBytes;
-    if (j <= ntiles && wave_active(j - 1)) {
+    if (j <= ntiles && (wave_active(j - 1) || (BAND && wave_active(j)))) {
       s_part(st);
       pv_part(st);
       // keep operand reads kLead MFMAs ahead of their use: this wavefront is the only one
@@ -395,24 +423,26 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
   // and the probabilities packed as the B operand of the next P.V
   auto softmax_block = [&](int j) __attribute__((always_inline)) {
     if (j >= ntiles || !wave_active(j)) return;
-    const int j0 = j * kBc;
-    const bool need_mask = (j0 + kBc > N) || (CAUSAL && j0 + kBc - 1 > qw0);
+    const int k0 = kv0 + j * kBc;                  // first key of the tile
+    bool need_mask = (k0 + kBc > N) || (CAUSAL && k0 + kBc - 1 > qw0);
+    if constexpr (BAND) need_mask = need_mask || k0 + kBc - 1 > qw0 + a.wr || k0 < qw0 + 31 - a.wl;
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int key = j0 + kb * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
-          const bool dead = key >= N || (CAUSAL && key > qi);
+          const int key = k0 + kb * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
+          bool dead = key >= N || (CAUSAL && key > qi);
+          if constexpr (BAND) dead = dead || key > qi + a.wr || key < qi - a.wl;
           s[kb][e] = dead ? -INFINITY : s[kb][e];
         }
     }
     // Probabilities against the running maximum m_run as it stands. Every p is at most this
     // lane's partial sum, so while that sum is <= Ops::kPMax no p can overflow the storage
     // type of P and no rescale is needed (exact in real arithmetic for any m_run). Otherwise
-    // (a score grew past m_run by more than log2(kPMax), or m_run is still -inf on the
-    // first tile, which makes the sum inf or NaN) take the tile's true maximum, rescale the
-    // accumulators and recompute.
+    // (a score grew past m_run by more than log2(kPMax), or m_run is still -FLT_MAX before
+    // the first visible key, which makes the sum inf) take the tile's true maximum, rescale
+    // the accumulators and recompute.
     f32x16 pe[kKb];
     auto exponentials = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -425,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
     if (__builtin_amdgcn_ballot_w64(!(lsum <= Ops::kPMax)) != 0) {
       const float mx = pair_max(tree_max<kKb>(s)) * a.c;
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run = -FLT_MAX
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -562,8 +592,10 @@ __device__ __forceinline__ int vt8_byte(int dim, int pos) {      // V^T tile: by
   return dim * 64 + ((((pos >> 4) ^ ((dim >> 2) & 3))) << 4) + (pos & 15);
 }
 
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
+  constexpr bool CAUSAL = MASK == kMaskCausal;
+  constexpr bool BAND = MASK == kMaskBand;
   constexpr float kTau = 2.5f;    // rescale once a row maximum grows by more than 2^kTau
   constexpr float kOff = 6.0f;    // probabilities are 2^kOff times softmax numerators
   constexpr int kKsteps = D / 16;                 // bf16 MFMA k-steps for S^T
@@ -581,18 +613,20 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  const TileCoord tc = tile_of_workgroup(a, blockIdx.x, CAUSAL);
+  const TileCoord tc = tile_of_workgroup(a, blockIdx.x, MASK != kMaskNone);
   const int b = tc.b, h = tc.h, qt = tc.qt;
   const int hk = h / a.group;
   const int N = a.N;
   const int q0 = qt * kBr;
   const int qw0 = q0 + wave * 32;
   const int qi = qw0 + l32;
+  const int kv0 = BAND ? max(0, q0 - a.wl) / kBc * kBc : 0;   // as in the 16-bit kernel
+  const int nk = N - kv0;
   const size_t q_row_stride = (size_t)a.H * D;    // bytes
   const size_t kv_row_stride = (size_t)a.Hkv * D;
   const uint8_t* qp = (const uint8_t*)a.q + ((size_t)b * N) * q_row_stride + (size_t)h * D;
-  const uint8_t* kp = (const uint8_t*)a.k + ((size_t)b * N) * kv_row_stride + (size_t)hk * D;
-  const uint8_t* vp = (const uint8_t*)a.v + ((size_t)b * N) * kv_row_stride + (size_t)hk * D;
+  const uint8_t* kp = (const uint8_t*)a.k + ((size_t)b * N + kv0) * kv_row_stride + (size_t)hk * D;
+  const uint8_t* vp = (const uint8_t*)a.v + ((size_t)b * N + kv0) * kv_row_stride + (size_t)hk * D;
 
   // Q^T operand in bf16: lane holds q[qi][16ks + 8hi .. +7]
   u32x4 qreg[kKsteps];
@@ -604,8 +638,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
     qreg[ks] = u32x4{lo[0], lo[1], hi4[0], hi4[1]};
   }
 
-  const int kv_end = CAUSAL ? min(N, q0 + kBr) : N;
-  const int ntiles = (kv_end + kBc - 1) / kBc;
+  const int kv_end = BAND ? min(N, q0 + kBr + a.wr) : CAUSAL ? min(N, q0 + kBr) : N;
+  const int ntiles = (kv_end - kv0 + kBc - 1) / kBc;
 
   int koff[kKsteps];
 #pragma unroll
@@ -621,8 +655,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
   //   V: lane l -> keys 8w + 4hi + 0..3, dims 4(l%32) .. +3 (4x4 bytes, transposed)
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const unsigned row_bytes = (unsigned)kv_row_stride;
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, (int)(row_bytes * (unsigned)N), kBufferWord3);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vp, 0, (int)(row_bytes * (unsigned)N), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, (int)(row_bytes * (unsigned)nk), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vp, 0, (int)(row_bytes * (unsigned)nk), kBufferWord3);
   constexpr int kKLanes = 8 * (D / 16);           // lanes with 16 K codes
   const bool k_lane = lane < kKLanes;
   const int k_key = min(lane / (D / 16), 7), k_chunk = lane % (D / 16);
@@ -631,16 +665,16 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
   u32x4 kst;
   unsigned vst[4];
   auto load_k = [&](int j) __attribute__((always_inline)) {
-    const int key = min(j * kBc + 8 * wv + k_key, N - 1);
+    const int key = min(j * kBc + 8 * wv + k_key, nk - 1);
     kst = __builtin_amdgcn_raw_buffer_load_b128(krs, (unsigned)key * row_bytes + k_chunk * 16u, 0, 0);
   };
   auto load_v = [&](int j) __attribute__((always_inline)) {
     const int j0 = j * kBc;
-    const bool full = j0 + kBc <= N;
+    const bool full = j0 + kBc <= nk;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       int key = j0 + 8 * wv + 4 * hi + r;
-      if (!full) key = min(key, N - 1);
+      if (!full) key = min(key, nk - 1);
       vst[r] = __builtin_amdgcn_raw_buffer_load_b32(vrs, (unsigned)v_dq * 4u, key * (int)row_bytes, 0);
     }
   };
@@ -686,9 +720,16 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
 #pragma unroll
   for (int e = 0; e < 16; ++e) lacc[e] = 0.0f;
   const u32x4 ones = {0x38383838u, 0x38383838u, 0x38383838u, 0x38383838u};  // e4m3 1.0
-  float m_run = -INFINITY;
+  float m_run = -__FLT_MAX__;   // as in the 16-bit kernel
   float l_run = 0.0f;        // float32 sum of the unrounded probabilities (for lse)
-  auto wave_active = [&](int j) __attribute__((always_inline)) { return !CAUSAL || j * kBc <= qw0 + 31; };
+  auto wave_active = [&](int j) __attribute__((always_inline)) {
+    if constexpr (BAND) {
+      const int k0 = kv0 + j * kBc;
+      return j >= 0 && j < ntiles && k0 <= qw0 + 31 + a.wr && k0 + kBc - 1 >= qw0 - a.wl;
+    } else {
+      return !CAUSAL || j * kBc <= qw0 + 31;
+    }
+  };
 
   auto s_part = [&](const lds_byte* st) __attribute__((always_inline)) {
 #pragma unroll
@@ -715,29 +756,31 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
   auto mfma_block = [&](auto buf_c, int j) __attribute__((always_inline)) {
     constexpr int buf = decltype(buf_c)::value;
     const lds_byte* st = (const lds_byte*)lds + buf * kStageBytes;
-    if (j <= ntiles && wave_active(j - 1)) {
+    if (j <= ntiles && (wave_active(j - 1) || (BAND && wave_active(j)))) {
       s_part(st);
       pv_part(st);
     }
   };
   auto softmax_block = [&](int j) __attribute__((always_inline)) {
     if (j >= ntiles || !wave_active(j)) return;
-    const int j0 = j * kBc;
-    const bool need_mask = (j0 + kBc > N) || (CAUSAL && j0 + kBc - 1 > qw0);
+    const int k0 = kv0 + j * kBc;                  // first key of the tile
+    bool need_mask = (k0 + kBc > N) || (CAUSAL && k0 + kBc - 1 > qw0);
+    if constexpr (BAND) need_mask = need_mask || k0 + kBc - 1 > qw0 + a.wr || k0 < qw0 + 31 - a.wl;
     if (need_mask) {
 #pragma unroll
       for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int key = j0 + kb * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
-          const bool dead = key >= N || (CAUSAL && key > qi);
+          const int key = k0 + kb * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
+          bool dead = key >= N || (CAUSAL && key > qi);
+          if constexpr (BAND) dead = dead || key > qi + a.wr || key < qi - a.wl;
           s[kb][e] = dead ? -INFINITY : s[kb][e];
         }
     }
     const float mx = pair_max(tree_max<kKb>(s)) * a.c;
     if (__builtin_amdgcn_ballot_w64(mx > m_run + kTau) != 0) {
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_run == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run = -FLT_MAX
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -843,31 +886,55 @@ fa_status check_sizes(int B, int H, int Hkv, int N, int d, int causal, fa_dtype 
   return FA_OK;
 }
 
-template <typename Ops, int D, bool CAUSAL>
+template <typename Ops, int D, int MASK>
 fa_status launch(const FwdArgs& args, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<Ops, D, CAUSAL>), dim3(args.total), dim3(kThreads), 0, stream, args);
+  hipLaunchKernelGGL((fa_fwd_kernel<Ops, D, MASK>), dim3(args.total), dim3(kThreads), 0, stream, args);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-template <int D, bool CAUSAL>
+template <int D, int MASK>
 fa_status launch_fp8(const FwdArgs& args, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, CAUSAL>), dim3(args.total), dim3(kThreads), 0, stream, args);
+  hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, MASK>), dim3(args.total), dim3(kThreads), 0, stream, args);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-template <typename Ops>
-fa_status dispatch(const FwdArgs& args, int d, int causal, hipStream_t stream) {
-  if (d == 128) return causal ? launch<Ops, 128, true>(args, stream) : launch<Ops, 128, false>(args, stream);
-  return causal ? launch<Ops, 64, true>(args, stream) : launch<Ops, 64, false>(args, stream);
+template <typename Ops, int D>
+fa_status dispatch_mask(const FwdArgs& args, int mask, hipStream_t stream) {
+  switch (mask) {
+    case kMaskNone: return launch<Ops, D, kMaskNone>(args, stream);
+    case kMaskCausal: return launch<Ops, D, kMaskCausal>(args, stream);
+    default: return launch<Ops, D, kMaskBand>(args, stream);
+  }
 }
 
-}  // namespace
+template <int D>
+fa_status dispatch_fp8(const FwdArgs& args, int mask, hipStream_t stream) {
+  switch (mask) {
+    case kMaskNone: return launch_fp8<D, kMaskNone>(args, stream);
+    case kMaskCausal: return launch_fp8<D, kMaskCausal>(args, stream);
+    default: return launch_fp8<D, kMaskBand>(args, stream);
+  }
+}
 
-extern "C" {
+// Mask of (causal, window_left, window_right) after normalising the window: a negative or
+// too-wide side is unbounded (wl/wr = N), a causal mask bounds the right side at 0. A
+// window that bounds nothing is the plain or causal case.
+int resolve_mask(int N, int causal, int window_left, int window_right, int* wl, int* wr) {
+  *wl = (window_left < 0 || window_left >= N) ? N : window_left;
+  *wr = (window_right < 0 || window_right >= N) ? N : window_right;
+  if (causal) *wr = 0;
+  if (*wl == N && *wr == N) return kMaskNone;
+  if (*wl == N && *wr == 0) return kMaskCausal;
+  return kMaskBand;
+}
 
-fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                 int Hkv, int N, int d, int causal, float scale, fa_dtype dtype,
-                 const float* descale_qkv, void* stream) {
+fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int Hkv, int N, int d, int causal, int window_left, int window_right,
+                   float scale, fa_dtype dtype, const float* descale_qkv, void* stream);
+
+fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int Hkv, int N, int d, int causal, int window_left, int window_right,
+                   float scale, fa_dtype dtype, const float* descale_qkv, void* stream) {
   fa_status st = check_sizes(B, H, Hkv, N, d, causal, dtype);
   if (st != FA_OK) return st;
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
@@ -896,19 +963,39 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
   args.total = args.num_qtiles * H * B;
   args.c = (float)((double)scale * 1.4426950408889634);
   args.v_scale = 1.0f;
+  const int mask = resolve_mask(N, causal, window_left, window_right, &args.wl, &args.wr);
   if (dtype == FA_DTYPE_FP8_E4M3) {
     args.c = (float)((double)scale * descale_qkv[0] * descale_qkv[1] * 1.4426950408889634);
     args.v_scale = descale_qkv[2];
   }
   hipStream_t s = (hipStream_t)stream;
   switch (dtype) {
-    case FA_DTYPE_BF16: return dispatch<Bf16Ops>(args, d, causal, s);
-    case FA_DTYPE_F16: return dispatch<F16Ops>(args, d, causal, s);
+    case FA_DTYPE_BF16:
+      return d == 128 ? dispatch_mask<Bf16Ops, 128>(args, mask, s) : dispatch_mask<Bf16Ops, 64>(args, mask, s);
+    case FA_DTYPE_F16:
+      return d == 128 ? dispatch_mask<F16Ops, 128>(args, mask, s) : dispatch_mask<F16Ops, 64>(args, mask, s);
     case FA_DTYPE_FP8_E4M3:
-      if (d == 128) return causal ? launch_fp8<128, true>(args, s) : launch_fp8<128, false>(args, s);
-      return causal ? launch_fp8<64, true>(args, s) : launch_fp8<64, false>(args, s);
+      return d == 128 ? dispatch_fp8<128>(args, mask, s) : dispatch_fp8<64>(args, mask, s);
     default: return FA_ERR_UNSUPPORTED;
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int Hkv, int N, int d, int causal, float scale, fa_dtype dtype,
+                 const float* descale_qkv, void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, Hkv, N, d, causal, -1, -1, scale, dtype, descale_qkv, stream);
+}
+
+fa_status fa_fwd_local(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                       int H, int Hkv, int N, int d, int causal, int window_left,
+                       int window_right, float scale, fa_dtype dtype, const float* descale_qkv,
+                       void* stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, Hkv, N, d, causal, window_left, window_right, scale, dtype,
+                  descale_qkv, stream);
 }
 
 fa_status fa_fwd_query(int B, int H, int Hkv, int N, int d, int causal, fa_dtype dtype,
@@ -935,6 +1022,6 @@ const char* fa_status_string(fa_status s) {
   return "unknown fa_status";
 }
 
-int fa_version(void) { return 100; }
+int fa_version(void) { return 10100; }
 
 }  // extern "C"

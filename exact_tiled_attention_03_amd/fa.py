@@ -39,6 +39,9 @@ def lib() -> ctypes.CDLL:
             L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, c_int, c_int, c_int, c_int, c_int, c_int,
                                  c_float, c_int, ctypes.POINTER(c_float), vp]
             L.fa_fwd.restype = c_int
+            L.fa_fwd_local.argtypes = [vp, vp, vp, vp, vp] + [c_int] * 8 + [c_float, c_int,
+                                                                            ctypes.POINTER(c_float), vp]
+            L.fa_fwd_local.restype = c_int
             L.fa_fwd_query.argtypes = [c_int] * 7 + [szp] * 5
             L.fa_fwd_query.restype = c_int
             L.fa_status_string.argtypes = [c_int]
@@ -70,6 +73,17 @@ def fa_fwd(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int,
                             float(scale), int(dtype), ds, stream))
 
 
+def fa_fwd_local(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int,
+                 Hkv: int, N: int, d: int, causal: int, window_left: int, window_right: int,
+                 scale: float, dtype: int, descale=None, stream: int = 0) -> int:
+    """Direct call of fa_fwd_local (key window i-left <= j <= i+right, negative bound =
+    unbounded) with raw pointers; returns the status code."""
+    ds = (ctypes.c_float * 3)(*descale) if descale is not None else None
+    return int(lib().fa_fwd_local(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Hkv, N, d, int(causal),
+                                  int(window_left), int(window_right), float(scale), int(dtype), ds,
+                                  stream))
+
+
 def fa_fwd_query(B: int, H: int, Hkv: int, N: int, d: int, causal: int, dtype: int) -> dict:
     """Byte sizes of q, k/v, o, lse and the workspace (always 0); raises on bad sizes."""
     out = [ctypes.c_size_t(0) for _ in range(5)]
@@ -86,12 +100,14 @@ def _dtype_code(t, dtype):
 
 
 def fwd(q, k, v, causal: bool = False, scale: float | None = None, descale=None, dtype: str | None = None,
-        out=None, lse=None, stream=None):
+        out=None, lse=None, stream=None, window=None):
     """Attention forward on device tensors.
 
     q [B,N,H,d], k and v [B,N,Hkv,d], contiguous, on one GPU; element type float16,
     bfloat16 or float8_e4m3fn (uint8 tensors with dtype="e4m3" are also accepted;
-    e4m3 needs descale=(dq, dk, dv)). Returns (o [B,N,H,d], lse [B,H,N] float32);
+    e4m3 needs descale=(dq, dk, dv)). `window` = (left, right) restricts query i to
+    keys i-left <= j <= i+right (negative: unbounded; calls fa_fwd_local). Returns
+    (o [B,N,H,d], lse [B,H,N] float32);
     o has q's type for 16-bit inputs and bfloat16 for e4m3. Enqueues on the current
     stream (or `stream`) and returns without synchronising."""
     import torch
@@ -114,7 +130,12 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, descale=None,
         raise ValueError("out/lse have the wrong shape or type")
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Hkv, N, d,
-                int(bool(causal)), scale, code, descale, stream)
+    if window is None:
+        st = fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Hkv, N,
+                    d, int(bool(causal)), scale, code, descale, stream)
+    else:
+        st = fa_fwd_local(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H,
+                          Hkv, N, d, int(bool(causal)), int(window[0]), int(window[1]), scale, code,
+                          descale, stream)
     _check(st)
     return out, lse

@@ -18,6 +18,7 @@
  * open; the library takes these readings:
  *   - `scale` multiplies the scores before the softmax;
  *   - causal masking keeps key j for query i iff j <= i (square, no offset);
+ *   - a key window (fa_fwd_local) keeps i - left <= j <= i + right on top of that;
  *   - grouped-query attention: query head h reads key/value head h / (H / Hkv);
  *   - lse is the natural log of the softmax denominator over the scaled scores;
  *   - e4m3 inputs (the low-precision mode in the abstract of "FlashAttention-3: Fast
@@ -82,6 +83,24 @@ fa_status fa_fwd(const void* q, const void* k, const void* v, void* o, float* ls
                  fa_dtype dtype, const float* descale_qkv, void* stream);
 
 /*
+ * Attention forward with a key window (sliding-window / local attention). The page
+ * "FlashAttention: The Algorithm That Made Long-Context AI Possible" names
+ * sliding-window patterns (section "Why context lengths exploded after 2022") without
+ * defining them; the library's reading: key j is visible to query i iff
+ *     i - window_left <= j <= i + window_right,
+ * intersected with the causal mask when causal = 1. A negative bound (or one >= N)
+ * leaves that side unbounded, so (-1, -1) is fa_fwd itself and (-1, 0) without the
+ * causal flag is the causal mask. Every query sees at least its own key, so no row is
+ * empty. The kernel visits only the key tiles inside the band of each query tile: the
+ * work is linear in N for a fixed window. Every other argument, layout, ownership rule
+ * and error is as for fa_fwd (window bounds themselves are never an error).
+ */
+fa_status fa_fwd_local(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int Hkv, int N, int d, int causal, int window_left,
+                       int window_right, float scale, fa_dtype dtype,
+                       const float* descale_qkv, void* stream);
+
+/*
  * Shape query: byte sizes of every buffer fa_fwd reads or writes for these arguments,
  * after the same size checks fa_fwd makes. Any output pointer may be NULL.
  * workspace_bytes is always 0 (no scratch memory). Pure host function.
@@ -93,7 +112,7 @@ fa_status fa_fwd_query(int B, int H, int Hkv, int N, int d, int causal, fa_dtype
 /* Static, human-readable text for a status code. */
 const char* fa_status_string(fa_status s);
 
-/* Library version, encoded as major * 10000 + minor * 100 + patch. */
+/* Library version, encoded as major * 10000 + minor * 100 + patch (10100: fa_fwd_local). */
 int fa_version(void);
 
 #ifdef __cplusplus

@@ -38,12 +38,22 @@ class Workload:
     scale: float
     outlier_frac: float = 0.0
     outlier_mult: float = 20.0
+    window: tuple | None = None     # (left, right) key window; negative side = unbounded
 
     @property
     def flops(self) -> float:
-        """4*B*H*N^2*d, halved under the causal mask (query heads H)."""
-        f = 4.0 * self.B * self.H * self.N * self.N * self.d
-        return f / 2 if self.causal else f
+        """4*B*H*N^2*d, halved under the causal mask (query heads H). With a key window:
+        4*B*H*d times the number of (query, key) pairs inside the window."""
+        if self.window is None:
+            f = 4.0 * self.B * self.H * self.N * self.N * self.d
+            return f / 2 if self.causal else f
+        i = np.arange(self.N, dtype=np.int64)
+        left, right = self.window
+        lo = np.maximum(0, i - left) if left >= 0 else np.zeros_like(i)
+        hi = i if self.causal else np.full_like(i, self.N - 1)
+        if right >= 0:
+            hi = np.minimum(hi, i + right)
+        return 4.0 * self.B * self.H * self.d * float(np.sum(hi - lo + 1))
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
@@ -54,7 +64,8 @@ def _w(name, B, H, Hkv, N, d, causal, dtype, seed, **kw):
 
 
 # The five workloads: a tiny fp16 case, bf16 multi-head, bf16 causal long sequence,
-# bf16 causal grouped-query, and e4m3 with outliers.
+# bf16 causal grouped-query, and e4m3 with outliers; then a causal sliding-window case
+# (each query sees itself and the 4095 keys before it).
 WORKLOADS = {
     w.name: w for w in [
         _w("tiny_f16_b1_h2_n128_d64", 1, 2, 2, 128, 64, False, "f16", 1001),
@@ -63,6 +74,8 @@ WORKLOADS = {
         _w("gqa_causal_bf16_b4_h32_kv8_n8192_d128", 4, 32, 8, 8192, 128, True, "bf16", 1004),
         _w("fp8_e4m3_b8_h16_n4096_d128", 8, 16, 16, 4096, 128, False, "e4m3", 1005,
            outlier_frac=1e-3, outlier_mult=20.0),
+        _w("swa_causal_bf16_b1_h32_kv8_n32768_d128_w4096", 1, 32, 8, 32768, 128, True, "bf16", 1006,
+           window=(4095, -1)),
     ]
 }
 

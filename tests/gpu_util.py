@@ -19,11 +19,12 @@ def to_dev(bits: np.ndarray, dtype: str, device="cuda:0") -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(TORCH_DT[dtype])
 
 
-def run(inp: dict, dtype: str, causal: bool, scale: float):
-    """Run the library on stored inputs; returns (o, lse) device tensors."""
+def run(inp: dict, dtype: str, causal: bool, scale: float, window=None):
+    """Run the library on stored inputs (fa_fwd, or fa_fwd_local with a key window);
+    returns (o, lse) device tensors."""
     q, k, v = (to_dev(inp[x], dtype) for x in "qkv")
     o, lse = fa.fwd(q, k, v, causal=causal, scale=scale, descale=inp.get("descale"),
-                    dtype=dtype if dtype == "e4m3" else None)
+                    dtype=dtype if dtype == "e4m3" else None, window=window)
     torch.cuda.synchronize()
     return o, lse
 
@@ -50,7 +51,8 @@ def compare(o, o_ref, lse, lse_ref, dtype: str, what: str = "", extra_bound=None
     return e_o, e_abs, e_l
 
 
-def fp8_quantization_bound(inp: dict, causal: bool, scale: float, o_ref: np.ndarray) -> np.ndarray:
+def fp8_quantization_bound(inp: dict, causal: bool, scale: float, o_ref: np.ndarray,
+                           window=None) -> np.ndarray:
     """Per-element bound on |O_gpu - O_ref| from rounding the probabilities to e4m3.
 
     The kernel stores p~_j = p_j (1 + d_j), |d_j| <= u = 2^-4 (round to nearest, 3 fraction
@@ -71,7 +73,7 @@ def fp8_quantization_bound(inp: dict, causal: bool, scale: float, o_ref: np.ndar
     bound = np.empty_like(o_ref)
     for b in range(B):
         for h in range(H):
-            w = oracle.attn_probs_f64(q, k, b, h, causal, scale)          # [N, N]
+            w = oracle.attn_probs_f64(q, k, b, h, causal, scale, window)  # [N, N]
             vh = v[b, :, h // g, :]                                       # [N, d]
             dev = np.abs(vh[None, :, :] - o_ref[b, :, h, None, :])        # [N(i), N(j), d]
             bound[b, :, h, :] = (2 * u / (1 - u)) * np.einsum("ij,ijt->it", w, dev)

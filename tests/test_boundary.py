@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert set(names) >= {"fa_fwd", "fa_fwd_query", "fa_status_string", "fa_version"}
+    assert set(names) >= {"fa_fwd", "fa_fwd_local", "fa_fwd_query", "fa_status_string", "fa_version"}
     lib = ctypes.CDLL(binding.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"libfa.so does not export {n}"
@@ -96,6 +96,25 @@ def _call(**over):
 ])
 def test_fwd_rejects_before_launch(over, status):
     assert _call(**over) == status
+
+
+@pytest.mark.parametrize("window", [(-1, -1), (0, 0), (5, 3), (1 << 30, -7)])
+@pytest.mark.parametrize("over,status", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=FAKE + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=3), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=fa.FA_DTYPE_FP8_E4M3, descale=None), fa.FA_ERR_INVALID_ARG),
+])
+def test_fwd_local_rejects_before_launch(over, status, window):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=4, Hkv=2, N=64, d=128, causal=0,
+             scale=0.125, dtype=fa.FA_DTYPE_BF16, descale=None)
+    a.update(over)
+    st = fa.fa_fwd_local(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"], a["d"],
+                         a["causal"], window[0], window[1], a["scale"], a["dtype"], a["descale"])
+    assert st == status
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

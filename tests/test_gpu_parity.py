@@ -54,15 +54,17 @@ def test_workload_sampled_parity(name):
     w = synth_inputs.WORKLOADS[name]
     _log(f"[workload] {name}")
     inp = synth_inputs.workload_inputs(w)
-    o_d, lse_d = gu.run(inp, w.dtype, w.causal, w.scale)
+    o_d, lse_d = gu.run(inp, w.dtype, w.causal, w.scale, w.window)
     assert bool(torch.isfinite(o_d.float()).all()) and bool(torch.isfinite(lse_d).all())
     if w.N <= 128:
-        o_ref, lse_ref = oracle.attn_fwd(inp["q"], inp["k"], inp["v"], w.dtype, w.causal, w.scale)
+        o_ref, lse_ref = oracle.attn_fwd(inp["q"], inp["k"], inp["v"], w.dtype, w.causal, w.scale,
+                                         window=w.window)
         o_g, l_g = gu.host(o_d, lse_d)
         gu.compare(o_g, o_ref, l_g, lse_ref, w.dtype, name)
         return
     rows = gu.sample_rows(w.B, w.H, w.N, n_random=40, seed=w.seed)
-    o_ref, lse_ref = oracle.attn_rows(inp["q"], inp["k"], inp["v"], w.dtype, w.causal, w.scale, rows)
+    o_ref, lse_ref = oracle.attn_rows(inp["q"], inp["k"], inp["v"], w.dtype, w.causal, w.scale, rows,
+                                      window=w.window)
     o_g = o_d[rows[:, 0], rows[:, 2], rows[:, 1]].float().cpu().numpy().astype(np.float64)
     l_g = lse_d[rows[:, 0], rows[:, 1], rows[:, 2]].cpu().numpy().astype(np.float64)
     e = gu.compare(o_g, o_ref, l_g, lse_ref, w.dtype, name)
