@@ -27,6 +27,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attn_oracle.c")
+_SOURCES = [_SRC, os.path.join(_HERE, "fp8_quant_oracle.c")]
 _SO = os.path.join(_HERE, "liboracle.so")
 _LOCK = threading.Lock()
 _LIB = None
@@ -35,11 +36,12 @@ DTYPE_CODES = {"f16": 0, "bf16": 1, "e4m3": 2}
 
 
 def build(force: bool = False) -> str:
-    """Compile attn_oracle.c into liboracle.so with gcc (-O2, OpenMP, no fast-math)."""
-    if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
+    """Compile the oracle's C sources into liboracle.so with gcc (-O2, OpenMP, no
+    fast-math, no contraction of a*b+c into fused multiply-adds)."""
+    if force or not os.path.exists(_SO) or any(os.path.getmtime(_SO) < os.path.getmtime(s) for s in _SOURCES):
         tmp = _SO + f".tmp{os.getpid()}"
         subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99", "-Wall",
-                        "-o", tmp, _SRC, "-lm"], check=True)
+                        "-ffp-contract=off", "-o", tmp, *_SOURCES, "-lm"], check=True)
         os.replace(tmp, _SO)
     return _SO
 
@@ -68,6 +70,16 @@ def load(path: str):
     lib.oracle_attn_probs_local_f64.argtypes = ([dp, dp] + [ctypes.c_int] * 8 + [ctypes.c_double] +
                                                 [ctypes.c_int, ctypes.c_int, dp])
     lib.oracle_attn_probs_local_f64.restype = ctypes.c_int
+    u8p = ctypes.POINTER(ctypes.c_uint8)
+    fp = ctypes.POINTER(ctypes.c_float)
+    lib.oracle_e4m3_encode_array.argtypes = [fp, ctypes.c_int64, u8p]
+    lib.oracle_e4m3_encode_array.restype = ctypes.c_int
+    lib.oracle_fwht_rows_f32.argtypes = [fp, ctypes.c_int64, ctypes.c_int]
+    lib.oracle_fwht_rows_f32.restype = ctypes.c_int
+    lib.oracle_block_exponent.argtypes = [ctypes.c_float]
+    lib.oracle_block_exponent.restype = ctypes.c_int
+    lib.oracle_block_quantize_e4m3.argtypes = [dp] + [ctypes.c_int] * 5 + [fp, u8p, u8p]
+    lib.oracle_block_quantize_e4m3.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -205,3 +217,64 @@ def attn_rows(q_raw: np.ndarray, k_raw: np.ndarray, v_raw: np.ndarray, dtype: st
     q_sel = q_raw[rows[:, 0], rows[:, 2], rows[:, 1], :]
     return attn_rows_f64(decode(q_sel, dtype, dq), decode(k_raw, dtype, dk), decode(v_raw, dtype, dv),
                          H, rows, causal, scale, window)
+
+
+# ---- block quantisation to e4m3 (fp8_quant_oracle.c) ----
+
+def _u8p(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+
+
+def _fp(a):
+    assert a.dtype == np.float32 and a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+
+
+def e4m3_encode(y: np.ndarray) -> np.ndarray:
+    """E4M3 codes (uint8) of float32 values: round to nearest even, saturating at 448."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(y.shape, dtype=np.uint8)
+    if _lib().oracle_e4m3_encode_array(_fp(y), y.size, _u8p(out)):
+        raise ValueError("oracle_e4m3_encode_array rejected its arguments")
+    return out
+
+
+def fwht_f32(x: np.ndarray) -> np.ndarray:
+    """Unnormalised fast Walsh-Hadamard transform of every row (last axis, a power of two)
+    in float32, butterfly stages h = 1, 2, ..., d/2."""
+    y = np.array(x, dtype=np.float32, order="C", copy=True)
+    d = y.shape[-1]
+    if _lib().oracle_fwht_rows_f32(_fp(y), y.size // d, d):
+        raise ValueError("oracle_fwht_rows_f32 rejected its arguments")
+    return y
+
+
+def block_exponent(amax: float) -> int:
+    return int(_lib().oracle_block_exponent(float(amax)))
+
+
+def block_quantize(x: np.ndarray, block_rows: int = 64, signs=None):
+    """Block quantisation of x [B,N,Hx,d] (exact float values) to e4m3 with one
+    power-of-two scale per block_rows x d slab of each (batch, head); with `signs` (d
+    values +-1), rows are first replaced by (x * signs) H. Returns (codes uint8
+    [B,N,Hx,d], scales uint8 E8M0 [B,Hx,ceil(N/block_rows)])."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    B, N, Hx, d = x.shape
+    nb = (N + block_rows - 1) // block_rows
+    codes = np.empty((B, N, Hx, d), dtype=np.uint8)
+    scales = np.empty((B, Hx, nb), dtype=np.uint8)
+    sg = None if signs is None else np.ascontiguousarray(signs, dtype=np.float32)
+    rc = _lib().oracle_block_quantize_e4m3(_dptr(x), B, N, Hx, d, int(block_rows),
+                                           _fp(sg) if sg is not None else None, _u8p(codes), _u8p(scales))
+    if rc:
+        raise ValueError(f"oracle_block_quantize_e4m3 failed ({rc})")
+    return codes, scales
+
+
+def block_dequantize(codes: np.ndarray, scales: np.ndarray, block_rows: int = 64) -> np.ndarray:
+    """Exact values code * 2^(scale - 127) of block-quantised e4m3 data, float64."""
+    B, N, Hx, d = codes.shape
+    vals = decode(codes, "e4m3")
+    rows = np.arange(N) // block_rows
+    mult = np.ldexp(1.0, scales.astype(np.int64) - 127)          # [B, Hx, nb]
+    return vals * mult[:, :, rows].transpose(0, 2, 1)[..., None]          # [B, N, Hx, 1]

@@ -137,6 +137,14 @@ def make_inputs(B: int, H: int, Hkv: int, N: int, d: int, dtype: str, seed: int,
     return out
 
 
+def random_signs(d: int, seed: int) -> np.ndarray:
+    """d random signs (+1.0 / -1.0, float32) for the incoherent-processing rotation: bit 0
+    of ``PCG64(seed)`` 32-bit draws, 1 -> -1."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    bits = rng.integers(0, 2**32, size=d, dtype=np.uint64) & 1
+    return np.where(bits == 1, -1.0, 1.0).astype(np.float32)
+
+
 def workload_inputs(w: Workload, keep_f32: bool = False, **overrides):
     """Inputs of a named workload (optionally with some sizes overridden)."""
     if overrides:

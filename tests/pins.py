@@ -430,7 +430,121 @@ def pin_window_reductions():
         _close(l2[:, :, 0], lse[:, :, i], 1e-13, f"causal window row {i} = slice attention (lse)")
 
 
+# Block quantisation to e4m3 and incoherent processing. The abstract of "FlashAttention-3:
+# Fast and Accurate Attention with Asynchrony and Low-precision" names both without
+# defining them; the readings pinned here: one power-of-two scale per 64-row slab of each
+# (batch, head), codes by round-to-nearest-even, rotation (x * s) H with H Sylvester-Hadamard.
+def _e4m3_values():
+    return torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+# P18 -- the e4m3 encoder against torch's float8_e4m3fn cast and against brute force
+# nearest-value search, including every tie and the saturation and sign rules.
+def pin_e4m3_encode():
+    vals = _e4m3_values()
+    fin = np.isfinite(vals)
+    grid = np.unique(vals[fin])                                   # sorted finite values
+    mids = (grid[:-1] + grid[1:]) / 2                             # exact ties (in float32 too)
+    rng = np.random.default_rng(41)
+    ys = np.concatenate([grid, mids, rng.uniform(-448, 448, 20000), rng.standard_normal(20000) * 0.01,
+                         np.ldexp(rng.uniform(-1, 1, 5000), rng.integers(-12, 9, 5000))]).astype(np.float32)
+    codes = oracle.e4m3_encode(ys)
+    ref = torch.from_numpy(ys).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref), f"e4m3 encode vs torch: {int((codes != ref).sum())} differ"
+    # brute force: the decoded code is a nearest finite value; at a tie its fraction is even
+    dec = vals[codes]
+    dist = np.abs(dec - ys.astype(np.float64))
+    best = np.min(np.abs(grid[None, :] - ys.astype(np.float64)[:, None]), axis=1)
+    assert np.all(dist == best), "e4m3 encode is not nearest"
+    tie = np.isin(ys.astype(np.float64), mids)
+    assert np.all((codes[tie] & 1) == 0), "e4m3 ties go to the even code"
+    sat = oracle.e4m3_encode(np.array([448.0, 460.0, 1e6, -500.0, np.inf, -np.inf], np.float32))
+    assert list(sat) == [0x7E, 0x7E, 0x7E, 0xFE, 0x7E, 0xFE], f"saturation {sat}"
+    special = oracle.e4m3_encode(np.array([0.0, -0.0, np.nan, 2.0 ** -10, -(2.0 ** -10) * 1.5], np.float32))
+    assert list(special) == [0x00, 0x80, 0x7F, 0x00, 0x81], f"zero/NaN/subnormal {special}"
+
+
+# P19 -- the fast Walsh-Hadamard transform against the Sylvester-Hadamard matrix of
+# scipy (fp64 product), H H = d I exactly on small integers, and Parseval.
+def pin_fwht():
+    import scipy.linalg
+    rng = np.random.default_rng(42)
+    for d in (1, 2, 8, 64, 128):
+        H = scipy.linalg.hadamard(d).astype(np.float64)
+        x = rng.standard_normal((7, d)).astype(np.float32)
+        y = oracle.fwht_f32(x)
+        ref = x.astype(np.float64) @ H
+        assert np.max(np.abs(y - ref)) <= 8 * d * 2.0 ** -24 * np.max(np.abs(x)) * np.log2(max(d, 2)), f"fwht d={d}"
+        xi = rng.integers(-8, 9, (5, d)).astype(np.float32)
+        assert np.array_equal(oracle.fwht_f32(oracle.fwht_f32(xi)), d * xi), f"H H = d I (d={d})"
+        assert np.array_equal(oracle.fwht_f32(xi), (xi.astype(np.float64) @ H).astype(np.float32)), \
+            f"exact on integers (d={d})"
+        assert abs(np.sum(ref ** 2) - d * np.sum(x.astype(np.float64) ** 2)) < 1e-6 * d * np.sum(x ** 2) + 1e-9
+
+
+# P20 -- block quantisation: the scale exponent is the smallest that fits the slab's
+# largest magnitude under 448 (floored at -127, 0 for a zero slab), every code is the
+# e4m3 rounding of the (rotated) value times 2^-e, and ragged tails form their own slab.
+def pin_block_quantize():
+    rng = np.random.default_rng(43)
+    vals = _e4m3_values()
+    grid = np.unique(vals[np.isfinite(vals)])
+    B, N, Hx, d, br = 2, 150, 3, 64, 64
+    x = (rng.standard_normal((B, N, Hx, d)) * np.exp(rng.uniform(-3, 3, (B, 1, Hx, 1)))).astype(np.float32)
+    x[0, 64:128, 1] = 0.0                                        # an all-zero slab
+    x[1, 0:64, 0] = 0.0
+    x[1, 5, 0, 7] = 448.0                                        # amax exactly 448: e = 0
+    x[1, 64:128, 2] *= 2.0 ** -140 / np.abs(x[1, 64:128, 2]).max()   # tiny slab: e floored
+    signs = np.where(rng.random(d) < 0.5, -1.0, 1.0).astype(np.float32)
+    import scipy.linalg
+    H = scipy.linalg.hadamard(d).astype(np.float64)
+    for sg in (None, signs):
+        codes, scales = oracle.block_quantize(x.astype(np.float64), br, sg)
+        nb = (N + br - 1) // br
+        assert scales.shape == (B, Hx, nb)
+        y = x.astype(np.float64) if sg is None else (x.astype(np.float64) * sg) @ H
+        for b in range(B):
+            for h in range(Hx):
+                for k in range(nb):
+                    slab = y[b, k * br:(k + 1) * br, h]
+                    amax = np.max(np.abs(slab))
+                    e = int(scales[b, h, k]) - 127
+                    if amax == 0:
+                        assert e == 0 and np.all(codes[b, k * br:(k + 1) * br, h] & 0x7F == 0), "zero slab"
+                        continue
+                    if e > -127:
+                        assert amax * 2.0 ** -e <= 448 < amax * 2.0 ** -(e - 1), f"exponent b{b} h{h} k{k}"
+                    else:
+                        assert amax * 2.0 ** 127 <= 448, "floored exponent"
+                    dec = vals[codes[b, k * br:(k + 1) * br, h]] * 2.0 ** e
+                    # nearest e4m3 value after exact scaling (float32 rounding of the rotation
+                    # moves a value by at most a few float32 ulps)
+                    z = slab * 2.0 ** -e
+                    best = np.min(np.abs(grid[None, :] - z.reshape(-1)[:, None]), axis=1).reshape(z.shape)
+                    slack = 64 * 2.0 ** -24 * np.abs(z) + (0 if sg is None else 1e-6 * np.max(np.abs(z)))
+                    assert np.all(np.abs(dec * 2.0 ** -e - z) <= best + slack), f"codes b{b} h{h} k{k}"
+    assert int(oracle.block_quantize(x.astype(np.float64), br)[1][1, 0, 0]) == 127, "amax 448 -> e = 0"
+    assert int(oracle.block_quantize(x.astype(np.float64), br)[1][1, 2, 1]) == 0, "tiny slab -> e = -127"
+
+
+# P21 -- incoherent processing leaves attention unchanged: rotating Q and K by s H and
+# dividing the score scale by d gives the same output and lse (fp64, unquantised).
+def pin_rotation_identity():
+    import scipy.linalg
+    rng = np.random.default_rng(44)
+    for d in (64, 128):
+        q, k, v = _qkv(rng, 2, 40, 4, 2, d)
+        s = np.where(rng.random(d) < 0.5, -1.0, 1.0)
+        H = scipy.linalg.hadamard(d).astype(np.float64)
+        for causal in (False, True):
+            o, lse = oracle.attn_fwd_f64(q, k, v, causal, 0.3)
+            o2, lse2 = oracle.attn_fwd_f64((q * s) @ H, (k * s) @ H, v, causal, 0.3 / d)
+            _close(o2, o, 1e-12, f"rotated attention O (d={d})")
+            _close(lse2, lse, 1e-12, f"rotated attention lse (d={d})")
+
+
 ALL_PINS = [pin_mpmath_bruteforce, pin_torch_sdpa, pin_zero_query, pin_single_key, pin_two_keys,
             pin_affine_in_v, pin_probability_rows, pin_key_permutation, pin_key_shift, pin_gqa_repeat,
             pin_causal_prefix, pin_split_merge, pin_hardmax_and_range, pin_decoders, pin_golden_fixtures,
-            pin_window_bruteforce_and_sdpa, pin_window_closed_forms, pin_window_reductions]
+            pin_window_bruteforce_and_sdpa, pin_window_closed_forms, pin_window_reductions,
+            pin_e4m3_encode, pin_fwht, pin_block_quantize, pin_rotation_identity]

@@ -12,7 +12,9 @@ import pytest
 import oracle
 from tests import pins
 
-SRC = os.path.join(os.path.dirname(oracle.__file__), "attn_oracle.c")
+ORACLE_DIR = os.path.dirname(oracle.__file__)
+SRC = os.path.join(ORACLE_DIR, "attn_oracle.c")
+QSRC = os.path.join(ORACLE_DIR, "fp8_quant_oracle.c")
 
 MUTANTS = {
     "gqa_map_modulo": ("h / group", "h % Hkv"),
@@ -47,18 +49,42 @@ MUTANTS = {
     "decode_ignores_descale": ("dst[i] = x * mult;", "dst[i] = x;"),
 }
 
+# mutants of the block-quantisation oracle (fp8_quant_oracle.c)
+QMUTANTS = {
+    "encode_ties_away": ("double m = rint(ldexp(a, 3 - E));", "double m = round(ldexp(a, 3 - E));"),
+    "encode_subnormal_quantum": ("code = (uint8_t)rint(a * 512.0);", "code = (uint8_t)rint(a * 256.0);"),
+    "encode_no_saturation": ("if (a > 448.0) a = 448.0;", ""),
+    "encode_drops_sign": ("return neg ? (uint8_t)(code | 0x80) : code;", "return code;"),
+    "fwht_sign_swapped": ("x[j + h] = a - b;", "x[j + h] = b - a;"),
+    "fwht_skips_last_stage": ("for (int h = 1; h < d; h <<= 1)", "for (int h = 1; 2 * h < d; h <<= 1)"),
+    "exponent_strict_bound": ("<= 448.0 ? E - 8 : E - 7;", "< 448.0 ? E - 8 : E - 7;"),
+    "exponent_one_too_high": ("<= 448.0 ? E - 8 : E - 7;", "<= 448.0 ? E - 7 : E - 6;"),
+    "exponent_no_floor": ("if (e < -127) e = -127;", ""),
+    "signs_ignored": ("y[t] = signs ? (float)xr[t] * signs[t] : (float)xr[t];", "y[t] = (float)xr[t];"),
+    "amax_signed": ("if (fabsf(y[t]) > amax) amax = fabsf(y[t]);", "if (y[t] > amax) amax = y[t];"),
+    "scale_not_applied": ("c[t] = oracle_e4m3_encode((float)ldexp((double)y[t], -e));",
+                          "c[t] = oracle_e4m3_encode(y[t]);"),
+}
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
+
+ALL = {**{n: (SRC,) + m for n, m in MUTANTS.items()}, **{n: (QSRC,) + m for n, m in QMUTANTS.items()}}
+
+
+@pytest.mark.parametrize("name", sorted(ALL))
 def test_mutant_is_caught(name, tmp_path):
-    pattern, repl = MUTANTS[name]
-    src = open(SRC).read()
-    assert pattern in src, f"mutant {name}: pattern no longer in the oracle"
-    mutated = src.replace(pattern, repl)
-    c_path = tmp_path / "mutant.c"
+    target, pattern, repl = ALL[name]
+    sources = []
+    for path in (SRC, QSRC):
+        src = open(path).read()
+        if path == target:
+            assert pattern in src, f"mutant {name}: pattern no longer in the oracle"
+            src = src.replace(pattern, repl)
+        c_path = tmp_path / os.path.basename(path)
+        c_path.write_text(src)
+        sources.append(str(c_path))
     so_path = tmp_path / "libmutant.so"
-    c_path.write_text(mutated)
-    subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99", "-o", str(so_path),
-                    str(c_path), "-lm"], check=True)
+    subprocess.run(["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99", "-ffp-contract=off", "-o",
+                    str(so_path), *sources, "-lm"], check=True)
     lib = oracle.load(str(so_path))
     saved = oracle._lib()
     oracle._LIB = lib
