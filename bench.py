@@ -63,9 +63,17 @@ def to_dev(bits, dtype):
 
 def cpu_baseline(w: synth_inputs.Workload, inp: dict, budget_s: float = 12.0):
     """The fp64 oracle on a bounded sample: whole (batch, GQA group) slices of the same
-    inputs, in order, until about budget_s seconds of wall time on the host cores."""
+    inputs, in order, until about budget_s seconds of wall time on the host cores (for a
+    block-quantised workload: the oracle's block quantisation of the slice, then attention
+    on the dequantised values)."""
     import oracle
     dq, dk, dv = inp["descale"] if inp["descale"] else (1.0, 1.0, 1.0)
+    signs = synth_inputs.random_signs(w.d, w.seed) if w.fp8_block else None
+
+    def prep(x, sg):
+        if not w.fp8_block:
+            return x
+        return oracle.block_dequantize(*oracle.block_quantize(x, 64, sg))
     g = w.H // w.Hkv
     per_head = w.flops / (w.B * w.H)
     heads, elapsed = 0, 0.0
@@ -79,8 +87,10 @@ def cpu_baseline(w: synth_inputs.Workload, inp: dict, budget_s: float = 12.0):
             if elapsed >= budget_s:
                 break
             t0 = time.perf_counter()
-            oracle.attn_fwd_f64(np.ascontiguousarray(q[:, :, hk * g:(hk + 1) * g]), k[:, :, hk:hk + 1],
-                                v[:, :, hk:hk + 1], w.causal, w.scale, w.window)
+            qs = prep(np.ascontiguousarray(q[:, :, hk * g:(hk + 1) * g]), signs)
+            ks = prep(np.ascontiguousarray(k[:, :, hk:hk + 1]), signs)
+            vs = prep(np.ascontiguousarray(v[:, :, hk:hk + 1]), None)
+            oracle.attn_fwd_f64(qs, ks, vs, w.causal, w.scale / (w.d if w.fp8_block else 1), w.window)
             elapsed += time.perf_counter() - t0
             heads += g
     flops = per_head * heads
@@ -124,22 +134,46 @@ def main():
     inp = synth_inputs.workload_inputs(w)
     q, k, v = (to_dev(inp[x], w.dtype) for x in "qkv")
     dt = w.dtype if w.dtype == "e4m3" else None
-    o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale, descale=inp["descale"], dtype=dt,
-                    window=w.window)
+    stream = torch.cuda.current_stream()
+    quant = None
+    if w.fp8_block:
+        # block quantisation (Q and K rotated) on the GPU, timed on its own; the step is
+        # the attention on the quantised codes, as for the per-tensor e4m3 workload
+        signs = torch.from_numpy(synth_inputs.random_signs(w.d, w.seed)).cuda()
+        qz = [fa.quantize_e4m3_block(x, sg) for x, sg in ((q, signs), (k, signs), (v, None))]
+        reps = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            for (x, sg), (c, sc) in zip(((q, signs), (k, signs), (v, None)), qz):
+                fa.quantize_e4m3_block(x, sg, codes=c, scales=sc)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        q_ms = e0.elapsed_time(e1) / reps
+        nbytes = sum(x.numel() * 3 + sc.numel() for x, (c, sc) in zip((q, k, v), qz))
+        quant = {"kernel": "quantize_e4m3_block (q, k, v)", "ms": round(q_ms, 5),
+                 "bytes": nbytes, "achieved_GBps": round(nbytes / (q_ms * 1e-3) / 1e9, 1), "peak_GBps": 8000.0,
+                 "frac": round(nbytes / (q_ms * 1e-3) / 1e9 / 8000.0, 4)}
+        (qc, qs), (kc, ks), (vc, vs) = qz
+
+        def step(o=None, lse=None):
+            return fa.fwd_fp8_block(qc, kc, vc, qs, ks, vs, causal=w.causal, scale=w.scale / w.d, out=o, lse=lse)
+    else:
+        def step(o=None, lse=None):
+            return fa.fwd(q, k, v, causal=w.causal, scale=w.scale, descale=inp["descale"], dtype=dt, out=o,
+                          lse=lse, window=w.window)
+    o, lse = step()
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o.float()).all()), "non-finite output"
 
     for _ in range(args.warmup):
-        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, descale=inp["descale"], dtype=dt, out=o, lse=lse,
-               window=w.window)
-    stream = torch.cuda.current_stream()
+        step(o, lse)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev0.record(stream)
     for _ in range(args.steps):
-        fa.fwd(q, k, v, causal=w.causal, scale=w.scale, descale=inp["descale"], dtype=dt, out=o, lse=lse,
-               window=w.window)
+        step(o, lse)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -148,7 +182,8 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     value = w.flops / (ms_per_step * 1e-3) / 1e12
     achieved = w.flops / (kernel_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[w.dtype]
+    cdt = "e4m3" if w.fp8_block else w.dtype
+    peak = PEAK_TFLOPS[cdt]
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -160,15 +195,18 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": cdt,
         "data": "synthetic (seeded N(0,1) inputs)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
                    "causal": w.causal, "scale": w.scale, "flop_per_step": w.flops,
-                   **({"window": list(w.window)} if w.window else {})},
+                   **({"window": list(w.window)} if w.window else {}),
+                   **({"fp8": "block scales (64 rows, E8M0), Hadamard-rotated q/k"} if w.fp8_block else {})},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name),
                      "kernel_ms": round(kernel_ms, 5)},
     }
+    if quant:
+        out["quantize"] = quant
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(out), flush=True)

@@ -66,6 +66,12 @@ struct FwdArgs {
   float c;              // scale * log2(e) (times the q and k descales for e4m3)
   float v_scale;        // 1 for 16-bit inputs; the v descale for e4m3
   int wl, wr;           // key window of the band mask: query i sees keys i-wl .. i+wr
+  // e4m3 with block scales: one E8M0 byte (2^(byte-127)) per FA_FP8_BLOCK_ROWS positions
+  // of each (batch, head), [B][H][nb] for q and [B][Hkv][nb] for k and v
+  const uint8_t* q_scales;
+  const uint8_t* k_scales;
+  const uint8_t* v_scales;
+  int nb;
 };
 
 // Masks, one kernel instance each: none; causal (key j visible to query i iff j <= i);
@@ -581,18 +587,30 @@ __device__ __forceinline__ f32x16 mfma_fp8(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b
   // formats 0/0: both operands e4m3; no block scales
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
-// four e4m3 codes -> four bf16 (exact: every e4m3 value is a bf16 value)
-__device__ __forceinline__ u32x2 e4m3x4_to_bf16(unsigned x) {
+// four e4m3 codes -> four bf16, times a power-of-two scale (exact: every e4m3 value is a
+// bf16 value, and a power-of-two factor only moves the exponent)
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16(unsigned x, float scale = 1.0f) {
   u32x2 r;
-  r[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x, 1.0f, false));
-  r[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x, 1.0f, true));
+  r[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x, scale, false));
+  r[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)x, scale, true));
   return r;
+}
+// the same P.V product with operand A (V^T) scaled by an E8M0 byte (2^(byte-127)) per lane;
+// every lane passes the same byte here, so the whole 64-key tile takes one scale
+__device__ __forceinline__ f32x16 mfma_fp8_scaled(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x16 c, int a_scale) {
+  const i32x8 a = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+  const i32x8 b = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, a_scale, 0, 127);
+}
+// E8M0 byte -> float 2^(byte-127) (byte 0 is the subnormal 2^-127)
+__device__ __forceinline__ float e8m0_to_f32(unsigned byte) {
+  return __uint_as_float(byte ? byte << 23 : 0x00400000u);
 }
 __device__ __forceinline__ int vt8_byte(int dim, int pos) {      // V^T tile: byte pos of a row
   return dim * 64 + ((((pos >> 4) ^ ((dim >> 2) & 3))) << 4) + (pos & 15);
 }
 
-template <int D, int MASK>
+template <int D, int MASK, bool BLOCK>
 __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
   constexpr bool CAUSAL = MASK == kMaskCausal;
   constexpr bool BAND = MASK == kMaskBand;
@@ -628,13 +646,16 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
   const uint8_t* kp = (const uint8_t*)a.k + ((size_t)b * N + kv0) * kv_row_stride + (size_t)hk * D;
   const uint8_t* vp = (const uint8_t*)a.v + ((size_t)b * N + kv0) * kv_row_stride + (size_t)hk * D;
 
-  // Q^T operand in bf16: lane holds q[qi][16ks + 8hi .. +7]
+  // Q^T operand in bf16: lane holds q[qi][16ks + 8hi .. +7]; with block scales the
+  // wavefront's 32 queries lie in one block, whose scale the conversion applies exactly
   u32x4 qreg[kKsteps];
   const int qi_ld = min(qi, N - 1);
+  float q_mult = 1.0f;
+  if constexpr (BLOCK) q_mult = e8m0_to_f32(a.q_scales[((size_t)b * a.H + h) * a.nb + min(qw0, N - 1) / FA_FP8_BLOCK_ROWS]);
 #pragma unroll
   for (int ks = 0; ks < kKsteps; ++ks) {
     const u32x2 raw = *(const u32x2*)(qp + (size_t)qi_ld * q_row_stride + ks * 16 + hi * 8);
-    const u32x2 lo = e4m3x4_to_bf16(raw[0]), hi4 = e4m3x4_to_bf16(raw[1]);
+    const u32x2 lo = e4m3x4_to_bf16(raw[0], q_mult), hi4 = e4m3x4_to_bf16(raw[1], q_mult);
     qreg[ks] = u32x4{lo[0], lo[1], hi4[0], hi4[1]};
   }
 
@@ -664,30 +685,50 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
   const int v_dq = min(l32, D / 4 - 1);
   u32x4 kst;
   unsigned vst[4];
+  // block scales of the staged tiles (key tile = scale block, both FA_FP8_BLOCK_ROWS = kBc
+  // keys, and kv0 is a multiple of kBc): K's byte rides with its codes from load to store
+  // and is applied by the conversion; V's becomes current when its tile is stored, and
+  // stays so for both halves' P.V of that tile. The bytes are only read where the codes
+  // are, so that no wait for the prefetch lands right after it is issued.
+  static_assert(FA_FP8_BLOCK_ROWS == kBc, "one scale per key tile");
+  const size_t kv_sc0 = ((size_t)b * a.Hkv + hk) * a.nb + kv0 / kBc;
+  unsigned k_sc = 127;
+  int v_sc_next = 127, v_sc = 127;
   auto load_k = [&](int j) __attribute__((always_inline)) {
     const int key = min(j * kBc + 8 * wv + k_key, nk - 1);
     kst = __builtin_amdgcn_raw_buffer_load_b128(krs, (unsigned)key * row_bytes + k_chunk * 16u, 0, 0);
+    if constexpr (BLOCK) k_sc = a.k_scales[kv_sc0 + j];
   };
+  // the row offset of a full tile is wavefront-uniform (scalar operand), the lane's half
+  // (4 hi rows) rides in the per-lane offset; a ragged tile clamps rows per lane
+  const unsigned v_lane_off = (unsigned)v_dq * 4u + (unsigned)(4 * hi) * row_bytes;
   auto load_v = [&](int j) __attribute__((always_inline)) {
     const int j0 = j * kBc;
-    const bool full = j0 + kBc <= nk;
+    if (j0 + kBc <= nk) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      int key = j0 + 8 * wv + 4 * hi + r;
-      if (!full) key = min(key, nk - 1);
-      vst[r] = __builtin_amdgcn_raw_buffer_load_b32(vrs, (unsigned)v_dq * 4u, key * (int)row_bytes, 0);
+      for (int r = 0; r < 4; ++r)
+        vst[r] = __builtin_amdgcn_raw_buffer_load_b32(vrs, v_lane_off, (j0 + 8 * wv + r) * (int)row_bytes, 0);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key = min(j0 + 8 * wv + 4 * hi + r, nk - 1);
+        vst[r] = __builtin_amdgcn_raw_buffer_load_b32(vrs, (unsigned)v_dq * 4u + (unsigned)key * row_bytes, 0, 0);
+      }
     }
+    if constexpr (BLOCK) v_sc_next = a.v_scales[kv_sc0 + j];
   };
   auto store_k = [&](int buf) __attribute__((always_inline)) {
     if (!k_lane) return;
+    const float k_mult = BLOCK ? e8m0_to_f32(k_sc) : 1.0f;
     unsigned char* st = lds + buf * kStageBytes;
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
-      const u32x2 c0 = e4m3x4_to_bf16(kst[2 * x]), c1 = e4m3x4_to_bf16(kst[2 * x + 1]);
+      const u32x2 c0 = e4m3x4_to_bf16(kst[2 * x], k_mult), c1 = e4m3x4_to_bf16(kst[2 * x + 1], k_mult);
       *(u32x4*)(st + k_byte<D>(8 * wv + k_key, k_chunk * 16 + x * 8)) = u32x4{c0[0], c0[1], c1[0], c1[1]};
     }
   };
   auto store_v = [&](int buf) __attribute__((always_inline)) {
+    if constexpr (BLOCK) v_sc = v_sc_next;
     if (!v_lane) return;
     // 4x4 byte transpose: out[dd] = bytes (key r = 0..3) of dim 4 v_dq + dd
     const unsigned t0 = __builtin_amdgcn_perm(vst[1], vst[0], 0x05010400u);
@@ -749,7 +790,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
     for (int db = 0; db < kDblocks; ++db) {
       const u32x4 a0 = lds_load<u32x4>(st, voff[db][0]);
       const u32x4 a1 = lds_load<u32x4>(st, voff[db][1]);
-      oacc[db] = mfma_fp8(a0, a1, p[0], p[1], oacc[db]);
+      if constexpr (BLOCK) oacc[db] = mfma_fp8_scaled(a0, a1, p[0], p[1], oacc[db], v_sc);
+      else oacc[db] = mfma_fp8(a0, a1, p[0], p[1], oacc[db]);
     }
     lacc = mfma_fp8(ones, ones, p[0], p[1], lacc);
   };
@@ -892,9 +934,9 @@ fa_status launch(const FwdArgs& args, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-template <int D, int MASK>
+template <int D, int MASK, bool BLOCK = false>
 fa_status launch_fp8(const FwdArgs& args, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, MASK>), dim3(args.total), dim3(kThreads), 0, stream, args);
+  hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, MASK, BLOCK>), dim3(args.total), dim3(kThreads), 0, stream, args);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -932,6 +974,24 @@ fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* 
                    int Hkv, int N, int d, int causal, int window_left, int window_right,
                    float scale, fa_dtype dtype, const float* descale_qkv, void* stream);
 
+void fill_common(FwdArgs& args, const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                 int H, int Hkv, int N) {
+  args.q = q;
+  args.k = k;
+  args.v = v;
+  args.o = o;
+  args.lse = lse;
+  args.B = B;
+  args.H = H;
+  args.Hkv = Hkv;
+  args.N = N;
+  args.group = H / Hkv;
+  args.num_qtiles = (N + kBr - 1) / kBr;
+  args.total = args.num_qtiles * H * B;
+  args.q_scales = args.k_scales = args.v_scales = nullptr;
+  args.nb = (N + FA_FP8_BLOCK_ROWS - 1) / FA_FP8_BLOCK_ROWS;
+}
+
 fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                    int Hkv, int N, int d, int causal, int window_left, int window_right,
                    float scale, fa_dtype dtype, const float* descale_qkv, void* stream) {
@@ -949,18 +1009,7 @@ fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* 
     return FA_ERR_INVALID_ARG;
   }
   FwdArgs args;
-  args.q = q;
-  args.k = k;
-  args.v = v;
-  args.o = o;
-  args.lse = lse;
-  args.B = B;
-  args.H = H;
-  args.Hkv = Hkv;
-  args.N = N;
-  args.group = H / Hkv;
-  args.num_qtiles = (N + kBr - 1) / kBr;
-  args.total = args.num_qtiles * H * B;
+  fill_common(args, q, k, v, o, lse, B, H, Hkv, N);
   args.c = (float)((double)scale * 1.4426950408889634);
   args.v_scale = 1.0f;
   const int mask = resolve_mask(N, causal, window_left, window_right, &args.wl, &args.wr);
@@ -996,6 +1045,29 @@ fa_status fa_fwd_local(const void* q, const void* k, const void* v, void* o, flo
                        void* stream) {
   return fwd_impl(q, k, v, o, lse, B, H, Hkv, N, d, causal, window_left, window_right, scale, dtype,
                   descale_qkv, stream);
+}
+
+fa_status fa_fwd_fp8_block(const void* q, const void* k, const void* v, const unsigned char* q_scales,
+                           const unsigned char* k_scales, const unsigned char* v_scales, void* o,
+                           float* lse, int B, int H, int Hkv, int N, int d, int causal, float scale,
+                           void* stream) {
+  fa_status st = check_sizes(B, H, Hkv, N, d, causal, FA_DTYPE_FP8_E4M3);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !o || !lse || !q_scales || !k_scales || !v_scales) return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  FwdArgs args;
+  fill_common(args, q, k, v, o, lse, B, H, Hkv, N);
+  args.c = (float)((double)scale * 1.4426950408889634);
+  args.v_scale = 1.0f;       // the V block scales are applied inside the P.V MFMA
+  args.wl = args.wr = N;
+  args.q_scales = q_scales;
+  args.k_scales = k_scales;
+  args.v_scales = v_scales;
+  hipStream_t s = (hipStream_t)stream;
+  if (d == 128) return causal ? launch_fp8<128, kMaskCausal, true>(args, s) : launch_fp8<128, kMaskNone, true>(args, s);
+  return causal ? launch_fp8<64, kMaskCausal, true>(args, s) : launch_fp8<64, kMaskNone, true>(args, s);
 }
 
 fa_status fa_fwd_query(int B, int H, int Hkv, int N, int d, int causal, fa_dtype dtype,

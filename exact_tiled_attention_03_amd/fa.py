@@ -13,6 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH = 0, 1, 2, 3
+FP8_BLOCK_ROWS = 64      # FA_FP8_BLOCK_ROWS
 FA_DTYPE_F16, FA_DTYPE_BF16, FA_DTYPE_FP8_E4M3 = 0, 1, 2
 DTYPE_NAMES = {"f16": FA_DTYPE_F16, "bf16": FA_DTYPE_BF16, "e4m3": FA_DTYPE_FP8_E4M3}
 
@@ -42,6 +43,10 @@ def lib() -> ctypes.CDLL:
             L.fa_fwd_local.argtypes = [vp, vp, vp, vp, vp] + [c_int] * 8 + [c_float, c_int,
                                                                             ctypes.POINTER(c_float), vp]
             L.fa_fwd_local.restype = c_int
+            L.fa_quantize_e4m3_block.argtypes = [vp, c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp]
+            L.fa_quantize_e4m3_block.restype = c_int
+            L.fa_fwd_fp8_block.argtypes = [vp] * 8 + [c_int] * 6 + [c_float, vp]
+            L.fa_fwd_fp8_block.restype = c_int
             L.fa_fwd_query.argtypes = [c_int] * 7 + [szp] * 5
             L.fa_fwd_query.restype = c_int
             L.fa_status_string.argtypes = [c_int]
@@ -82,6 +87,21 @@ def fa_fwd_local(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B
     return int(lib().fa_fwd_local(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Hkv, N, d, int(causal),
                                   int(window_left), int(window_right), float(scale), int(dtype), ds,
                                   stream))
+
+
+def fa_quantize_e4m3_block(x_ptr: int, in_dtype: int, B: int, N: int, Hx: int, d: int, signs_ptr: int,
+                           codes_ptr: int, scales_ptr: int, stream: int = 0) -> int:
+    """Direct call of fa_quantize_e4m3_block with raw pointers; returns the status code."""
+    return int(lib().fa_quantize_e4m3_block(x_ptr, int(in_dtype), B, N, Hx, d, signs_ptr or None, codes_ptr,
+                                            scales_ptr, stream))
+
+
+def fa_fwd_fp8_block(q_ptr: int, k_ptr: int, v_ptr: int, qs_ptr: int, ks_ptr: int, vs_ptr: int, o_ptr: int,
+                     lse_ptr: int, B: int, H: int, Hkv: int, N: int, d: int, causal: int, scale: float,
+                     stream: int = 0) -> int:
+    """Direct call of fa_fwd_fp8_block with raw pointers; returns the status code."""
+    return int(lib().fa_fwd_fp8_block(q_ptr, k_ptr, v_ptr, qs_ptr, ks_ptr, vs_ptr, o_ptr, lse_ptr, B, H, Hkv,
+                                      N, d, int(causal), float(scale), stream))
 
 
 def fa_fwd_query(B: int, H: int, Hkv: int, N: int, d: int, causal: int, dtype: int) -> dict:
@@ -138,4 +158,64 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, descale=None,
                           Hkv, N, d, int(bool(causal)), int(window[0]), int(window[1]), scale, code,
                           descale, stream)
     _check(st)
+    return out, lse
+
+
+def _stream(t, stream):
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream if stream is None else stream
+
+
+def quantize_e4m3_block(x, signs=None, codes=None, scales=None, stream=None):
+    """Block quantisation of a float16/bfloat16 device tensor x [B,N,Hx,d] to e4m3 with
+    one power-of-two scale per FP8_BLOCK_ROWS positions of each (batch, head); with
+    `signs` (float32 device tensor of d values +-1), rows are rotated by (x * signs) H
+    first. Returns (codes uint8 [B,N,Hx,d], scales uint8 E8M0 [B,Hx,nb])."""
+    import torch
+    B, N, Hx, d = x.shape
+    code = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16}[x.dtype]
+    nb = (N + FP8_BLOCK_ROWS - 1) // FP8_BLOCK_ROWS
+    if codes is None:
+        codes = torch.empty((B, N, Hx, d), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, Hx, nb), dtype=torch.uint8, device=x.device)
+    for t in (x, codes, scales) + ((signs,) if signs is not None else ()):
+        if not t.is_contiguous() or t.device != x.device:
+            raise ValueError("tensors must be contiguous and on the same device")
+    if tuple(codes.shape) != (B, N, Hx, d) or codes.dtype != torch.uint8 or tuple(scales.shape) != (B, Hx, nb):
+        raise ValueError("codes/scales have the wrong shape or type")
+    if signs is not None and (tuple(signs.shape) != (d,) or signs.dtype != torch.float32):
+        raise ValueError("signs must be a float32 tensor of d values")
+    _check(fa_quantize_e4m3_block(x.data_ptr(), code, B, N, Hx, d, signs.data_ptr() if signs is not None else 0,
+                                  codes.data_ptr(), scales.data_ptr(), _stream(x, stream)))
+    return codes, scales
+
+
+def fwd_fp8_block(q, k, v, q_scales, k_scales, v_scales, causal: bool = False, scale: float | None = None,
+                  out=None, lse=None, stream=None):
+    """Attention forward on block-quantised e4m3 inputs (uint8 code tensors q [B,N,H,d],
+    k and v [B,N,Hkv,d], with their E8M0 block scales). Returns (o bfloat16, lse)."""
+    import torch
+    B, N, H, d = q.shape
+    Hkv = k.shape[2]
+    nb = (N + FP8_BLOCK_ROWS - 1) // FP8_BLOCK_ROWS
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, N, H, d), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    for t in (q, k, v, q_scales, k_scales, v_scales, out, lse):
+        if not t.is_contiguous() or t.device != q.device:
+            raise ValueError("tensors must be contiguous and on the same device")
+    if tuple(k.shape) != (B, N, Hkv, d) or tuple(v.shape) != (B, N, Hkv, d):
+        raise ValueError("k and v must be [B,N,Hkv,d] matching q")
+    if (tuple(q_scales.shape) != (B, H, nb) or tuple(k_scales.shape) != (B, Hkv, nb)
+            or tuple(v_scales.shape) != (B, Hkv, nb)):
+        raise ValueError("block scales must be [B,H,nb] (q) and [B,Hkv,nb] (k, v)")
+    if tuple(out.shape) != (B, N, H, d) or out.dtype != torch.bfloat16 or tuple(lse.shape) != (B, H, N):
+        raise ValueError("out/lse have the wrong shape or type")
+    _check(fa_fwd_fp8_block(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_scales.data_ptr(), k_scales.data_ptr(),
+                            v_scales.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Hkv, N, d, int(bool(causal)),
+                            scale, _stream(q, stream)))
     return out, lse

@@ -100,6 +100,48 @@ fa_status fa_fwd_local(const void* q, const void* k, const void* v, void* o, flo
                        int window_right, float scale, fa_dtype dtype,
                        const float* descale_qkv, void* stream);
 
+/* Rows (sequence positions) per block of the e4m3 block quantisation. */
+#define FA_FP8_BLOCK_ROWS 64
+
+/*
+ * Block quantisation to e4m3 with optional incoherent processing: the two parts of the
+ * FP8 mode named in the abstract of "FlashAttention-3: Fast and Accurate Attention with
+ * Asynchrony and Low-precision", which defines neither; the library's reading:
+ *   - x is a [B][N][Hx][d] tensor of in_dtype (F16 or BF16), 16-byte aligned;
+ *   - if `signs` is not NULL (device pointer to d floats, each +1 or -1, 16-byte
+ *     aligned), every row is first replaced by (x * signs) H, H the d x d
+ *     Sylvester-Hadamard matrix (entries +-1, H H^T = d I), computed in float32 by the
+ *     fast Walsh-Hadamard butterflies h = 1, 2, ..., d/2; rotating both Q and K this way
+ *     multiplies every score by d, so pass scale / d to the attention call;
+ *   - every block of FA_FP8_BLOCK_ROWS consecutive positions of one (b, head) gets the
+ *     scale 2^e, e the smallest integer with (block max |x|) * 2^-e <= 448, floored at
+ *     -127, and 0 for an all-zero block; scales[(b * Hx + head) * nb + blk] = e + 127
+ *     (an E8M0 byte), nb = ceil(N / FA_FP8_BLOCK_ROWS);
+ *   - codes (same layout as x, one byte each, 8-byte aligned) are the OCP E4M3 round-to-
+ *     nearest-even of x * 2^-e (exact scaling, saturated at +-448).
+ * Inputs must be finite. d in {64, 128}. Ownership, errors and execution as for fa_fwd
+ * (F16/BF16 only: FP8_E4M3 input is FA_ERR_UNSUPPORTED). One kernel on `stream`.
+ */
+fa_status fa_quantize_e4m3_block(const void* x, fa_dtype in_dtype, int B, int N, int Hx, int d,
+                                 const float* signs, void* codes, unsigned char* scales,
+                                 void* stream);
+
+/*
+ * Attention forward on block-quantised e4m3 inputs (as written by
+ * fa_quantize_e4m3_block): the logical value of element (b, n, head, t) is its e4m3 code
+ * times 2^(scale byte - 127) of block n / FA_FP8_BLOCK_ROWS of that (b, head).
+ *   q_scales  device pointer, [B][H][nb] bytes; k_scales, v_scales [B][Hkv][nb] bytes,
+ *             nb = ceil(N / FA_FP8_BLOCK_ROWS).
+ * Q and K scales are applied exactly when their codes are widened to bf16 for the
+ * Q K^T product; V scales are the per-tile scale operand of the scaled e4m3 P.V MFMA.
+ * o is bfloat16. Otherwise as fa_fwd with dtype FP8_E4M3 (no descale argument; when Q
+ * and K were rotated by the quantiser, pass scale / d).
+ */
+fa_status fa_fwd_fp8_block(const void* q, const void* k, const void* v,
+                           const unsigned char* q_scales, const unsigned char* k_scales,
+                           const unsigned char* v_scales, void* o, float* lse, int B, int H,
+                           int Hkv, int N, int d, int causal, float scale, void* stream);
+
 /*
  * Shape query: byte sizes of every buffer fa_fwd reads or writes for these arguments,
  * after the same size checks fa_fwd makes. Any output pointer may be NULL.

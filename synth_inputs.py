@@ -39,6 +39,7 @@ class Workload:
     outlier_frac: float = 0.0
     outlier_mult: float = 20.0
     window: tuple | None = None     # (left, right) key window; negative side = unbounded
+    fp8_block: bool = False         # e4m3 block-quantised on the GPU (drawn as bf16, rotated Q/K)
 
     @property
     def flops(self) -> float:
@@ -65,7 +66,8 @@ def _w(name, B, H, Hkv, N, d, causal, dtype, seed, **kw):
 
 # The five workloads: a tiny fp16 case, bf16 multi-head, bf16 causal long sequence,
 # bf16 causal grouped-query, and e4m3 with outliers; then a causal sliding-window case
-# (each query sees itself and the 4095 keys before it).
+# (each query sees itself and the 4095 keys before it), and the e4m3 shape again drawn in
+# bf16 for block quantisation with the Hadamard rotation (signs from the same seed).
 WORKLOADS = {
     w.name: w for w in [
         _w("tiny_f16_b1_h2_n128_d64", 1, 2, 2, 128, 64, False, "f16", 1001),
@@ -76,6 +78,8 @@ WORKLOADS = {
            outlier_frac=1e-3, outlier_mult=20.0),
         _w("swa_causal_bf16_b1_h32_kv8_n32768_d128_w4096", 1, 32, 8, 32768, 128, True, "bf16", 1006,
            window=(4095, -1)),
+        _w("fp8_block_hadamard_b8_h16_n4096_d128", 8, 16, 16, 4096, 128, False, "bf16", 1005,
+           outlier_frac=1e-3, outlier_mult=20.0, fp8_block=True),
     ]
 }
 

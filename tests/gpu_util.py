@@ -53,6 +53,17 @@ def compare(o, o_ref, lse, lse_ref, dtype: str, what: str = "", extra_bound=None
 
 def fp8_quantization_bound(inp: dict, causal: bool, scale: float, o_ref: np.ndarray,
                            window=None) -> np.ndarray:
+    """fp8_bound_from_values on the decoded per-tensor-scaled e4m3 inputs of `inp`."""
+    import oracle
+    dq, dk, dv = inp["descale"]
+    q = oracle.decode(inp["q"], "e4m3", dq)
+    k = oracle.decode(inp["k"], "e4m3", dk)
+    v = oracle.decode(inp["v"], "e4m3", dv)
+    return fp8_bound_from_values(q, k, v, causal, scale, o_ref, window)
+
+
+def fp8_bound_from_values(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: float,
+                          o_ref: np.ndarray, window=None) -> np.ndarray:
     """Per-element bound on |O_gpu - O_ref| from rounding the probabilities to e4m3.
 
     The kernel stores p~_j = p_j (1 + d_j), |d_j| <= u = 2^-4 (round to nearest, 3 fraction
@@ -61,12 +72,8 @@ def fp8_quantization_bound(inp: dict, causal: bool, scale: float, o_ref: np.ndar
       |O_gpu - O_ref| = |sum_j (w~_j - w_j) (v_j - O_ref)| <= 2u/(1-u) * sum_j w_j |v_j - O_ref|.
     Added: bf16 output rounding (2^-8 |O|, twice the half-ulp) and 2e-3 for float32
     accumulation and probabilities below the e4m3 normal range. Small shapes only (uses the
-    oracle's N x N probabilities)."""
+    oracle's N x N probabilities); q, k, v are the exact fp64 input values."""
     import oracle
-    dq, dk, dv = inp["descale"]
-    q = oracle.decode(inp["q"], "e4m3", dq)
-    k = oracle.decode(inp["k"], "e4m3", dk)
-    v = oracle.decode(inp["v"], "e4m3", dv)
     B, N, H, d = q.shape
     g = H // k.shape[2]
     u = 2.0 ** -4

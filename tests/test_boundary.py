@@ -117,6 +117,47 @@ def test_fwd_local_rejects_before_launch(over, status, window):
     assert st == status
 
 
+@pytest.mark.parametrize("over,status", [
+    (dict(x=0), fa.FA_ERR_INVALID_ARG),
+    (dict(codes=0), fa.FA_ERR_INVALID_ARG),
+    (dict(scales=0), fa.FA_ERR_INVALID_ARG),
+    (dict(x=FAKE + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(codes=FAKE + 4), fa.FA_ERR_INVALID_ARG),
+    (dict(signs=FAKE + 4), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=fa.FA_DTYPE_FP8_E4M3), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=9), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=0), fa.FA_ERR_INVALID_ARG),
+    (dict(N=1 << 20, Hx=1 << 5, d=128), fa.FA_ERR_INVALID_ARG),   # 2^32 elements
+])
+def test_quantize_rejects_before_launch(over, status):
+    a = dict(x=FAKE, dtype=fa.FA_DTYPE_BF16, B=1, N=64, Hx=2, d=128, signs=0, codes=FAKE, scales=FAKE)
+    a.update(over)
+    st = fa.fa_quantize_e4m3_block(a["x"], a["dtype"], a["B"], a["N"], a["Hx"], a["d"], a["signs"], a["codes"],
+                                   a["scales"])
+    assert st == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(qs=0), fa.FA_ERR_INVALID_ARG),
+    (dict(ks=0), fa.FA_ERR_INVALID_ARG),
+    (dict(vs=0), fa.FA_ERR_INVALID_ARG),
+    (dict(o=FAKE + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=3), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=3), fa.FA_ERR_INVALID_ARG),
+    (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+])
+def test_fwd_fp8_block_rejects_before_launch(over, status):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, qs=FAKE, ks=FAKE, vs=FAKE, o=FAKE, lse=FAKE, B=1, H=4, Hkv=2, N=64, d=128,
+             causal=0, scale=0.1)
+    a.update(over)
+    st = fa.fa_fwd_fp8_block(a["q"], a["k"], a["v"], a["qs"], a["ks"], a["vs"], a["o"], a["lse"], a["B"], a["H"],
+                             a["Hkv"], a["N"], a["d"], a["causal"], a["scale"])
+    assert st == status
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "absent.so"))
     monkeypatch.setattr(binding, "_lib", None)

@@ -49,7 +49,7 @@ def test_small_full_parity(case):
     gu.compare(o, o_ref, lse, lse_ref, dtype, str(case))
 
 
-@pytest.mark.parametrize("name", [n for n in synth_inputs.WORKLOADS if synth_inputs.WORKLOADS[n].dtype != "e4m3"])
+@pytest.mark.parametrize("name", [n for n, w in synth_inputs.WORKLOADS.items() if w.dtype != "e4m3" and not w.fp8_block])
 def test_workload_sampled_parity(name):
     w = synth_inputs.WORKLOADS[name]
     _log(f"[workload] {name}")
