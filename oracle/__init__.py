@@ -27,7 +27,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "attn_oracle.c")
-_SOURCES = [_SRC, os.path.join(_HERE, "fp8_quant_oracle.c")]
+_SOURCES = [_SRC, os.path.join(_HERE, "fp8_quant_oracle.c"), os.path.join(_HERE, "attn_bwd_oracle.c")]
 _SO = os.path.join(_HERE, "liboracle.so")
 _LOCK = threading.Lock()
 _LIB = None
@@ -80,6 +80,8 @@ def load(path: str):
     lib.oracle_block_exponent.restype = ctypes.c_int
     lib.oracle_block_quantize_e4m3.argtypes = [dp] + [ctypes.c_int] * 5 + [fp, u8p, u8p]
     lib.oracle_block_quantize_e4m3.restype = ctypes.c_int
+    lib.oracle_attn_bwd_f64.argtypes = [dp] * 7 + [ctypes.c_int] * 8 + [ctypes.c_double]
+    lib.oracle_attn_bwd_f64.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -278,3 +280,24 @@ def block_dequantize(codes: np.ndarray, scales: np.ndarray, block_rows: int = 64
     rows = np.arange(N) // block_rows
     mult = np.ldexp(1.0, scales.astype(np.int64) - 127)          # [B, Hx, nb]
     return vals * mult[:, :, rows].transpose(0, 2, 1)[..., None]          # [B, N, Hx, 1]
+
+
+# ---- gradient of the forward (attn_bwd_oracle.c) ----
+
+def attn_bwd_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, causal: bool, scale: float,
+                 window=None):
+    """Analytic fp64 gradient of O = softmax(scale Q K^T [mask]) V for upstream dO (no
+    gradient through lse). q, dout [B,N,H,d]; k, v [B,N,Hkv,d]. Returns (dq, dk, dv)."""
+    q, k, v, dout = (np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v, dout))
+    B, N, H, Hkv, d = _shape(q, k, v)
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    left, right = _window(window)
+    dq = np.empty_like(q)
+    dk = np.empty_like(k)
+    dv = np.empty_like(v)
+    rc = _lib().oracle_attn_bwd_f64(_dptr(q), _dptr(k), _dptr(v), _dptr(dout), _dptr(dq), _dptr(dk), _dptr(dv),
+                                    B, H, Hkv, N, d, int(bool(causal)), left, right, float(scale))
+    if rc:
+        raise ValueError(f"oracle_attn_bwd_f64 failed ({rc})")
+    return dq, dk, dv

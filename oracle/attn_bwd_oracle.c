@@ -1,0 +1,108 @@
+/*
+ * attn_bwd_oracle.c -- plain, slow, fp64 CPU oracle for the gradient of the exact
+ * attention forward pass.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg may load or call this file. The product path (the HIP library)
+ * never links, imports or falls back to it, and this file shares no code, header,
+ * table or helper with that library.
+ *
+ * What it computes. The pages report training speed-ups (abstract of "FlashAttention-2:
+ * Faster Attention with Better Parallelism and Work Partitioning"; abstract of
+ * "FlashAttention: Fast and Memory-Efficient Exact Attention with IO-Awareness"), so a
+ * backward pass exists, but they print no algorithm for it. This oracle is therefore the
+ * analytic gradient of the forward definition (S = scale Q K^T with the mask,
+ * P = softmax(S) row by row, O = P V), for a loss L whose gradient with respect to O is
+ * dO, taking no gradient through lse:
+ *     dV_j  = sum_i P_ij dO_i
+ *     dP_ij = <dO_i, v_j>,   D_i = sum_j P_ij dP_ij  (= <dO_i, O_i>)
+ *     dS_ij = P_ij (dP_ij - D_i)
+ *     dQ_i  = scale sum_j dS_ij k_j
+ *     dK_j  = scale sum_i dS_ij q_i
+ * With grouped-query attention, dK and dV of a key/value head sum over the query heads
+ * h with h / (H / Hkv) equal to it. Masking and key windows as in attn_oracle.c: masked
+ * pairs have P_ij = 0 and contribute nothing.
+ *
+ * Layouts: q, o, dout, dq [B][N][H][d]; k, v, dk, dv [B][N][Hkv][d].
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+static void visible_keys(int i, int N, int causal, int left, int right, int* jlo, int* jhi) {
+  int lo = 0, hi = causal ? i : N - 1;
+  if (left >= 0 && i - left > lo) lo = i - left;
+  if (right >= 0 && i + right < hi) hi = i + right;
+  *jlo = lo;
+  *jhi = hi;
+}
+
+/* Returns 0, 1 on bad arguments, 2 if scratch allocation failed. dq, dk, dv are
+ * overwritten. Serial over (b, kv head), so that dK and dV sum in a fixed order. */
+int oracle_attn_bwd_f64(const double* q, const double* k, const double* v, const double* dout,
+                        double* dq, double* dk, double* dv, int B, int H, int Hkv, int N, int d,
+                        int causal, int left, int right, double scale) {
+  if (B < 1 || H < 1 || Hkv < 1 || N < 1 || d < 1 || Hkv > H || H % Hkv) return 1;
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return 1;
+  const int group = H / Hkv;
+  double* p = (double*)malloc(sizeof(double) * (size_t)N);
+  double* dp = (double*)malloc(sizeof(double) * (size_t)N);
+  if (!p || !dp) {
+    free(p);
+    free(dp);
+    return 2;
+  }
+  memset(dk, 0, sizeof(double) * (size_t)B * N * Hkv * d);
+  memset(dv, 0, sizeof(double) * (size_t)B * N * Hkv * d);
+  for (int b = 0; b < B; ++b)
+    for (int h = 0; h < H; ++h) {
+      const int hk = h / group;
+      for (int i = 0; i < N; ++i) {
+        const double* qi = q + (((size_t)b * N + i) * H + h) * d;
+        const double* gi = dout + (((size_t)b * N + i) * H + h) * d;
+        double* dqi = dq + (((size_t)b * N + i) * H + h) * d;
+        int jlo, jhi;
+        visible_keys(i, N, causal, left, right, &jlo, &jhi);
+        /* P row: scores, max, exponentials, normalisation */
+        double m = -INFINITY;
+        for (int j = jlo; j <= jhi; ++j) {
+          const double* kj = k + (((size_t)b * N + j) * Hkv + hk) * d;
+          double s = 0.0;
+          for (int t = 0; t < d; ++t) s += qi[t] * kj[t];
+          p[j] = scale * s;
+          if (p[j] > m) m = p[j];
+        }
+        double l = 0.0;
+        for (int j = jlo; j <= jhi; ++j) {
+          p[j] = exp(p[j] - m);
+          l += p[j];
+        }
+        for (int j = jlo; j <= jhi; ++j) p[j] /= l;
+        /* dP_ij = <dO_i, v_j> and D_i = sum_j P_ij dP_ij */
+        double D = 0.0;
+        for (int j = jlo; j <= jhi; ++j) {
+          const double* vj = v + (((size_t)b * N + j) * Hkv + hk) * d;
+          double s = 0.0;
+          for (int t = 0; t < d; ++t) s += gi[t] * vj[t];
+          dp[j] = s;
+          D += p[j] * s;
+        }
+        for (int t = 0; t < d; ++t) dqi[t] = 0.0;
+        for (int j = jlo; j <= jhi; ++j) {
+          const double ds = p[j] * (dp[j] - D);
+          const double* kj = k + (((size_t)b * N + j) * Hkv + hk) * d;
+          double* dkj = dk + (((size_t)b * N + j) * Hkv + hk) * d;
+          double* dvj = dv + (((size_t)b * N + j) * Hkv + hk) * d;
+          for (int t = 0; t < d; ++t) {
+            dqi[t] += scale * ds * kj[t];
+            dkj[t] += scale * ds * qi[t];
+            dvj[t] += p[j] * gi[t];
+          }
+        }
+      }
+    }
+  free(p);
+  free(dp);
+  return 0;
+}

@@ -543,8 +543,87 @@ def pin_rotation_identity():
             _close(lse2, lse, 1e-12, f"rotated attention lse (d={d})")
 
 
+# Gradients. The pages report training throughput but print no backward algorithm; the
+# oracle's gradient is the analytic derivative of the forward definition for an upstream
+# dO (no gradient through lse).
+def _loss(q, k, v, g, causal, scale, window=None):
+    """L = sum(O * g) with O from a direct numpy evaluation of the definition (masked
+    softmax of the scaled scores times V), independent of the oracle's code."""
+    B, N, H, d = q.shape
+    kr = np.repeat(k, H // k.shape[2], axis=2)
+    vr = np.repeat(v, H // v.shape[2], axis=2)
+    s = np.einsum("bihd,bjhd->bhij", q, kr) * scale
+    keep = _window_mask(N, causal, *(window if window is not None else (-1, -1)))
+    s = np.where(keep, s, -np.inf)
+    p = np.exp(s - s.max(axis=-1, keepdims=True))
+    p /= p.sum(axis=-1, keepdims=True)
+    return float(np.sum(np.einsum("bhij,bjhd->bihd", p, vr) * g))
+
+
+# P22 -- central finite differences of L = sum(O * dO) in every coordinate of tiny inputs.
+def pin_bwd_finite_differences():
+    rng = np.random.default_rng(51)
+    for causal, window in ((False, None), (True, None), (False, (1, 2))):
+        B, N, H, Hkv, d = 1, 5, 2, 1, 3
+        q, k, v = _qkv(rng, B, N, H, Hkv, d)
+        g = rng.standard_normal(q.shape)
+        dq, dk, dv = oracle.attn_bwd_f64(q, k, v, g, causal, 0.7, window)
+        h = 1e-6
+        for x, dx, name in ((q, dq, "dq"), (k, dk, "dk"), (v, dv, "dv")):
+            fd = np.empty_like(x)
+            for idx in np.ndindex(x.shape):
+                old = x[idx]
+                x[idx] = old + h
+                lp = _loss(q, k, v, g, causal, 0.7, window)
+                x[idx] = old - h
+                lm = _loss(q, k, v, g, causal, 0.7, window)
+                x[idx] = old
+                fd[idx] = (lp - lm) / (2 * h)
+            assert np.max(np.abs(fd - dx)) <= 1e-7 * max(1.0, np.max(np.abs(dx))), \
+                f"{name} vs finite differences (causal={causal}, window={window})"
+
+
+# P23 -- torch float64 autograd of scaled_dot_product_attention (an independent library).
+def pin_bwd_torch_autograd():
+    rng = np.random.default_rng(52)
+    for B, H, Hkv, N, d, causal, window in ((1, 2, 2, 40, 16, False, None), (2, 4, 2, 37, 8, True, None),
+                                             (1, 4, 1, 50, 8, False, (6, 3)), (1, 2, 2, 45, 8, True, (10, -1))):
+        q, k, v = _qkv(rng, B, N, H, Hkv, d)
+        g = rng.standard_normal(q.shape)
+        dq, dk, dv = oracle.attn_bwd_f64(q, k, v, g, causal, 0.3, window)
+        t = lambda x: torch.from_numpy(x.copy()).permute(0, 2, 1, 3).requires_grad_(True)
+        tq, tk, tv = t(q), t(k), t(v)
+        if window is None:
+            o = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=0.3, enable_gqa=(H != Hkv))
+        else:
+            mask = torch.from_numpy(_window_mask(N, causal, *window))
+            o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=0.3, enable_gqa=(H != Hkv))
+        o.backward(torch.from_numpy(g).permute(0, 2, 1, 3))
+        for mine, ref, name in ((dq, tq.grad, "dq"), (dk, tk.grad, "dk"), (dv, tv.grad, "dv")):
+            _close(mine, ref.permute(0, 2, 1, 3).numpy(), 1e-11, f"{name} vs torch autograd (B{B} H{H}/{Hkv} N{N})")
+
+
+# P24 -- exact invariants: the dS rows sum to zero, so sum_j dK_j = 0; the P rows sum to
+# one, so sum_j dV_j = sum over the group's query heads of sum_i dO_i; a window of width
+# zero makes every P row one-hot, so dQ = dK = 0 and dV_j = sum over the group of dO_j.
+def pin_bwd_invariants():
+    rng = np.random.default_rng(53)
+    B, N, H, Hkv, d = 2, 30, 4, 2, 6
+    q, k, v = _qkv(rng, B, N, H, Hkv, d)
+    g = rng.standard_normal(q.shape)
+    gs = g.reshape(B, N, Hkv, H // Hkv, d).sum(axis=3)               # group sums of dO per position
+    for causal in (False, True):
+        dq, dk, dv = oracle.attn_bwd_f64(q, k, v, g, causal, 0.45)
+        assert np.max(np.abs(dk.sum(axis=1))) < 1e-12, "sum_j dK_j = 0"
+        _close(dv.sum(axis=1), gs.sum(axis=1), 1e-12, "sum_j dV_j = sum_i dO_i")
+    dq, dk, dv = oracle.attn_bwd_f64(q, k, v, g, False, 0.45, (0, 0))
+    assert np.max(np.abs(dq)) < 1e-15 and np.max(np.abs(dk)) < 1e-15, "one-hot P: dQ = dK = 0"
+    _close(dv, gs, 1e-14, "one-hot P: dV_j = group sum of dO_j")
+
+
 ALL_PINS = [pin_mpmath_bruteforce, pin_torch_sdpa, pin_zero_query, pin_single_key, pin_two_keys,
             pin_affine_in_v, pin_probability_rows, pin_key_permutation, pin_key_shift, pin_gqa_repeat,
             pin_causal_prefix, pin_split_merge, pin_hardmax_and_range, pin_decoders, pin_golden_fixtures,
             pin_window_bruteforce_and_sdpa, pin_window_closed_forms, pin_window_reductions,
-            pin_e4m3_encode, pin_fwht, pin_block_quantize, pin_rotation_identity]
+            pin_e4m3_encode, pin_fwht, pin_block_quantize, pin_rotation_identity,
+            pin_bwd_finite_differences, pin_bwd_torch_autograd, pin_bwd_invariants]

@@ -15,6 +15,7 @@ from tests import pins
 ORACLE_DIR = os.path.dirname(oracle.__file__)
 SRC = os.path.join(ORACLE_DIR, "attn_oracle.c")
 QSRC = os.path.join(ORACLE_DIR, "fp8_quant_oracle.c")
+BSRC = os.path.join(ORACLE_DIR, "attn_bwd_oracle.c")
 
 MUTANTS = {
     "gqa_map_modulo": ("h / group", "h % Hkv"),
@@ -67,14 +68,30 @@ QMUTANTS = {
 }
 
 
-ALL = {**{n: (SRC,) + m for n, m in MUTANTS.items()}, **{n: (QSRC,) + m for n, m in QMUTANTS.items()}}
+# mutants of the gradient oracle (attn_bwd_oracle.c)
+BMUTANTS = {
+    "bwd_D_without_p": ("D += p[j] * s;", "D += s;"),
+    "bwd_dS_sign": ("const double ds = p[j] * (dp[j] - D);", "const double ds = p[j] * (D - dp[j]);"),
+    "bwd_dK_unscaled": ("dkj[t] += scale * ds * qi[t];", "dkj[t] += ds * qi[t];"),
+    "bwd_dV_uses_dS": ("dvj[t] += p[j] * gi[t];", "dvj[t] += ds * gi[t];"),
+    "bwd_dQ_uses_q": ("dqi[t] += scale * ds * kj[t];", "dqi[t] += scale * ds * qi[t];"),
+    "bwd_gqa_modulo": ("const int hk = h / group;", "const int hk = h % Hkv;"),
+    "bwd_P_unnormalised": ("for (int j = jlo; j <= jhi; ++j) p[j] /= l;", ""),
+    "bwd_dP_uses_k": ("const double* vj = v + (((size_t)b * N + j) * Hkv + hk) * d;",
+                      "const double* vj = k + (((size_t)b * N + j) * Hkv + hk) * d;"),
+    "bwd_window_left_off_by_one": ("if (left >= 0 && i - left > lo) lo = i - left;",
+                                   "if (left >= 0 && i - left + 1 > lo) lo = i - left + 1;"),
+}
+
+ALL = {**{n: (SRC,) + m for n, m in MUTANTS.items()}, **{n: (QSRC,) + m for n, m in QMUTANTS.items()},
+       **{n: (BSRC,) + m for n, m in BMUTANTS.items()}}
 
 
 @pytest.mark.parametrize("name", sorted(ALL))
 def test_mutant_is_caught(name, tmp_path):
     target, pattern, repl = ALL[name]
     sources = []
-    for path in (SRC, QSRC):
+    for path in (SRC, QSRC, BSRC):
         src = open(path).read()
         if path == target:
             assert pattern in src, f"mutant {name}: pattern no longer in the oracle"
