@@ -70,6 +70,9 @@ def cpu_baseline(w: synth_inputs.Workload, inp: dict, budget_s: float = 12.0):
     dq, dk, dv = inp["descale"] if inp["descale"] else (1.0, 1.0, 1.0)
     signs = synth_inputs.random_signs(w.d, w.seed) if w.fp8_block else None
 
+    if w.backward:
+        dout = synth_inputs.make_dout(w.B, w.N, w.H, w.d, w.dtype, w.seed + 100)
+
     def prep(x, sg):
         if not w.fp8_block:
             return x
@@ -90,7 +93,11 @@ def cpu_baseline(w: synth_inputs.Workload, inp: dict, budget_s: float = 12.0):
             qs = prep(np.ascontiguousarray(q[:, :, hk * g:(hk + 1) * g]), signs)
             ks = prep(np.ascontiguousarray(k[:, :, hk:hk + 1]), signs)
             vs = prep(np.ascontiguousarray(v[:, :, hk:hk + 1]), None)
-            oracle.attn_fwd_f64(qs, ks, vs, w.causal, w.scale / (w.d if w.fp8_block else 1), w.window)
+            if w.backward:
+                ds = oracle.decode(dout[b:b + 1, :, hk * g:(hk + 1) * g], w.dtype)
+                oracle.attn_bwd_f64(qs, ks, vs, ds, w.causal, w.scale)
+            else:
+                oracle.attn_fwd_f64(qs, ks, vs, w.causal, w.scale / (w.d if w.fp8_block else 1), w.window)
             elapsed += time.perf_counter() - t0
             heads += g
     flops = per_head * heads
@@ -158,6 +165,18 @@ def main():
 
         def step(o=None, lse=None):
             return fa.fwd_fp8_block(qc, kc, vc, qs, ks, vs, causal=w.causal, scale=w.scale / w.d, out=o, lse=lse)
+    elif w.backward:
+        # the gradient pass: the forward's o and lse are computed once, outside the timed
+        # region; a step is one fa_bwd call (three launches)
+        fo, flse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
+        dout = to_dev(synth_inputs.make_dout(w.B, w.N, w.H, w.d, w.dtype, w.seed + 100), w.dtype)
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        ws = torch.empty(fa.fa_bwd_workspace_bytes(w.B, w.H, w.N) // 4, dtype=torch.float32, device="cuda")
+
+        def step(o=None, lse=None):
+            fa.bwd(q, k, v, fo, flse, dout, causal=w.causal, scale=w.scale, dq=grads[0], dk=grads[1], dv=grads[2],
+                   workspace=ws)
+            return grads[0], flse
     else:
         def step(o=None, lse=None):
             return fa.fwd(q, k, v, causal=w.causal, scale=w.scale, descale=inp["descale"], dtype=dt, out=o,
@@ -198,6 +217,7 @@ def main():
         "dtype": cdt,
         "data": "synthetic (seeded N(0,1) inputs)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
+                   **({"pass": "backward (dq, dk, dv; FLOP = 2.5x forward)"} if w.backward else {}),
                    "causal": w.causal, "scale": w.scale, "flop_per_step": w.flops,
                    **({"window": list(w.window)} if w.window else {}),
                    **({"fp8": "block scales (64 rows, E8M0), Hadamard-rotated q/k"} if w.fp8_block else {})},

@@ -1,0 +1,589 @@
+// fa_bwd.hip -- gradient of the exact attention forward for gfx950 (MI355X), and its C ABI.
+//
+// The pages report training speed-ups for the tiled method (abstracts of "FlashAttention:
+// Fast and Memory-Efficient Exact Attention with IO-Awareness" and "FlashAttention-2:
+// Faster Attention with Better Parallelism and Work Partitioning") but print no backward
+// algorithm. This is the analytic gradient of the forward definition for an upstream dO,
+// with no gradient through lse, computed the same I/O-aware way as the forward: the
+// probabilities are recomputed tile by tile from Q, K and the saved lse, so no N x N
+// matrix reaches HBM.
+//     D_i   = <dO_i, O_i>                                   (preprocess kernel)
+//     P_ij  = exp(scale <q_i, k_j> - lse_i)                 (masked pairs: 0)
+//     dV_j  = sum_i P_ij dO_i,   dS_ij = P_ij (<dO_i, v_j> - D_i)
+//     dK_j  = scale sum_i dS_ij q_i,   dQ_i = scale sum_j dS_ij k_j
+// With grouped-query attention dK and dV of a key/value head sum over its query heads.
+//
+// gfx950 mapping (64-lane wavefronts, v_mfma_f32_32x32x16_{bf16,f16}):
+//   * dK/dV kernel: one workgroup of 4 wavefronts per (batch, K/V head, 128 keys), each
+//     wavefront owning 32 keys, whose K and V rows stay in VGPRs as MFMA B operands. It
+//     walks every query tile (64 rows) of every query head of the group: S = Q K^T and
+//     dP = dO V^T come out with one key per lane (MFMA columns), so P and dS are
+//     lane-local elementwise work, and they leave the accumulator already in the B-operand
+//     layout of dV^T += dO^T P and dK^T += Q^T dS (queries consumed in a permuted order
+//     that the transposed Q^T / dO^T tiles in LDS are written in). dK and dV accumulate
+//     in registers over all query tiles: no atomics, deterministic.
+//   * dQ kernel: one workgroup of 4 wavefronts per (batch, head, 128 queries), the
+//     forward's orientation: S^T = K Q^T and dP^T = V dO^T with one query per lane, then
+//     dQ^T += K^T dS^T with K^T staged transposed in LDS.
+//   * Tiles are double-buffered in LDS; the next tile's global loads are in flight while
+//     the current one is computed. Row-major tiles use a 16-byte-chunk XOR swizzle, the
+//     transposed tiles a chunk swizzle by the low bits of the dim.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa.h"
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;          // 4 wavefronts
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct Bf16 {
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ unsigned pack2(float x, float y) {
+    bf16x2 r = {(__bf16)x, (__bf16)y};
+    return __builtin_bit_cast(unsigned, r);
+  }
+  static __device__ __forceinline__ float lo(unsigned w) { return __uint_as_float(w << 16); }
+  static __device__ __forceinline__ float hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+};
+struct F16 {
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ unsigned pack2(float x, float y) {
+    f16x2 r = {(_Float16)x, (_Float16)y};
+    return __builtin_bit_cast(unsigned, r);
+  }
+  static __device__ __forceinline__ float lo(unsigned w) { return (float)__builtin_bit_cast(_Float16, (unsigned short)(w & 0xffffu)); }
+  static __device__ __forceinline__ float hi(unsigned w) { return (float)__builtin_bit_cast(_Float16, (unsigned short)(w >> 16)); }
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  float* delta;          // workspace: D = rowsum(dO * O), [B][H][N]
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, H, Hkv, N, group;
+  float c;               // scale * log2(e)
+  float scale;
+  int tiles;             // workgroup tiles along the sequence for this kernel
+  int total;             // workgroups in the grid
+};
+
+// Workgroup L runs on XCD L % 8; give each XCD one contiguous range of the logical list
+// so that workgroups sharing inputs share an L2.
+__device__ __forceinline__ int logical_index(int L, int total) {
+  const int xcd = L & 7, slot = L >> 3;
+  const int per = total >> 3, rem = total & 7;
+  return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
+template <typename T>
+__device__ __forceinline__ T lds_read(const unsigned char* base, int byte) {
+  return *(const T*)(base + byte);
+}
+
+// LDS layouts of an R-row x D tile of 16-bit elements:
+//   row-major: 16-byte chunk c of row r at r*2D + ((c ^ (r & 7)) * 16);
+//   transposed: element (row x, dim t) at t*2R + chunk swizzle, with rows in slot order
+//     slot(x) = 16(x/16) + 8((x%8)/4) + 4((x%16)/8) + x%4, the order in which an MFMA
+//     accumulator (rows 8(i/4) + 4(l/32) + i%4 of lane l) hands its rows to the next
+//     MFMA's k index (8(l/32) + i).
+template <int D>
+__device__ __forceinline__ int rm_byte(int r, int chunk) {
+  return r * (2 * D) + ((chunk ^ (r & 7)) << 4);
+}
+template <int R>
+__device__ __forceinline__ int tr_byte(int dim, int slot) {
+  constexpr int kChunks = R / 8;
+  return dim * (2 * R) + ((((slot >> 3) ^ (dim & 7)) & (kChunks - 1)) << 4) + ((slot & 7) << 1);
+}
+__device__ __forceinline__ int slot_of(int x) {
+  return (x & ~15) + (((x & 7) >> 2) << 3) + (((x & 15) >> 3) << 2) + (x & 3);
+}
+
+// Stage loaded rows (4 consecutive rows x 8 dims per unit) into LDS, row-major and/or
+// transposed. rows[j] holds dims 8c..8c+7 of row 4g + j.
+template <int D, int R, bool ROWMAJOR, bool TRANSPOSED>
+__device__ __forceinline__ void stage_rows(unsigned char* rm, unsigned char* tr, int g, int c, const u32x4 (&rows)[4]) {
+  if constexpr (ROWMAJOR) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *(u32x4*)(rm + rm_byte<D>(4 * g + j, c)) = rows[j];
+  }
+  if constexpr (TRANSPOSED) {
+    const int s0 = slot_of(4 * g);                        // rows 4g..4g+3 take slots s0..s0+3
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      u32x2 w;
+      w[0] = __builtin_amdgcn_perm(rows[1][e >> 1], rows[0][e >> 1], sel);
+      w[1] = __builtin_amdgcn_perm(rows[3][e >> 1], rows[2][e >> 1], sel);
+      *(u32x2*)(tr + tr_byte<R>(8 * c + e, s0)) = w;
+    }
+  }
+}
+
+// ---- preprocess: D_i = <dO_i, O_i> in float32 ----------------------------------------
+template <typename Ops, int D>
+__global__ __launch_bounds__(kThreads) void bwd_delta_kernel(BwdArgs a) {
+  constexpr int kLanes = D / 8;                    // lanes per row, 8 elements each
+  const int row = blockIdx.x * (kThreads / kLanes) + threadIdx.x / kLanes;   // (b, i, h) flattened
+  const int c = threadIdx.x % kLanes;
+  const int rows = a.B * a.N * a.H;
+  float s = 0.0f;
+  if (row < rows) {
+    const u32x4 x = *(const u32x4*)((const uint16_t*)a.o + (size_t)row * D + c * 8);
+    const u32x4 y = *(const u32x4*)((const uint16_t*)a.dout + (size_t)row * D + c * 8);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) s += Ops::lo(x[w]) * Ops::lo(y[w]) + Ops::hi(x[w]) * Ops::hi(y[w]);
+  }
+#pragma unroll
+  for (int m = 1; m < kLanes; m <<= 1) s += __shfl_xor(s, m, 64);
+  if (row < rows && c == 0) {
+    const int h = row % a.H, i = (row / a.H) % a.N, b = row / (a.H * a.N);
+    a.delta[((size_t)b * a.H + h) * a.N + i] = s;
+  }
+}
+
+// ---- dK / dV -------------------------------------------------------------------------
+template <typename Ops, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int kBk = 128;                 // keys per workgroup, 32 per wavefront
+  constexpr int kBq = 64;                  // queries per tile
+  constexpr int kKsteps = D / 16;
+  constexpr int kDblocks = D / 32;
+  constexpr int kTile = kBq * D * 2;       // one 16-bit tile
+  constexpr int kBuf = 4 * kTile + 2 * kBq * 4;   // Q, dO (row-major), Q^T, dO^T, lse2, D
+  constexpr int kChunks = D / 8;
+  constexpr int kUnits = (kBq / 4) * kChunks;      // staging units of 4 rows x 8 dims
+  static_assert(kUnits % 64 == 0 && kUnits <= kThreads, "staging units fill whole wavefronts");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kBuf];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int lg = logical_index(blockIdx.x, a.total);
+  const int kt = lg % a.tiles;
+  const int bh = lg / a.tiles;               // b * Hkv + hk
+  const int hk = bh % a.Hkv, b = bh / a.Hkv;
+  const int N = a.N;
+  const int k0 = kt * kBk;
+  const int kw0 = k0 + 32 * wave;            // this wavefront's first key
+  const int key = kw0 + l32;                 // this lane's key (MFMA column)
+  const size_t q_stride = (size_t)a.H * D, kv_stride = (size_t)a.Hkv * D;
+
+  // K and V rows of the lane's key as B operands: dims 16ks + 8hi .. +7
+  u32x4 kreg[kKsteps], vreg[kKsteps];
+  {
+    const int kr = min(key, N - 1);
+    const uint16_t* kp = (const uint16_t*)a.k + ((size_t)b * N + kr) * kv_stride + (size_t)hk * D + hi * 8;
+    const uint16_t* vp = (const uint16_t*)a.v + ((size_t)b * N + kr) * kv_stride + (size_t)hk * D + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < kKsteps; ++ks) {
+      kreg[ks] = *(const u32x4*)(kp + ks * 16);
+      vreg[ks] = *(const u32x4*)(vp + ks * 16);
+    }
+  }
+  f32x16 dkT[kDblocks], dvT[kDblocks];       // C[dim][key]
+#pragma unroll
+  for (int i = 0; i < kDblocks; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dkT[i][e] = dvT[i][e] = 0.0f;
+
+  // query tiles: every head of the group, and under the causal mask only tiles that
+  // reach this workgroup's first key
+  const int qt0 = CAUSAL ? k0 / kBq : 0;
+  const int nqt = (N + kBq - 1) / kBq;
+  const int per_head = nqt - qt0;
+  const int T = per_head * a.group;
+
+  // staging: unit u = tid (< kUnits): rows 4g..4g+3 of the tile, dims 8c..8c+7
+  const bool stager = tid < kUnits;
+  const int sg = tid / kChunks, sc = tid % kChunks;
+  u32x4 qrows[4], drows[4];
+  float lse_st = 0.0f, del_st = 0.0f;
+  auto tile_coords = [&](int t, int& h, int& q0) __attribute__((always_inline)) {
+    h = hk * a.group + t / per_head;
+    q0 = (qt0 + t % per_head) * kBq;
+  };
+  auto load_tile = [&](int t) __attribute__((always_inline)) {
+    int h, q0;
+    tile_coords(t, h, q0);
+    if (stager) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = min(q0 + 4 * sg + j, N - 1);
+        const size_t off = ((size_t)b * N + r) * q_stride + (size_t)h * D + sc * 8;
+        qrows[j] = *(const u32x4*)((const uint16_t*)a.q + off);
+        drows[j] = *(const u32x4*)((const uint16_t*)a.dout + off);
+      }
+    }
+    if (tid < kBq) {
+      const int r = q0 + tid;
+      const size_t off = ((size_t)b * a.H + h) * N + min(r, N - 1);
+      lse_st = r < N ? a.lse[off] * kLog2e : INFINITY;     // rows past the end: P = 0
+      del_st = r < N ? a.delta[off] : 0.0f;
+    }
+  };
+  auto store_tile = [&](int buf) __attribute__((always_inline)) {
+    unsigned char* base = lds + buf * kBuf;
+    if (stager) {
+      stage_rows<D, kBq, true, true>(base, base + 2 * kTile, sg, sc, qrows);
+      stage_rows<D, kBq, true, true>(base + kTile, base + 3 * kTile, sg, sc, drows);
+    }
+    if (tid < kBq) {
+      ((float*)(base + 4 * kTile))[tid] = lse_st;
+      ((float*)(base + 4 * kTile + kBq * 4))[tid] = del_st;
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < T; ++t) {
+    if (t + 1 < T) load_tile(t + 1);
+    int h, q0;
+    tile_coords(t, h, q0);
+    const unsigned char* base = lds + (t & 1) * kBuf;
+    const unsigned char* qrm = base;
+    const unsigned char* drm = base + kTile;
+    const unsigned char* qtr = base + 2 * kTile;
+    const unsigned char* dtr = base + 3 * kTile;
+    const float* lse2 = (const float*)(base + 4 * kTile);
+    const float* dlt = (const float*)(base + 4 * kTile + kBq * 4);
+#pragma unroll
+    for (int qb = 0; qb < kBq / 32; ++qb) {
+      const int qb0 = q0 + qb * 32;
+      // causal: no key of this wavefront is visible to any query of the block
+      if (CAUSAL && kw0 > qb0 + 31) continue;
+      f32x16 s, dp;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < kKsteps; ++ks) {
+        const int r = qb * 32 + l32;
+        const u32x4 qa = lds_read<u32x4>(qrm, rm_byte<D>(r, 2 * ks + hi));
+        const u32x4 da = lds_read<u32x4>(drm, rm_byte<D>(r, 2 * ks + hi));
+        s = Ops::mfma(qa, kreg[ks], s);
+        dp = Ops::mfma(da, vreg[ks], dp);
+      }
+      // P and dS, lane-local: accumulator e holds query row qb*32 + 8(e/4) + 4hi + e%4
+      float pv[16], dsv[16];
+      const bool need_mask = (CAUSAL && kw0 + 31 > qb0) || key >= N;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 l4 = *(const float4*)(lse2 + qb * 32 + 8 * g + 4 * hi);
+        const float4 d4 = *(const float4*)(dlt + qb * 32 + 8 * g + 4 * hi);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int e = 4 * g + j;
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], a.c, -lv[j]));
+          if (need_mask) {
+            const int qi = qb0 + 8 * g + 4 * hi + j;
+            if ((CAUSAL && key > qi) || key >= N) p = 0.0f;
+          }
+          pv[e] = p;
+          dsv[e] = p * (dp[e] - dv[j]);
+        }
+      }
+      // B operands for the two k-steps (16 queries each): registers 8t .. 8t+7
+      u32x4 pb[2], db[2];
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          pb[t2][w] = Ops::pack2(pv[8 * t2 + 2 * w], pv[8 * t2 + 2 * w + 1]);
+          db[t2][w] = Ops::pack2(dsv[8 * t2 + 2 * w], dsv[8 * t2 + 2 * w + 1]);
+        }
+      // dV^T += dO^T P, dK^T += Q^T dS: A operands from the transposed tiles, slots
+      // qb*32 + 16 t2 + 8 hi .. +7 of dim 32 db + l32
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+        for (int dbk = 0; dbk < kDblocks; ++dbk) {
+          const int dim = dbk * 32 + l32, slot = qb * 32 + t2 * 16 + hi * 8;
+          const u32x4 da = lds_read<u32x4>(dtr, tr_byte<kBq>(dim, slot));
+          const u32x4 qa = lds_read<u32x4>(qtr, tr_byte<kBq>(dim, slot));
+          dvT[dbk] = Ops::mfma(da, pb[t2], dvT[dbk]);
+          dkT[dbk] = Ops::mfma(qa, db[t2], dkT[dbk]);
+        }
+    }
+    if (t + 1 < T) store_tile((t + 1) & 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane holds dims 32db + 8g + 4hi + 0..3 of its key
+  if (key < N) {
+    const size_t off = ((size_t)b * N + key) * kv_stride + (size_t)hk * D;
+#pragma unroll
+    for (int dbk = 0; dbk < kDblocks; ++dbk)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dim = dbk * 32 + 8 * g + 4 * hi;
+        u32x2 wk, wv;
+        wk[0] = Ops::pack2(dkT[dbk][4 * g] * a.scale, dkT[dbk][4 * g + 1] * a.scale);
+        wk[1] = Ops::pack2(dkT[dbk][4 * g + 2] * a.scale, dkT[dbk][4 * g + 3] * a.scale);
+        wv[0] = Ops::pack2(dvT[dbk][4 * g], dvT[dbk][4 * g + 1]);
+        wv[1] = Ops::pack2(dvT[dbk][4 * g + 2], dvT[dbk][4 * g + 3]);
+        *(u32x2*)((uint16_t*)a.dk + off + dim) = wk;
+        *(u32x2*)((uint16_t*)a.dv + off + dim) = wv;
+      }
+  }
+}
+
+// ---- dQ ------------------------------------------------------------------------------
+template <typename Ops, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int kBq = 128;                 // queries per workgroup, 32 per wavefront
+  constexpr int kBk = 64;                  // keys per tile
+  constexpr int kKsteps = D / 16;
+  constexpr int kDblocks = D / 32;
+  constexpr int kTile = kBk * D * 2;
+  constexpr int kBuf = 3 * kTile;          // K, V (row-major), K^T
+  constexpr int kChunks = D / 8;
+  constexpr int kUnits = (kBk / 4) * kChunks;
+  static_assert(kUnits % 64 == 0 && kUnits <= kThreads, "staging units fill whole wavefronts");
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kBuf];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int lg = logical_index(blockIdx.x, a.total);
+  // logical order (b, hk, query tile, head in group): heads sharing K/V are neighbours
+  const int gm = lg % a.group;
+  int t_ = lg / a.group;
+  int qt = t_ % a.tiles;
+  t_ /= a.tiles;
+  const int hk = t_ % a.Hkv, b = t_ / a.Hkv;
+  if (CAUSAL) qt = a.tiles - 1 - qt;       // longest first
+  const int h = hk * a.group + gm;
+  const int N = a.N;
+  const int q0 = qt * kBq;
+  const int qw0 = q0 + 32 * wave;
+  const int qi = qw0 + l32;
+  const size_t q_stride = (size_t)a.H * D, kv_stride = (size_t)a.Hkv * D;
+
+  u32x4 qreg[kKsteps], dreg[kKsteps];
+  {
+    const int r = min(qi, N - 1);
+    const size_t off = ((size_t)b * N + r) * q_stride + (size_t)h * D + hi * 8;
+#pragma unroll
+    for (int ks = 0; ks < kKsteps; ++ks) {
+      qreg[ks] = *(const u32x4*)((const uint16_t*)a.q + off + ks * 16);
+      dreg[ks] = *(const u32x4*)((const uint16_t*)a.dout + off + ks * 16);
+    }
+  }
+  const size_t lrow = ((size_t)b * a.H + h) * N + min(qi, N - 1);
+  const float lse2 = qi < N ? a.lse[lrow] * kLog2e : INFINITY;
+  const float dlt = qi < N ? a.delta[lrow] : 0.0f;
+  f32x16 dqT[kDblocks];                      // C[dim][query]
+#pragma unroll
+  for (int i = 0; i < kDblocks; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dqT[i][e] = 0.0f;
+
+  const int kv_end = CAUSAL ? min(N, q0 + kBq) : N;
+  const int T = (kv_end + kBk - 1) / kBk;
+
+  const bool stager = tid < kUnits;
+  const int sg = tid / kChunks, sc = tid % kChunks;
+  u32x4 krows[4], vrows[4];
+  auto load_tile = [&](int t) __attribute__((always_inline)) {
+    if (stager) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = min(t * kBk + 4 * sg + j, N - 1);
+        const size_t off = ((size_t)b * N + r) * kv_stride + (size_t)hk * D + sc * 8;
+        krows[j] = *(const u32x4*)((const uint16_t*)a.k + off);
+        vrows[j] = *(const u32x4*)((const uint16_t*)a.v + off);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) __attribute__((always_inline)) {
+    unsigned char* base = lds + buf * kBuf;
+    if (stager) {
+      stage_rows<D, kBk, true, true>(base, base + 2 * kTile, sg, sc, krows);
+      stage_rows<D, kBk, true, false>(base + kTile, nullptr, sg, sc, vrows);
+    }
+  };
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < T; ++t) {
+    if (t + 1 < T) load_tile(t + 1);
+    const unsigned char* base = lds + (t & 1) * kBuf;
+    const unsigned char* krm = base;
+    const unsigned char* vrm = base + kTile;
+    const unsigned char* ktr = base + 2 * kTile;
+    const int j0 = t * kBk;
+    const bool active = !CAUSAL || j0 <= qw0 + 31;
+    if (active) {
+      u32x4 db[2][2];                        // dS^T as B operands: [key block][k-step]
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        f32x16 s, dp;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < kKsteps; ++ks) {
+          const int r = kb * 32 + l32;
+          const u32x4 ka = lds_read<u32x4>(krm, rm_byte<D>(r, 2 * ks + hi));
+          const u32x4 va = lds_read<u32x4>(vrm, rm_byte<D>(r, 2 * ks + hi));
+          s = Ops::mfma(ka, qreg[ks], s);
+          dp = Ops::mfma(va, dreg[ks], dp);
+        }
+        const bool need_mask = (j0 + kBk > N) || (CAUSAL && j0 + kBk - 1 > qw0);
+        float dsv[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], a.c, -lse2));
+          if (need_mask) {
+            const int kj = j0 + kb * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
+            if (kj >= N || (CAUSAL && kj > qi)) p = 0.0f;
+          }
+          dsv[e] = p * (dp[e] - dlt);
+        }
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) db[kb][t2][w] = Ops::pack2(dsv[8 * t2 + 2 * w], dsv[8 * t2 + 2 * w + 1]);
+      }
+      // dQ^T += K^T dS^T: A = K^T (dim 32 dbk + l32, slots kb*32 + 16 t2 + 8 hi .. +7)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+          for (int dbk = 0; dbk < kDblocks; ++dbk) {
+            const u32x4 ka = lds_read<u32x4>(ktr, tr_byte<kBk>(dbk * 32 + l32, kb * 32 + t2 * 16 + hi * 8));
+            dqT[dbk] = Ops::mfma(ka, db[kb][t2], dqT[dbk]);
+          }
+    }
+    if (t + 1 < T) store_tile((t + 1) & 1);
+    __syncthreads();
+  }
+
+  if (qi < N) {
+    const size_t off = ((size_t)b * N + qi) * q_stride + (size_t)h * D;
+#pragma unroll
+    for (int dbk = 0; dbk < kDblocks; ++dbk)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dim = dbk * 32 + 8 * g + 4 * hi;
+        u32x2 w;
+        w[0] = Ops::pack2(dqT[dbk][4 * g] * a.scale, dqT[dbk][4 * g + 1] * a.scale);
+        w[1] = Ops::pack2(dqT[dbk][4 * g + 2] * a.scale, dqT[dbk][4 * g + 3] * a.scale);
+        *(u32x2*)((uint16_t*)a.dq + off + dim) = w;
+      }
+  }
+}
+
+// ---- host ----------------------------------------------------------------------------
+bool aligned(const void* p, size_t n) { return ((uintptr_t)p % n) == 0; }
+
+template <typename Ops, int D, bool CAUSAL>
+fa_status launch_bwd(BwdArgs args, hipStream_t s) {
+  const int rows = args.B * args.N * args.H;
+  const int per_block = kThreads / (D / 8);
+  hipLaunchKernelGGL((bwd_delta_kernel<Ops, D>), dim3((rows + per_block - 1) / per_block), dim3(kThreads), 0, s, args);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+  BwdArgs kv = args;
+  kv.tiles = (args.N + 127) / 128;
+  kv.total = kv.tiles * args.Hkv * args.B;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<Ops, D, CAUSAL>), dim3(kv.total), dim3(kThreads), 0, s, kv);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
+  BwdArgs qa = args;
+  qa.tiles = (args.N + 127) / 128;
+  qa.total = qa.tiles * args.H * args.B;
+  hipLaunchKernelGGL((bwd_dq_kernel<Ops, D, CAUSAL>), dim3(qa.total), dim3(kThreads), 0, s, qa);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+template <typename Ops>
+fa_status dispatch_bwd(const BwdArgs& args, int d, int causal, hipStream_t s) {
+  if (d == 128) return causal ? launch_bwd<Ops, 128, true>(args, s) : launch_bwd<Ops, 128, false>(args, s);
+  return causal ? launch_bwd<Ops, 64, true>(args, s) : launch_bwd<Ops, 64, false>(args, s);
+}
+
+fa_status check_bwd(int B, int H, int Hkv, int N, int d, int causal, fa_dtype dtype) {
+  if (B < 1 || H < 1 || Hkv < 1 || N < 1 || d < 1) return FA_ERR_INVALID_ARG;
+  if (Hkv > H || H % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_BF16) {
+    return dtype == FA_DTYPE_FP8_E4M3 ? FA_ERR_UNSUPPORTED : FA_ERR_INVALID_ARG;
+  }
+  if ((long long)B * N * H * d >= (1LL << 31)) return FA_ERR_INVALID_ARG;
+  if ((long long)(N + 127) / 128 * H * B > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N) {
+  if (B < 1 || H < 1 || N < 1) return 0;
+  return (size_t)B * H * N * sizeof(float);
+}
+
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
+                 int causal, float scale, fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  fa_status st = check_bwd(B, H, Hkv, N, d, causal, dtype);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace) return FA_ERR_INVALID_ARG;
+  const void* p16[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* p : p16)
+    if (!aligned(p, 16)) return FA_ERR_INVALID_ARG;
+  if (!aligned(lse, 4) || !aligned(workspace, 4)) return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < fa_bwd_workspace_bytes(B, H, N)) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  BwdArgs args;
+  args.q = q;
+  args.k = k;
+  args.v = v;
+  args.o = o;
+  args.dout = dout;
+  args.lse = lse;
+  args.delta = (float*)workspace;
+  args.dq = dq;
+  args.dk = dk;
+  args.dv = dv;
+  args.B = B;
+  args.H = H;
+  args.Hkv = Hkv;
+  args.N = N;
+  args.group = H / Hkv;
+  args.c = (float)((double)scale * 1.4426950408889634);
+  args.scale = scale;
+  args.tiles = 0;
+  args.total = 0;
+  hipStream_t s = (hipStream_t)stream;
+  return dtype == FA_DTYPE_BF16 ? dispatch_bwd<Bf16>(args, d, causal, s) : dispatch_bwd<F16>(args, d, causal, s);
+}
+
+}  // extern "C"

@@ -47,6 +47,10 @@ def lib() -> ctypes.CDLL:
             L.fa_quantize_e4m3_block.restype = c_int
             L.fa_fwd_fp8_block.argtypes = [vp] * 8 + [c_int] * 6 + [c_float, vp]
             L.fa_fwd_fp8_block.restype = c_int
+            L.fa_bwd_workspace_bytes.argtypes = [c_int] * 3
+            L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
+            L.fa_bwd.argtypes = [vp] * 9 + [c_int] * 6 + [c_float, c_int, vp, ctypes.c_size_t, vp]
+            L.fa_bwd.restype = c_int
             L.fa_fwd_query.argtypes = [c_int] * 7 + [szp] * 5
             L.fa_fwd_query.restype = c_int
             L.fa_status_string.argtypes = [c_int]
@@ -102,6 +106,18 @@ def fa_fwd_fp8_block(q_ptr: int, k_ptr: int, v_ptr: int, qs_ptr: int, ks_ptr: in
     """Direct call of fa_fwd_fp8_block with raw pointers; returns the status code."""
     return int(lib().fa_fwd_fp8_block(q_ptr, k_ptr, v_ptr, qs_ptr, ks_ptr, vs_ptr, o_ptr, lse_ptr, B, H, Hkv,
                                       N, d, int(causal), float(scale), stream))
+
+
+def fa_bwd_workspace_bytes(B: int, H: int, N: int) -> int:
+    return int(lib().fa_bwd_workspace_bytes(B, H, N))
+
+
+def fa_bwd(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, do_ptr: int, lse_ptr: int, dq_ptr: int, dk_ptr: int,
+           dv_ptr: int, B: int, H: int, Hkv: int, N: int, d: int, causal: int, scale: float, dtype: int,
+           ws_ptr: int, ws_bytes: int, stream: int = 0) -> int:
+    """Direct call of fa_bwd with raw pointers; returns the status code."""
+    return int(lib().fa_bwd(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr, dk_ptr, dv_ptr, B, H, Hkv, N, d,
+                            int(causal), float(scale), int(dtype), ws_ptr, int(ws_bytes), stream))
 
 
 def fa_fwd_query(B: int, H: int, Hkv: int, N: int, d: int, causal: int, dtype: int) -> dict:
@@ -219,3 +235,37 @@ def fwd_fp8_block(q, k, v, q_scales, k_scales, v_scales, causal: bool = False, s
                             v_scales.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Hkv, N, d, int(bool(causal)),
                             scale, _stream(q, stream)))
     return out, lse
+
+
+def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None, dq=None, dk=None, dv=None,
+        workspace=None, stream=None):
+    """Gradient of the attention forward on device tensors: q, o, dout [B,N,H,d], k, v
+    [B,N,Hkv,d] (float16 or bfloat16), lse [B,H,N] float32 as returned by fwd. Returns
+    (dq, dk, dv). The D workspace (B*H*N float32) is allocated here unless given."""
+    import torch
+    code = _dtype_code(q, None)
+    B, N, H, d = q.shape
+    Hkv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    nbytes = fa_bwd_workspace_bytes(B, H, N)
+    if workspace is None:
+        workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device)
+    for t in (q, k, v, o, lse, dout, dq, dk, dv, workspace):
+        if not t.is_contiguous() or t.device != q.device:
+            raise ValueError("tensors must be contiguous and on the same device")
+    for t in (o, dout, dq):
+        if tuple(t.shape) != (B, N, H, d) or t.dtype != q.dtype:
+            raise ValueError("o, dout and dq must match q")
+    for t in (v, dk, dv):
+        if tuple(t.shape) != (B, N, Hkv, d) or t.dtype != q.dtype:
+            raise ValueError("k, v, dk and dv must be [B,N,Hkv,d] of q's type")
+    if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32:
+        raise ValueError("lse must be [B,H,N] float32")
+    _check(fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                  dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d, int(bool(causal)), scale, code,
+                  workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q, stream)))
+    return dq, dk, dv

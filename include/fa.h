@@ -143,6 +143,33 @@ fa_status fa_fwd_fp8_block(const void* q, const void* k, const void* v,
                            int Hkv, int N, int d, int causal, float scale, void* stream);
 
 /*
+ * Gradient of the attention forward (fa_fwd) for an upstream gradient dout of o. The
+ * pages report training speed-ups but print no backward algorithm; the library computes
+ * the analytic gradient of the forward definition, with no gradient through lse:
+ *     D_i = <dout_i, o_i>,  P_ij = exp(scale <q_i, k_j> - lse_i)  (0 where masked)
+ *     dv_j = sum_i P_ij dout_i,  dS_ij = P_ij (<dout_i, v_j> - D_i)
+ *     dk_j = scale sum_i dS_ij q_i,  dq_i = scale sum_j dS_ij k_j
+ * summing dk and dv over the query heads of each key/value head (grouped-query).
+ *   q, k, v     the forward's inputs; o and lse its outputs (lse as written by fa_fwd);
+ *   dout        [B][N][H][d], the gradient of o;
+ *   dq          [B][N][H][d]; dk, dv [B][N][Hkv][d]; outputs, fully overwritten;
+ *   q..dv       device pointers, 16-byte aligned, of dtype F16 or BF16 (FP8_E4M3 is
+ *               FA_ERR_UNSUPPORTED); lse 4-byte aligned float32;
+ *   workspace   device scratch of at least fa_bwd_workspace_bytes(B, H, N) bytes, 4-byte
+ *               aligned, owned by the caller; it holds D between the launches of one call
+ *               (calls that share a workspace must not overlap);
+ *   causal      0 or 1 (key windows are not supported here); scale as for fa_fwd.
+ * Enqueues three kernels on `stream` (D, then dk/dv, then dq) and returns. Accumulation
+ * is float32; dq, dk, dv are rounded once. Deterministic (no atomics). Errors as for
+ * fa_fwd; every check happens on the host before any launch.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N);
+fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                 const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N,
+                 int d, int causal, float scale, fa_dtype dtype, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/*
  * Shape query: byte sizes of every buffer fa_fwd reads or writes for these arguments,
  * after the same size checks fa_fwd makes. Any output pointer may be NULL.
  * workspace_bytes is always 0 (no scratch memory). Pure host function.

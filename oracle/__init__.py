@@ -82,6 +82,9 @@ def load(path: str):
     lib.oracle_block_quantize_e4m3.restype = ctypes.c_int
     lib.oracle_attn_bwd_f64.argtypes = [dp] * 7 + [ctypes.c_int] * 8 + [ctypes.c_double]
     lib.oracle_attn_bwd_f64.restype = ctypes.c_int
+    lib.oracle_attn_bwd_dq_rows_f64.argtypes = [dp] * 4 + [ctypes.c_int] * 6 + [ctypes.c_double, ctypes.c_int64,
+                                                                                i64p, dp]
+    lib.oracle_attn_bwd_dq_rows_f64.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -301,3 +304,18 @@ def attn_bwd_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, 
     if rc:
         raise ValueError(f"oracle_attn_bwd_f64 failed ({rc})")
     return dq, dk, dv
+
+
+def attn_bwd_dq_rows_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, causal: bool,
+                         scale: float, rows: np.ndarray) -> np.ndarray:
+    """dQ of the selected rows (b, h, i) only, [R, d] (same definition as attn_bwd_f64)."""
+    q, k, v, dout = (np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v, dout))
+    B, N, H, Hkv, d = _shape(q, k, v)
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+    out = np.empty((rows.shape[0], d), dtype=np.float64)
+    rc = _lib().oracle_attn_bwd_dq_rows_f64(_dptr(q), _dptr(k), _dptr(v), _dptr(dout), B, H, Hkv, N, d,
+                                            int(bool(causal)), float(scale), rows.shape[0],
+                                            rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _dptr(out))
+    if rc:
+        raise ValueError(f"oracle_attn_bwd_dq_rows_f64 failed ({rc})")
+    return out

@@ -29,6 +29,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 static void visible_keys(int i, int N, int causal, int left, int right, int* jlo, int* jhi) {
   int lo = 0, hi = causal ? i : N - 1;
@@ -105,4 +108,68 @@ int oracle_attn_bwd_f64(const double* q, const double* k, const double* v, const
   free(p);
   free(dp);
   return 0;
+}
+
+/* dQ of selected query rows only (rows[3r..3r+2] = (b, h, i)), for checking large problems:
+ * row i of dQ needs only row i of P and dP. dq_rows is [nrows][d]. */
+int oracle_attn_bwd_dq_rows_f64(const double* q, const double* k, const double* v,
+                                const double* dout, int B, int H, int Hkv, int N, int d,
+                                int causal, double scale, int64_t nrows, const int64_t* rows,
+                                double* dq_rows) {
+  if (B < 1 || H < 1 || Hkv < 1 || N < 1 || d < 1 || Hkv > H || H % Hkv) return 1;
+  if (!q || !k || !v || !dout || !rows || !dq_rows) return 1;
+  for (int64_t r = 0; r < nrows; ++r)
+    if (rows[3 * r] < 0 || rows[3 * r] >= B || rows[3 * r + 1] < 0 || rows[3 * r + 1] >= H ||
+        rows[3 * r + 2] < 0 || rows[3 * r + 2] >= N)
+      return 1;
+  const int group = H / Hkv;
+  int failed = 0;
+#pragma omp parallel reduction(| : failed)
+  {
+    double* p = (double*)malloc(sizeof(double) * (size_t)N);
+    double* dp = (double*)malloc(sizeof(double) * (size_t)N);
+    if (!p || !dp) failed = 1;
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+      if (!p || !dp) continue;
+      const int b = (int)rows[3 * r], h = (int)rows[3 * r + 1], i = (int)rows[3 * r + 2];
+      const int hk = h / group;
+      const double* qi = q + (((size_t)b * N + i) * H + h) * d;
+      const double* gi = dout + (((size_t)b * N + i) * H + h) * d;
+      double* dqi = dq_rows + (size_t)r * d;
+      int jlo, jhi;
+      visible_keys(i, N, causal, -1, -1, &jlo, &jhi);
+      double m = -INFINITY;
+      for (int j = jlo; j <= jhi; ++j) {
+        const double* kj = k + (((size_t)b * N + j) * Hkv + hk) * d;
+        double s = 0.0;
+        for (int t = 0; t < d; ++t) s += qi[t] * kj[t];
+        p[j] = scale * s;
+        if (p[j] > m) m = p[j];
+      }
+      double l = 0.0;
+      for (int j = jlo; j <= jhi; ++j) {
+        p[j] = exp(p[j] - m);
+        l += p[j];
+      }
+      for (int j = jlo; j <= jhi; ++j) p[j] /= l;
+      double D = 0.0;
+      for (int j = jlo; j <= jhi; ++j) {
+        const double* vj = v + (((size_t)b * N + j) * Hkv + hk) * d;
+        double s = 0.0;
+        for (int t = 0; t < d; ++t) s += gi[t] * vj[t];
+        dp[j] = s;
+        D += p[j] * s;
+      }
+      for (int t = 0; t < d; ++t) dqi[t] = 0.0;
+      for (int j = jlo; j <= jhi; ++j) {
+        const double ds = p[j] * (dp[j] - D);
+        const double* kj = k + (((size_t)b * N + j) * Hkv + hk) * d;
+        for (int t = 0; t < d; ++t) dqi[t] += scale * ds * kj[t];
+      }
+    }
+    free(p);
+    free(dp);
+  }
+  return failed ? 2 : 0;
 }

@@ -40,11 +40,15 @@ class Workload:
     outlier_mult: float = 20.0
     window: tuple | None = None     # (left, right) key window; negative side = unbounded
     fp8_block: bool = False         # e4m3 block-quantised on the GPU (drawn as bf16, rotated Q/K)
+    backward: bool = False          # the gradient pass (upstream dO drawn with seed + 100)
 
     @property
     def flops(self) -> float:
         """4*B*H*N^2*d, halved under the causal mask (query heads H). With a key window:
-        4*B*H*d times the number of (query, key) pairs inside the window."""
+        4*B*H*d times the number of (query, key) pairs inside the window. The gradient
+        pass counts 2.5 times its forward (five N x N x d products instead of two)."""
+        if self.backward:
+            return 2.5 * replace(self, backward=False).flops
         if self.window is None:
             f = 4.0 * self.B * self.H * self.N * self.N * self.d
             return f / 2 if self.causal else f
@@ -66,8 +70,9 @@ def _w(name, B, H, Hkv, N, d, causal, dtype, seed, **kw):
 
 # The five workloads: a tiny fp16 case, bf16 multi-head, bf16 causal long sequence,
 # bf16 causal grouped-query, and e4m3 with outliers; then a causal sliding-window case
-# (each query sees itself and the 4095 keys before it), and the e4m3 shape again drawn in
-# bf16 for block quantisation with the Hadamard rotation (signs from the same seed).
+# (each query sees itself and the 4095 keys before it), the e4m3 shape again drawn in
+# bf16 for block quantisation with the Hadamard rotation (signs from the same seed), and
+# the gradient pass on the multi-head and the causal grouped-query shapes (same inputs).
 WORKLOADS = {
     w.name: w for w in [
         _w("tiny_f16_b1_h2_n128_d64", 1, 2, 2, 128, 64, False, "f16", 1001),
@@ -80,6 +85,8 @@ WORKLOADS = {
            window=(4095, -1)),
         _w("fp8_block_hadamard_b8_h16_n4096_d128", 8, 16, 16, 4096, 128, False, "bf16", 1005,
            outlier_frac=1e-3, outlier_mult=20.0, fp8_block=True),
+        _w("bwd_bf16_b16_h16_n2048_d128", 16, 16, 16, 2048, 128, False, "bf16", 1002, backward=True),
+        _w("bwd_causal_gqa_bf16_b4_h32_kv8_n8192_d128", 4, 32, 8, 8192, 128, True, "bf16", 1004, backward=True),
     ]
 }
 
@@ -139,6 +146,13 @@ def make_inputs(B: int, H: int, Hkv: int, N: int, d: int, dtype: str, seed: int,
         for name in ("q", "k", "v"):
             out[name + "32"] = raw[name]
     return out
+
+
+def make_dout(B: int, N: int, H: int, d: int, dtype: str, seed: int) -> np.ndarray:
+    """An upstream gradient dO [B,N,H,d]: float32 N(0,1) from ``PCG64(seed)`` rounded to
+    `dtype` (bit patterns)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return _round_bits(rng.standard_normal(size=(B, N, H, d), dtype=np.float32), dtype)
 
 
 def random_signs(d: int, seed: int) -> np.ndarray:

@@ -101,3 +101,41 @@ def sample_rows(B: int, H: int, N: int, n_random: int, seed: int, br: int = 128)
     for _ in range(n_random):
         rows.append((int(rng.integers(B)), int(rng.integers(H)), int(rng.integers(N))))
     return np.array(rows, dtype=np.int64)
+
+
+UNIT_ROUNDOFF = {"bf16": 2.0 ** -8, "f16": 2.0 ** -11}
+
+
+def bwd_error_bound(q, k, v, dout, causal: bool, scale: float, dtype: str):
+    """Per-element bounds on |g_gpu - g_ref| for (dq, dk, dv), from the roundings the kernels
+    make with unit roundoff u of the storage type (fp64 inputs q, k, v, dout; small shapes):
+      * dS and P are rounded to the storage type as MFMA operands (relative u each);
+      * D_i = <dO_i, O_i> uses the forward's rounded O: |dD_i| <= u sum_t |dO_it O_it|,
+        which moves dS_ij by P_ij dD_i;
+      * dq, dk, dv are rounded once on output (u |g|).
+    So |d dq_i| <= scale (u sum_j |dS_ij| |k_j| + dD_i sum_j P_ij |k_j|) + u |dq_i|,
+       |d dk_j| <= scale (u sum_i |dS_ij| |q_i| + sum_i P_ij dD_i |q_i|) + u |dk_j|,
+       |d dv_j| <= u sum_i P_ij |dO_i| + u |dv_j|,
+    float32 accumulation adding far less. P and dS come from the oracle's probabilities."""
+    import oracle
+    B, N, H, d = q.shape
+    Hkv = k.shape[2]
+    g = H // Hkv
+    u = UNIT_ROUNDOFF[dtype]
+    o_ref, _ = oracle.attn_fwd_f64(q, k, v, causal, scale)
+    dq_r, dk_r, dv_r = oracle.attn_bwd_f64(q, k, v, dout, causal, scale)
+    bq = np.zeros_like(q)
+    bk = np.zeros_like(k)
+    bv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(H):
+            hk = h // g
+            P = oracle.attn_probs_f64(q, k, b, h, causal, scale)           # [N, N]
+            dO, Vh, Kh, Qh = dout[b, :, h], v[b, :, hk], k[b, :, hk], q[b, :, h]
+            D = np.sum(dO * o_ref[b, :, h], axis=1)
+            dS = P * (dO @ Vh.T - D[:, None])
+            dD = u * np.sum(np.abs(dO) * np.abs(o_ref[b, :, h]), axis=1)
+            bq[b, :, h] = scale * (u * np.abs(dS) @ np.abs(Kh) + (dD[:, None] * (P @ np.abs(Kh))))
+            bk[b, :, hk] += scale * (u * np.abs(dS).T @ np.abs(Qh) + P.T @ (dD[:, None] * np.abs(Qh)))
+            bv[b, :, hk] += u * P.T @ np.abs(dO)
+    return (bq + u * np.abs(dq_r), bk + u * np.abs(dk_r), bv + u * np.abs(dv_r)), (dq_r, dk_r, dv_r)

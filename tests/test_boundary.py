@@ -158,6 +158,37 @@ def test_fwd_fp8_block_rejects_before_launch(over, status):
     assert st == status
 
 
+def test_bwd_workspace_bytes():
+    assert fa.fa_bwd_workspace_bytes(2, 8, 1000) == 2 * 8 * 1000 * 4
+    assert fa.fa_bwd_workspace_bytes(0, 8, 1000) == 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dout=0), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=0), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=0), fa.FA_ERR_INVALID_ARG),
+    (dict(dq=FAKE + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(o=FAKE + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=FAKE + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(ws_bytes=1 * 4 * 64 * 4 - 4), fa.FA_ERR_INVALID_ARG),        # one float short
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=3), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=fa.FA_DTYPE_FP8_E4M3), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=5), fa.FA_ERR_INVALID_ARG),
+    (dict(N=0), fa.FA_ERR_INVALID_ARG),
+])
+def test_bwd_rejects_before_launch(over, status):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, dout=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1, H=4, Hkv=2, N=64,
+             d=128, causal=0, scale=0.1, dtype=fa.FA_DTYPE_BF16, ws=FAKE, ws_bytes=1 * 4 * 64 * 4)
+    a.update(over)
+    st = fa.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["dout"], a["lse"], a["dq"], a["dk"], a["dv"], a["B"], a["H"],
+                   a["Hkv"], a["N"], a["d"], a["causal"], a["scale"], a["dtype"], a["ws"], a["ws_bytes"])
+    assert st == status
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "absent.so"))
     monkeypatch.setattr(binding, "_lib", None)

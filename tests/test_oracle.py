@@ -43,3 +43,15 @@ def test_oracle_rejects_bad_shapes():
     q = np.zeros((1, 4, 3, 8)); k = np.zeros((1, 4, 2, 8))
     with pytest.raises(ValueError):
         oracle.attn_fwd_f64(q, k, k, False, 1.0)   # H % Hkv != 0
+
+
+def test_bwd_dq_rows_match_full_gradient():
+    rng = np.random.default_rng(6)
+    for causal in (False, True):
+        B, N, H, Hkv, d = 2, 33, 4, 2, 8
+        q, k, v, g = (rng.standard_normal(s) for s in ((B, N, H, d), (B, N, Hkv, d), (B, N, Hkv, d), (B, N, H, d)))
+        dq, _, _ = oracle.attn_bwd_f64(q, k, v, g, causal, 0.4)
+        rows = np.array([[0, 0, 0], [1, 3, 32], [0, 2, 17], [1, 1, 5]])
+        dqr = oracle.attn_bwd_dq_rows_f64(q, k, v, g, causal, 0.4, rows)
+        for r, (b, h, i) in enumerate(rows):
+            assert np.allclose(dqr[r], dq[b, i, h], rtol=1e-13, atol=1e-15)
