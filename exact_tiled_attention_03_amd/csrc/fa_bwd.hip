@@ -357,6 +357,7 @@ template <typename Ops, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
   constexpr int kBq = 128;                 // queries per workgroup, 32 per wavefront
   constexpr int kBk = 64;                  // keys per tile
+  constexpr int kKb = kBk / 32;            // 32-key blocks per tile
   constexpr int kKsteps = D / 16;
   constexpr int kDblocks = D / 32;
   constexpr int kTile = kBk * D * 2;
@@ -440,9 +441,9 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
     const int j0 = t * kBk;
     const bool active = !CAUSAL || j0 <= qw0 + 31;
     if (active) {
-      u32x4 db[2][2];                        // dS^T as B operands: [key block][k-step]
+      u32x4 db[kKb][2];                      // dS^T as B operands: [key block][k-step]
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < kKb; ++kb) {
         f32x16 s, dp;
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.0f;
@@ -472,7 +473,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
       }
       // dQ^T += K^T dS^T: A = K^T (dim 32 dbk + l32, slots kb*32 + 16 t2 + 8 hi .. +7)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
         for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
