@@ -85,6 +85,8 @@ def load(path: str):
     lib.oracle_attn_bwd_dq_rows_f64.argtypes = [dp] * 4 + [ctypes.c_int] * 6 + [ctypes.c_double, ctypes.c_int64,
                                                                                 i64p, dp]
     lib.oracle_attn_bwd_dq_rows_f64.restype = ctypes.c_int
+    lib.oracle_attn_fwd_kv_f64.argtypes = [dp] * 5 + [ctypes.c_int] * 7 + [ctypes.c_double]
+    lib.oracle_attn_fwd_kv_f64.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -319,3 +321,21 @@ def attn_bwd_dq_rows_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.n
     if rc:
         raise ValueError(f"oracle_attn_bwd_dq_rows_f64 failed ({rc})")
     return out
+
+
+def attn_fwd_kv_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: float):
+    """Rectangular forward: q [B,Nq,H,d] are the last Nq positions of a sequence whose keys
+    k, v [B,Nk,Hkv,d] cover all Nk positions (decode); under the causal mask query i sees
+    keys j <= Nk - Nq + i. Returns (o [B,Nq,H,d], lse [B,H,Nq])."""
+    q, k, v = (np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v))
+    B, Nq, H, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k/v shape does not match q")
+    o = np.empty_like(q)
+    lse = np.empty((B, H, Nq), dtype=np.float64)
+    rc = _lib().oracle_attn_fwd_kv_f64(_dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(lse), B, H, Hkv, Nq, Nk, d,
+                                       int(bool(causal)), float(scale))
+    if rc:
+        raise ValueError(f"oracle_attn_fwd_kv_f64 failed ({rc})")
+    return o, lse

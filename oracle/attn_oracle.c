@@ -252,6 +252,35 @@ int oracle_attn_probs_f64(const double* q, const double* k, int B, int H, int Hk
   return oracle_attn_probs_local_f64(q, k, B, H, Hkv, N, d, causal, -1, -1, scale, b, h, p);
 }
 
+/* Rectangular forward: Nq queries against Nk keys (q, o [B][Nq][H][d]; k, v [B][Nk][Hkv][d];
+ * lse [B][H][Nq]). Query i sits at sequence position Nk - Nq + i, the queries being the last
+ * Nq positions of a sequence whose keys are all Nk positions (decode); under the causal mask
+ * it sees keys j <= Nk - Nq + i. Nq <= Nk. With Nq = Nk this is oracle_attn_fwd_f64. */
+int oracle_attn_fwd_kv_f64(const double* q, const double* k, const double* v, double* o, double* lse,
+                           int B, int H, int Hkv, int Nq, int Nk, int d, int causal, double scale) {
+  if (B < 1 || H < 1 || Hkv < 1 || Nq < 1 || Nk < Nq || d < 1 || Hkv > H || H % Hkv) return 1;
+  if (!q || !k || !v || !o || !lse) return 1;
+  const int64_t rows = (int64_t)B * H * Nq;
+  const int group = H / Hkv;
+  int failed = 0;
+#pragma omp parallel reduction(| : failed)
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)Nk);
+    if (!s) failed = 1;
+#pragma omp for schedule(dynamic, 16)
+    for (int64_t r = 0; r < rows; ++r) {
+      if (!s) continue;
+      const int i = (int)(r % Nq), h = (int)((r / Nq) % H), b = (int)(r / ((int64_t)Nq * H));
+      const size_t qo = (((size_t)b * Nq + i) * H + h) * d;
+      const int pos = Nk - Nq + i;                            /* the query's sequence position */
+      attn_row(q + qo, k, v, Hkv, Nk, d, 0, causal ? pos : Nk - 1, scale, b, h / group, s, o + qo,
+               lse + ((size_t)b * H + h) * Nq + i);
+    }
+    free(s);
+  }
+  return failed ? 2 : 0;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

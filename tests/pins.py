@@ -621,9 +621,34 @@ def pin_bwd_invariants():
     _close(dv, gs, 1e-14, "one-hot P: dV_j = group sum of dO_j")
 
 
+# Decode / split-KV. The pages name work-centric and split decode schedules (the Lean
+# Attention and Stream-K titles in the reference lists) without defining them; the reading:
+# Nq queries are the last Nq positions of a sequence of Nk keys.
+# P25 -- the rectangular forward equals the last Nq rows of the square forward over Nk
+# positions (causal and not), reduces to it at Nq = Nk, and matches torch's float64 SDPA
+# with an explicit bottom-right mask.
+def pin_decode_rectangular():
+    rng = np.random.default_rng(61)
+    for B, H, Hkv, Nq, Nk, d in ((1, 4, 2, 1, 50, 8), (2, 2, 1, 7, 40, 16), (1, 2, 2, 13, 13, 4)):
+        q_full, k, v = _qkv(rng, B, Nk, H, Hkv, d)
+        q = np.ascontiguousarray(q_full[:, Nk - Nq:])
+        for causal in (False, True):
+            o, lse = oracle.attn_fwd_kv_f64(q, k, v, causal, 0.35)
+            of, lf = oracle.attn_fwd_f64(q_full, k, v, causal, 0.35)
+            _close(o, of[:, Nk - Nq:], 1e-13, f"decode O = last rows of square (Nq{Nq} Nk{Nk} c{causal})")
+            _close(lse, lf[:, :, Nk - Nq:], 1e-13, "decode lse = last rows of square")
+            keep = np.ones((Nq, Nk), dtype=bool)
+            if causal:
+                keep = np.arange(Nk)[None, :] <= (Nk - Nq + np.arange(Nq))[:, None]
+            t = lambda x: torch.from_numpy(x).permute(0, 2, 1, 3)
+            ref = F.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=torch.from_numpy(keep), scale=0.35,
+                                                 enable_gqa=(H != Hkv)).permute(0, 2, 1, 3).numpy()
+            _close(o, ref, 1e-12, "decode vs sdpa with bottom-right mask")
+
+
 ALL_PINS = [pin_mpmath_bruteforce, pin_torch_sdpa, pin_zero_query, pin_single_key, pin_two_keys,
             pin_affine_in_v, pin_probability_rows, pin_key_permutation, pin_key_shift, pin_gqa_repeat,
             pin_causal_prefix, pin_split_merge, pin_hardmax_and_range, pin_decoders, pin_golden_fixtures,
             pin_window_bruteforce_and_sdpa, pin_window_closed_forms, pin_window_reductions,
             pin_e4m3_encode, pin_fwht, pin_block_quantize, pin_rotation_identity,
-            pin_bwd_finite_differences, pin_bwd_torch_autograd, pin_bwd_invariants]
+            pin_bwd_finite_differences, pin_bwd_torch_autograd, pin_bwd_invariants, pin_decode_rectangular]

@@ -48,6 +48,8 @@ MUTANTS = {
     "e4m3_subnormal_scale": ("mag = ldexp((double)f, -9);", "mag = ldexp((double)f, -10);"),
     "e4m3_ieee_style_top_exponent": ("if (e == 15 && f == 7) mag = NAN;", "if (e == 15) mag = NAN;"),
     "decode_ignores_descale": ("dst[i] = x * mult;", "dst[i] = x;"),
+    "kv_causal_top_left": ("const int pos = Nk - Nq + i;", "const int pos = i;"),
+    "kv_causal_one_short": ("const int pos = Nk - Nq + i;", "const int pos = Nk - Nq + i - 1;"),
 }
 
 # mutants of the block-quantisation oracle (fp8_quant_oracle.c)
