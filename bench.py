@@ -73,6 +73,18 @@ def cpu_baseline(w: synth_inputs.Workload, inp: dict, budget_s: float = 12.0):
     if w.backward:
         dout = synth_inputs.make_dout(w.B, w.N, w.H, w.d, w.dtype, w.seed + 100)
 
+    if w.decode_nq:
+        t0 = time.perf_counter()
+        bs = 0
+        while bs < w.B and time.perf_counter() - t0 < budget_s:
+            sl = lambda n: oracle.decode(np.ascontiguousarray(inp[n][bs:bs + 1]), w.dtype)
+            oracle.attn_fwd_kv_f64(sl("q"), sl("k"), sl("v"), w.causal, w.scale)
+            bs += 1
+        el = time.perf_counter() - t0
+        fl = w.flops * bs / w.B
+        return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+                "sample": f"first {bs} of {w.B} batches of {w.name} ({fl / 1e9:.2f} GFLOP, {el:.1f} s in fp64)"}
+
     def prep(x, sg):
         if not w.fp8_block:
             return x
@@ -165,6 +177,13 @@ def main():
 
         def step(o=None, lse=None):
             return fa.fwd_fp8_block(qc, kc, vc, qs, ks, vs, causal=w.causal, scale=w.scale / w.d, out=o, lse=lse)
+    elif w.decode_nq:
+        # split-KV decode: a step is one fa_fwd_splitkv call (partials + merge)
+        nbytes = fa.fa_fwd_splitkv_workspace_bytes(w.B, w.H, w.Hkv, w.decode_nq, w.N, w.d, 0)
+        ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+
+        def step(o=None, lse=None):
+            return fa.fwd_splitkv(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=ws)
     elif w.backward:
         # the gradient pass: the forward's o and lse are computed once, outside the timed
         # region; a step is one fa_bwd call (three launches)
@@ -203,6 +222,16 @@ def main():
     achieved = w.flops / (kernel_ms * 1e-3) / 1e12
     cdt = "e4m3" if w.fp8_block else w.dtype
     peak = PEAK_TFLOPS[cdt]
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name), "kernel_ms": round(kernel_ms, 5)}
+    if w.decode_nq:
+        # decode reads every K/V element once: HBM-bound; algorithmic bytes = Q + K + V + O + lse
+        el = 2
+        alg = (w.B * w.decode_nq * w.H * w.d * el * 2 + 2 * w.B * w.N * w.Hkv * w.d * el + 4 * w.B * w.H * w.decode_nq)
+        gbps = alg / (kernel_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": 8000.0, "unit": "GB/s",
+                "frac": round(gbps / 8000.0, 4), "traffic": measured_traffic(w.name), "kernel_ms": round(kernel_ms, 5),
+                "algorithmic_bytes": alg}
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -218,12 +247,11 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs)",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "Hkv": w.Hkv, "N": w.N, "d": w.d,
                    **({"pass": "backward (dq, dk, dv; FLOP = 2.5x forward)"} if w.backward else {}),
+                   **({"Nq": w.decode_nq, "Nk": w.N, "pass": "split-KV decode"} if w.decode_nq else {}),
                    "causal": w.causal, "scale": w.scale, "flop_per_step": w.flops,
                    **({"window": list(w.window)} if w.window else {}),
                    **({"fp8": "block scales (64 rows, E8M0), Hadamard-rotated q/k"} if w.fp8_block else {})},
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name),
-                     "kernel_ms": round(kernel_ms, 5)},
+        "roofline": roof,
     }
     if quant:
         out["quantize"] = quant

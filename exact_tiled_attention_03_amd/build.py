@@ -6,7 +6,7 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SOURCES = [os.path.join(PKG, "csrc", n) for n in ("fa_fwd.hip", "fa_quant.hip", "fa_bwd.hip")]
+SOURCES = [os.path.join(PKG, "csrc", n) for n in ("fa_fwd.hip", "fa_quant.hip", "fa_bwd.hip", "fa_splitkv.hip")]
 LIB = os.path.join(PKG, "libfa.so")
 
 HIPCC_FLAGS = [

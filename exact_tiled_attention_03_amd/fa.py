@@ -51,6 +51,10 @@ def lib() -> ctypes.CDLL:
             L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
             L.fa_bwd.argtypes = [vp] * 9 + [c_int] * 6 + [c_float, c_int, vp, ctypes.c_size_t, vp]
             L.fa_bwd.restype = c_int
+            L.fa_fwd_splitkv_workspace_bytes.argtypes = [c_int] * 7
+            L.fa_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
+            L.fa_fwd_splitkv.argtypes = [vp] * 5 + [c_int] * 7 + [c_float, c_int, c_int, vp, ctypes.c_size_t, vp]
+            L.fa_fwd_splitkv.restype = c_int
             L.fa_fwd_query.argtypes = [c_int] * 7 + [szp] * 5
             L.fa_fwd_query.restype = c_int
             L.fa_status_string.argtypes = [c_int]
@@ -118,6 +122,18 @@ def fa_bwd(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, do_ptr: int, lse_ptr:
     """Direct call of fa_bwd with raw pointers; returns the status code."""
     return int(lib().fa_bwd(q_ptr, k_ptr, v_ptr, o_ptr, do_ptr, lse_ptr, dq_ptr, dk_ptr, dv_ptr, B, H, Hkv, N, d,
                             int(causal), float(scale), int(dtype), ws_ptr, int(ws_bytes), stream))
+
+
+def fa_fwd_splitkv_workspace_bytes(B: int, H: int, Hkv: int, Nq: int, Nk: int, d: int, num_splits: int = 0) -> int:
+    return int(lib().fa_fwd_splitkv_workspace_bytes(B, H, Hkv, Nq, Nk, d, int(num_splits)))
+
+
+def fa_fwd_splitkv(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int, Hkv: int, Nq: int,
+                   Nk: int, d: int, causal: int, scale: float, dtype: int, num_splits: int, ws_ptr: int,
+                   ws_bytes: int, stream: int = 0) -> int:
+    """Direct call of fa_fwd_splitkv with raw pointers; returns the status code."""
+    return int(lib().fa_fwd_splitkv(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Hkv, Nq, Nk, d, int(causal),
+                                    float(scale), int(dtype), int(num_splits), ws_ptr, int(ws_bytes), stream))
 
 
 def fa_fwd_query(B: int, H: int, Hkv: int, N: int, d: int, causal: int, dtype: int) -> dict:
@@ -269,3 +285,33 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
                   dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d, int(bool(causal)), scale, code,
                   workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q, stream)))
     return dq, dk, dv
+
+
+def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_splits: int = 0, out=None, lse=None,
+                workspace=None, stream=None):
+    """Split-KV decode forward on device tensors: q [B,Nq,H,d] are the last Nq positions of
+    the sequence whose keys k, v [B,Nk,Hkv,d] cover all Nk positions. Returns (o, lse [B,H,Nq])."""
+    import torch
+    code = _dtype_code(q, None)
+    B, Nq, H, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    nbytes = fa_fwd_splitkv_workspace_bytes(B, H, Hkv, Nq, Nk, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 4) // 4, dtype=torch.float32, device=q.device)
+    for t in (q, k, v, out, lse, workspace):
+        if not t.is_contiguous() or t.device != q.device:
+            raise ValueError("tensors must be contiguous and on the same device")
+    if tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k and v must be [B,Nk,Hkv,d] matching q")
+    if tuple(out.shape) != (B, Nq, H, d) or out.dtype != q.dtype or tuple(lse.shape) != (B, H, Nq):
+        raise ValueError("out/lse have the wrong shape or type")
+    _check(fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Hkv, Nq, Nk,
+                          d, int(bool(causal)), scale, code, num_splits, workspace.data_ptr(),
+                          workspace.numel() * workspace.element_size(), _stream(q, stream)))
+    return out, lse

@@ -170,6 +170,31 @@ fa_status fa_bwd(const void* q, const void* k, const void* v, const void* o, con
                  size_t workspace_bytes, void* stream);
 
 /*
+ * Split-KV attention forward for decode: Nq queries that are the last Nq positions of a
+ * sequence whose keys and values cover all Nk positions (Nq <= Nk). Under the causal mask
+ * query i sees keys j <= Nk - Nq + i (with Nq = Nk this is fa_fwd's mask). The pages name
+ * work-centric and split schedules for decoding (the Lean Attention and Stream-K titles
+ * of their reference lists) without describing them; the library's reading: the key axis
+ * of each (batch, key/value head) is cut into ranges processed independently, each
+ * leaving an output normalised over its keys and its log-sum-exp, merged exactly by
+ * lse = ln sum_s exp(lse_s), O = sum_s exp(lse_s - lse) O_s.
+ *   q, o       [B][Nq][H][d]; k, v [B][Nk][Hkv][d]; lse [B][H][Nq] float32;
+ *   num_splits ranges per (batch, key/value head); <= 0 picks a count that keeps the GPU
+ *              busy; the effective count is at most ceil(Nk / 32);
+ *   workspace  device scratch of at least fa_fwd_splitkv_workspace_bytes(...) bytes (same
+ *              num_splits), 16-byte aligned, owned by the caller (partial outputs);
+ *              calls sharing a workspace must not overlap.
+ * Requires (H / Hkv) * Nq <= 64 (query rows sharing one key/value head); otherwise
+ * FA_ERR_UNSUPPORTED (use fa_fwd). q, k, v 16-byte aligned, o and lse 4-byte aligned;
+ * dtype F16 or BF16; d in {64, 128}. Enqueues two kernels (partials, merge) on `stream`.
+ */
+size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, int num_splits);
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                         int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                         fa_dtype dtype, int num_splits, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
  * Shape query: byte sizes of every buffer fa_fwd reads or writes for these arguments,
  * after the same size checks fa_fwd makes. Any output pointer may be NULL.
  * workspace_bytes is always 0 (no scratch memory). Pure host function.

@@ -41,6 +41,7 @@ class Workload:
     window: tuple | None = None     # (left, right) key window; negative side = unbounded
     fp8_block: bool = False         # e4m3 block-quantised on the GPU (drawn as bf16, rotated Q/K)
     backward: bool = False          # the gradient pass (upstream dO drawn with seed + 100)
+    decode_nq: int = 0              # split-KV decode: Nq queries against N keys (0: square)
 
     @property
     def flops(self) -> float:
@@ -49,6 +50,10 @@ class Workload:
         pass counts 2.5 times its forward (five N x N x d products instead of two)."""
         if self.backward:
             return 2.5 * replace(self, backward=False).flops
+        if self.decode_nq:
+            nq, nk = self.decode_nq, self.N
+            pairs = nq * nk - (nq * (nq - 1) // 2 if self.causal else 0)
+            return 4.0 * self.B * self.H * self.d * pairs
         if self.window is None:
             f = 4.0 * self.B * self.H * self.N * self.N * self.d
             return f / 2 if self.causal else f
@@ -72,7 +77,8 @@ def _w(name, B, H, Hkv, N, d, causal, dtype, seed, **kw):
 # bf16 causal grouped-query, and e4m3 with outliers; then a causal sliding-window case
 # (each query sees itself and the 4095 keys before it), the e4m3 shape again drawn in
 # bf16 for block quantisation with the Hadamard rotation (signs from the same seed), and
-# the gradient pass on the multi-head and the causal grouped-query shapes (same inputs).
+# the gradient pass on the multi-head and the causal grouped-query shapes (same inputs),
+# and single-query decode against a 16384-key grouped-query cache (split-KV).
 WORKLOADS = {
     w.name: w for w in [
         _w("tiny_f16_b1_h2_n128_d64", 1, 2, 2, 128, 64, False, "f16", 1001),
@@ -87,6 +93,7 @@ WORKLOADS = {
            outlier_frac=1e-3, outlier_mult=20.0, fp8_block=True),
         _w("bwd_bf16_b16_h16_n2048_d128", 16, 16, 16, 2048, 128, False, "bf16", 1002, backward=True),
         _w("bwd_causal_gqa_bf16_b4_h32_kv8_n8192_d128", 4, 32, 8, 8192, 128, True, "bf16", 1004, backward=True),
+        _w("decode_bf16_b8_h32_kv8_nq1_nk16384_d128", 8, 32, 8, 16384, 128, False, "bf16", 1007, decode_nq=1),
     ]
 }
 
@@ -148,6 +155,17 @@ def make_inputs(B: int, H: int, Hkv: int, N: int, d: int, dtype: str, seed: int,
     return out
 
 
+def make_decode_inputs(B: int, H: int, Hkv: int, Nq: int, Nk: int, d: int, dtype: str, seed: int):
+    """Q [B,Nq,H,d], then K and V [B,Nk,Hkv,d]: float32 N(0,1) from ``PCG64(seed)`` in that
+    order, rounded to `dtype` (bit patterns)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {}
+    for name, n, heads in (("q", Nq, H), ("k", Nk, Hkv), ("v", Nk, Hkv)):
+        out[name] = _round_bits(rng.standard_normal(size=(B, n, heads, d), dtype=np.float32), dtype)
+    out["descale"] = None
+    return out
+
+
 def make_dout(B: int, N: int, H: int, d: int, dtype: str, seed: int) -> np.ndarray:
     """An upstream gradient dO [B,N,H,d]: float32 N(0,1) from ``PCG64(seed)`` rounded to
     `dtype` (bit patterns)."""
@@ -167,5 +185,7 @@ def workload_inputs(w: Workload, keep_f32: bool = False, **overrides):
     """Inputs of a named workload (optionally with some sizes overridden)."""
     if overrides:
         w = w.with_(**overrides)
+    if w.decode_nq:
+        return make_decode_inputs(w.B, w.H, w.Hkv, w.decode_nq, w.N, w.d, w.dtype, w.seed)
     return make_inputs(w.B, w.H, w.Hkv, w.N, w.d, w.dtype, w.seed, w.outlier_frac,
                        w.outlier_mult, keep_f32=keep_f32)

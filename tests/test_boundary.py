@@ -189,6 +189,36 @@ def test_bwd_rejects_before_launch(over, status):
     assert st == status
 
 
+def test_splitkv_workspace_bytes():
+    # ranges are rounded up to whole 32-key blocks: Nk = 100 in 3 ranges -> 64-key ranges -> 2
+    assert fa.fa_fwd_splitkv_workspace_bytes(2, 8, 2, 1, 100, 128, 3) == 2 * 2 * 8 * 1 * 129 * 4
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 4, 4, 1, 64, 64, 50) == 2 * 1 * 4 * 1 * 65 * 4   # capped at 2
+    assert fa.fa_fwd_splitkv_workspace_bytes(1, 4, 4, 1, 64, 64, 0) > 0
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(ws=0), fa.FA_ERR_INVALID_ARG),
+    (dict(ws_bytes=0), fa.FA_ERR_INVALID_ARG),
+    (dict(q=FAKE + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(lse=FAKE + 2), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=10, Nk=5), fa.FA_ERR_INVALID_ARG),          # more queries than keys
+    (dict(Nq=0), fa.FA_ERR_INVALID_ARG),
+    (dict(H=16, Hkv=2, Nq=9), fa.FA_ERR_UNSUPPORTED),      # 72 query rows per K/V head
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=fa.FA_DTYPE_FP8_E4M3), fa.FA_ERR_UNSUPPORTED),
+    (dict(causal=5), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+])
+def test_splitkv_rejects_before_launch(over, status):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=4, Hkv=2, Nq=1, Nk=64, d=128, causal=0, scale=0.1,
+             dtype=fa.FA_DTYPE_BF16, splits=0, ws=FAKE, ws_bytes=1 << 20)
+    a.update(over)
+    st = fa.fa_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"],
+                           a["d"], a["causal"], a["scale"], a["dtype"], a["splits"], a["ws"], a["ws_bytes"])
+    assert st == status
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "absent.so"))
     monkeypatch.setattr(binding, "_lib", None)
