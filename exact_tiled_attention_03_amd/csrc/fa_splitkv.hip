@@ -282,13 +282,14 @@ __global__ __launch_bounds__(kThreads) void splitkv_merge_kernel(SkvArgs a) {
 // ---- host ----------------------------------------------------------------------------
 bool aligned(const void* p, size_t n) { return ((uintptr_t)p % n) == 0; }
 
-// Ranges per (batch, K/V head): num_splits if positive, else enough units to keep about
-// 2048 wavefronts busy with at least 256 keys each; then the range length is rounded up
-// to whole key blocks and the count recomputed, so that no range is empty.
+// Ranges per (batch, K/V head): num_splits if positive, else about one unit per SIMD
+// (1024 on MI355X; the d = 128 kernel holds one wavefront per SIMD, so more units only
+// queue behind the first round) with at least 256 keys each; then the range length is
+// rounded up to whole key blocks and the count recomputed, so that no range is empty.
 void plan(int B, int Hkv, int Nk, int num_splits, int* S, int* L) {
   int s = num_splits;
   if (s <= 0) {
-    const int want = (2048 + B * Hkv - 1) / (B * Hkv);
+    const int want = (1024 + B * Hkv - 1) / (B * Hkv);
     const int most = (Nk + 255) / 256;
     s = want < most ? want : most;
   }
