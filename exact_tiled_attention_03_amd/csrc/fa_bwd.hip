@@ -22,11 +22,12 @@
 //     layout of dV^T += dO^T P and dK^T += Q^T dS (queries consumed in a permuted order
 //     that the transposed Q^T / dO^T tiles in LDS are written in). dK and dV accumulate
 //     in registers over all query tiles: no atomics, deterministic.
-//   * dQ kernel: one workgroup of 4 wavefronts per (batch, head, 128 queries), the
+//   * dQ kernel: one workgroup of 8 wavefronts per (batch, head, 256 queries), the
 //     forward's orientation: S^T = K Q^T and dP^T = V dO^T with one query per lane, then
 //     dQ^T += K^T dS^T with K^T staged transposed in LDS.
 //   * Tiles are double-buffered in LDS; the next tile's global loads are in flight while
-//     the current one is computed. Row-major tiles use a 16-byte-chunk XOR swizzle, the
+//     the current one is computed. Eight wavefronts share each LDS tile, two per SIMD, so
+//     that one's MFMAs overlap the other's exponentials and LDS reads. Row-major tiles use a 16-byte-chunk XOR swizzle, the
 //     transposed tiles a chunk swizzle by the low bits of the dim.
 #include <hip/hip_runtime.h>
 
@@ -45,7 +46,9 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kThreads = 256;          // 4 wavefronts
+constexpr int kThreads = 256;          // preprocess kernel
+constexpr int kWavesKV = 4;            // dK/dV kernel: wavefronts per workgroup, 32 keys each
+constexpr int kWavesQ = 8;             // dQ kernel: wavefronts per workgroup, 32 queries each
 constexpr float kLog2e = 1.4426950408889634f;
 
 struct Bf16 {
@@ -166,8 +169,8 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(BwdArgs a) {
 
 // ---- dK / dV -------------------------------------------------------------------------
 template <typename Ops, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int kBk = 128;                 // keys per workgroup, 32 per wavefront
+__global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int kBk = 32 * kWavesKV;       // keys per workgroup, 32 per wavefront
   constexpr int kBq = 64;                  // queries per tile
   constexpr int kKsteps = D / 16;
   constexpr int kDblocks = D / 32;
@@ -175,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int kBuf = 4 * kTile + 2 * kBq * 4;   // Q, dO (row-major), Q^T, dO^T, lse2, D
   constexpr int kChunks = D / 8;
   constexpr int kUnits = (kBq / 4) * kChunks;      // staging units of 4 rows x 8 dims
-  static_assert(kUnits % 64 == 0 && kUnits <= kThreads, "staging units fill whole wavefronts");
+  static_assert(kUnits % 64 == 0 && kUnits <= 64 * kWavesKV, "staging units fill whole wavefronts");
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kBuf];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -354,8 +357,8 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(BwdArgs a) {
 
 // ---- dQ ------------------------------------------------------------------------------
 template <typename Ops, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
-  constexpr int kBq = 128;                 // queries per workgroup, 32 per wavefront
+__global__ __launch_bounds__(64 * kWavesQ) void bwd_dq_kernel(BwdArgs a) {
+  constexpr int kBq = 32 * kWavesQ;        // queries per workgroup, 32 per wavefront
   constexpr int kBk = 64;                  // keys per tile
   constexpr int kKb = kBk / 32;            // 32-key blocks per tile
   constexpr int kKsteps = D / 16;
@@ -364,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(BwdArgs a) {
   constexpr int kBuf = 3 * kTile;          // K, V (row-major), K^T
   constexpr int kChunks = D / 8;
   constexpr int kUnits = (kBk / 4) * kChunks;
-  static_assert(kUnits % 64 == 0 && kUnits <= kThreads, "staging units fill whole wavefronts");
+  static_assert(kUnits % 64 == 0 && kUnits <= 64 * kWavesQ, "staging units fill whole wavefronts");
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kBuf];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -511,14 +514,14 @@ fa_status launch_bwd(BwdArgs args, hipStream_t s) {
   hipLaunchKernelGGL((bwd_delta_kernel<Ops, D>), dim3((rows + per_block - 1) / per_block), dim3(kThreads), 0, s, args);
   if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
   BwdArgs kv = args;
-  kv.tiles = (args.N + 127) / 128;
+  kv.tiles = (args.N + 32 * kWavesKV - 1) / (32 * kWavesKV);
   kv.total = kv.tiles * args.Hkv * args.B;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<Ops, D, CAUSAL>), dim3(kv.total), dim3(kThreads), 0, s, kv);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<Ops, D, CAUSAL>), dim3(kv.total), dim3(64 * kWavesKV), 0, s, kv);
   if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
   BwdArgs qa = args;
-  qa.tiles = (args.N + 127) / 128;
+  qa.tiles = (args.N + 32 * kWavesQ - 1) / (32 * kWavesQ);
   qa.total = qa.tiles * args.H * args.B;
-  hipLaunchKernelGGL((bwd_dq_kernel<Ops, D, CAUSAL>), dim3(qa.total), dim3(kThreads), 0, s, qa);
+  hipLaunchKernelGGL((bwd_dq_kernel<Ops, D, CAUSAL>), dim3(qa.total), dim3(64 * kWavesQ), 0, s, qa);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -536,7 +539,7 @@ fa_status check_bwd(int B, int H, int Hkv, int N, int d, int causal, fa_dtype dt
     return dtype == FA_DTYPE_FP8_E4M3 ? FA_ERR_UNSUPPORTED : FA_ERR_INVALID_ARG;
   }
   if ((long long)B * N * H * d >= (1LL << 31)) return FA_ERR_INVALID_ARG;
-  if ((long long)(N + 127) / 128 * H * B > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  if ((long long)(N + 31) / 32 * H * B > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
