@@ -47,7 +47,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;          // preprocess kernel
-constexpr int kWavesKV = 4;            // dK/dV kernel: wavefronts per workgroup, 32 keys each
+constexpr int kWavesKV = 8;            // dK/dV kernel: wavefronts per workgroup, 16 keys each
 constexpr int kWavesQ = 8;             // dQ kernel: wavefronts per workgroup, 32 queries each
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -168,61 +168,89 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_kernel(BwdArgs a) {
 }
 
 // ---- dK / dV -------------------------------------------------------------------------
+// v_mfma_f32_16x16x32 layouts (lane l, g = l/16, c = l%16): A[m = c][k = 8g + i],
+// B[k = 8g + i][n = c], C[row = 4g + i][col = c]. Two 16-row accumulator blocks hand
+// their 32 rows to the next MFMA's k index in the order
+//   slot(x) = 32(x/32) + 8((x%16)/4) + 4((x%32)/16) + x%4,
+// in which the transposed Q^T / dO^T tiles are written.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+template <typename Ops>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c);
+template <>
+__device__ __forceinline__ f32x4 mfma16<Bf16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f32x4 mfma16<F16>(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ int slot32_of(int x) {
+  return (x & ~31) + (((x & 15) >> 2) << 3) + (((x & 31) >> 4) << 2) + (x & 3);
+}
+template <int D>
+__device__ __forceinline__ int rm16_byte(int r, int chunk) {       // row-major, 16-byte chunks
+  return r * (2 * D) + ((chunk ^ (r & (D / 8 - 1))) << 4);
+}
+template <int R>
+__device__ __forceinline__ int tr16_byte(int dim, int slot) {      // transposed, rows in slot order
+  return dim * (2 * R) + ((((slot >> 3) ^ dim) & (R / 8 - 1)) << 4) + ((slot & 7) << 1);
+}
+
 template <typename Ops, int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int kBk = 32 * kWavesKV;       // keys per workgroup, 32 per wavefront
+  constexpr int kKeysPerWave = 16;
+  constexpr int kBk = kKeysPerWave * kWavesKV;   // keys per workgroup
   constexpr int kBq = 64;                  // queries per tile
-  constexpr int kKsteps = D / 16;
-  constexpr int kDblocks = D / 32;
+  constexpr int kKsteps = D / 32;          // k-steps of the 16x16x32 MFMA over d
+  constexpr int kDblocks = D / 16;         // 16-dim blocks of dK^T / dV^T
   constexpr int kTile = kBq * D * 2;       // one 16-bit tile
   constexpr int kBuf = 4 * kTile + 2 * kBq * 4;   // Q, dO (row-major), Q^T, dO^T, lse2, D
   constexpr int kChunks = D / 8;
-  constexpr int kUnits = (kBq / 4) * kChunks;      // staging units of 4 rows x 8 dims
-  static_assert(kUnits % 64 == 0 && kUnits <= 64 * kWavesKV, "staging units fill whole wavefronts");
+  constexpr int kUnits = (kBq / 4) * kChunks;      // staging units (4 rows x 8 dims) per tensor
+  static_assert(2 * kUnits <= 64 * kWavesKV && kUnits % 64 == 0, "each half stages one tensor");
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kBuf];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l32 = lane & 31, hi = lane >> 5;
+  const int g = lane >> 4, c = lane & 15;
   const int lg = logical_index(blockIdx.x, a.total);
   const int kt = lg % a.tiles;
   const int bh = lg / a.tiles;               // b * Hkv + hk
   const int hk = bh % a.Hkv, b = bh / a.Hkv;
   const int N = a.N;
   const int k0 = kt * kBk;
-  const int kw0 = k0 + 32 * wave;            // this wavefront's first key
-  const int key = kw0 + l32;                 // this lane's key (MFMA column)
+  const int kw0 = k0 + kKeysPerWave * wave;  // this wavefront's first key
+  const int key = kw0 + c;                   // this lane's key (MFMA column)
   const size_t q_stride = (size_t)a.H * D, kv_stride = (size_t)a.Hkv * D;
 
-  // K and V rows of the lane's key as B operands: dims 16ks + 8hi .. +7
+  // K and V rows of the lane's key as B operands: dims 32ks + 8g .. +7
   u32x4 kreg[kKsteps], vreg[kKsteps];
   {
     const int kr = min(key, N - 1);
-    const uint16_t* kp = (const uint16_t*)a.k + ((size_t)b * N + kr) * kv_stride + (size_t)hk * D + hi * 8;
-    const uint16_t* vp = (const uint16_t*)a.v + ((size_t)b * N + kr) * kv_stride + (size_t)hk * D + hi * 8;
+    const uint16_t* kp = (const uint16_t*)a.k + ((size_t)b * N + kr) * kv_stride + (size_t)hk * D + g * 8;
+    const uint16_t* vp = (const uint16_t*)a.v + ((size_t)b * N + kr) * kv_stride + (size_t)hk * D + g * 8;
 #pragma unroll
     for (int ks = 0; ks < kKsteps; ++ks) {
-      kreg[ks] = *(const u32x4*)(kp + ks * 16);
-      vreg[ks] = *(const u32x4*)(vp + ks * 16);
+      kreg[ks] = *(const u32x4*)(kp + ks * 32);
+      vreg[ks] = *(const u32x4*)(vp + ks * 32);
     }
   }
-  f32x16 dkT[kDblocks], dvT[kDblocks];       // C[dim][key]
+  f32x4 dkT[kDblocks], dvT[kDblocks];        // C[dim][key]
 #pragma unroll
   for (int i = 0; i < kDblocks; ++i)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) dkT[i][e] = dvT[i][e] = 0.0f;
+    for (int e = 0; e < 4; ++e) dkT[i][e] = dvT[i][e] = 0.0f;
 
-  // query tiles: every head of the group, and under the causal mask only tiles that
-  // reach this workgroup's first key
   const int qt0 = CAUSAL ? k0 / kBq : 0;
   const int nqt = (N + kBq - 1) / kBq;
   const int per_head = nqt - qt0;
   const int T = per_head * a.group;
 
-  // staging: unit u = tid (< kUnits): rows 4g..4g+3 of the tile, dims 8c..8c+7
-  const bool stager = tid < kUnits;
-  const int sg = tid / kChunks, sc = tid % kChunks;
-  u32x4 qrows[4], drows[4];
-  float lse_st = 0.0f, del_st = 0.0f;
+  // staging: the first kUnits threads stage Q, the next kUnits dO; unit = rows 4sg..4sg+3,
+  // dims 8sc..8sc+7
+  const int su = tid % kUnits, which = tid / kUnits;   // which: 0 Q, 1 dO, 2+ none
+  const int sg = su / kChunks, sc = su % kChunks;
+  u32x4 rows[4];
+  float lse_st = 0.0f;
   auto tile_coords = [&](int t, int& h, int& q0) __attribute__((always_inline)) {
     h = hk * a.group + t / per_head;
     q0 = (qt0 + t % per_head) * kBq;
@@ -230,32 +258,39 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
   auto load_tile = [&](int t) __attribute__((always_inline)) {
     int h, q0;
     tile_coords(t, h, q0);
-    if (stager) {
+    if (which < 2) {
+      const uint16_t* src = (const uint16_t*)(which == 0 ? a.q : a.dout);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = min(q0 + 4 * sg + j, N - 1);
-        const size_t off = ((size_t)b * N + r) * q_stride + (size_t)h * D + sc * 8;
-        qrows[j] = *(const u32x4*)((const uint16_t*)a.q + off);
-        drows[j] = *(const u32x4*)((const uint16_t*)a.dout + off);
+        rows[j] = *(const u32x4*)(src + ((size_t)b * N + r) * q_stride + (size_t)h * D + sc * 8);
       }
     }
-    if (tid < kBq) {
-      const int r = q0 + tid;
+    if (tid < 2 * kBq) {                     // lse (scaled to base 2) then D
+      const int r = q0 + (tid % kBq);
       const size_t off = ((size_t)b * a.H + h) * N + min(r, N - 1);
-      lse_st = r < N ? a.lse[off] * kLog2e : INFINITY;     // rows past the end: P = 0
-      del_st = r < N ? a.delta[off] : 0.0f;
+      if (tid < kBq) lse_st = r < N ? a.lse[off] * kLog2e : INFINITY;     // rows past the end: P = 0
+      else lse_st = r < N ? a.delta[off] : 0.0f;
     }
   };
   auto store_tile = [&](int buf) __attribute__((always_inline)) {
     unsigned char* base = lds + buf * kBuf;
-    if (stager) {
-      stage_rows<D, kBq, true, true>(base, base + 2 * kTile, sg, sc, qrows);
-      stage_rows<D, kBq, true, true>(base + kTile, base + 3 * kTile, sg, sc, drows);
+    if (which < 2) {
+      unsigned char* rm = base + which * kTile;
+      unsigned char* tr = base + (2 + which) * kTile;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *(u32x4*)(rm + rm16_byte<D>(4 * sg + j, sc)) = rows[j];
+      const int s0 = slot32_of(4 * sg);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        u32x2 w;
+        w[0] = __builtin_amdgcn_perm(rows[1][e >> 1], rows[0][e >> 1], sel);
+        w[1] = __builtin_amdgcn_perm(rows[3][e >> 1], rows[2][e >> 1], sel);
+        *(u32x2*)(tr + tr16_byte<kBq>(8 * sc + e, s0)) = w;
+      }
     }
-    if (tid < kBq) {
-      ((float*)(base + 4 * kTile))[tid] = lse_st;
-      ((float*)(base + 4 * kTile + kBq * 4))[tid] = del_st;
-    }
+    if (tid < 2 * kBq) ((float*)(base + 4 * kTile))[tid] = lse_st;
   };
 
   load_tile(0);
@@ -272,86 +307,73 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
     const unsigned char* qtr = base + 2 * kTile;
     const unsigned char* dtr = base + 3 * kTile;
     const float* lse2 = (const float*)(base + 4 * kTile);
-    const float* dlt = (const float*)(base + 4 * kTile + kBq * 4);
+    const float* dlt = lse2 + kBq;
 #pragma unroll
-    for (int qb = 0; qb < kBq / 32; ++qb) {
-      const int qb0 = q0 + qb * 32;
-      // causal: no key of this wavefront is visible to any query of the block
-      if (CAUSAL && kw0 > qb0 + 31) continue;
-      f32x16 s, dp;
+    for (int qc = 0; qc < kBq / 32; ++qc) {  // 32-query chunks
+      const int qc0 = q0 + qc * 32;
+      if (CAUSAL && kw0 > qc0 + 31) continue;
+      u32x4 pb, db;                          // P and dS of the chunk as B operands
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.0f;
+      for (int half = 0; half < 2; ++half) { // 16-query blocks of the chunk
+        const int r = qc * 32 + half * 16 + c;
+        f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f}, dpacc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int ks = 0; ks < kKsteps; ++ks) {
-        const int r = qb * 32 + l32;
-        const u32x4 qa = lds_read<u32x4>(qrm, rm_byte<D>(r, 2 * ks + hi));
-        const u32x4 da = lds_read<u32x4>(drm, rm_byte<D>(r, 2 * ks + hi));
-        s = Ops::mfma(qa, kreg[ks], s);
-        dp = Ops::mfma(da, vreg[ks], dp);
-      }
-      // P and dS, lane-local: accumulator e holds query row qb*32 + 8(e/4) + 4hi + e%4
-      float pv[16], dsv[16];
-      const bool need_mask = (CAUSAL && kw0 + 31 > qb0) || key >= N;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 l4 = *(const float4*)(lse2 + qb * 32 + 8 * g + 4 * hi);
-        const float4 d4 = *(const float4*)(dlt + qb * 32 + 8 * g + 4 * hi);
+        for (int ks = 0; ks < kKsteps; ++ks) {
+          const u32x4 qa = lds_read<u32x4>(qrm, rm16_byte<D>(r, 4 * ks + g));
+          const u32x4 da = lds_read<u32x4>(drm, rm16_byte<D>(r, 4 * ks + g));
+          sacc = mfma16<Ops>(qa, kreg[ks], sacc);
+          dpacc = mfma16<Ops>(da, vreg[ks], dpacc);
+        }
+        // accumulator i: query row qc*32 + half*16 + 4g + i, key column c
+        const int q4 = qc * 32 + half * 16 + 4 * g;
+        const float4 l4 = *(const float4*)(lse2 + q4);
+        const float4 d4 = *(const float4*)(dlt + q4);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+        const bool need_mask = (CAUSAL && kw0 + kKeysPerWave - 1 > q0 + q4) || key >= N;
+        float pv[4], dsv[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int e = 4 * g + j;
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], a.c, -lv[j]));
-          if (need_mask) {
-            const int qi = qb0 + 8 * g + 4 * hi + j;
-            if ((CAUSAL && key > qi) || key >= N) p = 0.0f;
-          }
-          pv[e] = p;
-          dsv[e] = p * (dp[e] - dv[j]);
+        for (int i = 0; i < 4; ++i) {
+          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], a.c, -lv[i]));
+          if (need_mask && ((CAUSAL && key > q0 + q4 + i) || key >= N)) p = 0.0f;
+          pv[i] = p;
+          dsv[i] = p * (dpacc[i] - dv4[i]);
         }
+        // k-slots 8g + 4*half + i of the chunk's B operand
+        pb[2 * half] = Ops::pack2(pv[0], pv[1]);
+        pb[2 * half + 1] = Ops::pack2(pv[2], pv[3]);
+        db[2 * half] = Ops::pack2(dsv[0], dsv[1]);
+        db[2 * half + 1] = Ops::pack2(dsv[2], dsv[3]);
       }
-      // B operands for the two k-steps (16 queries each): registers 8t .. 8t+7
-      u32x4 pb[2], db[2];
+      // dV^T += dO^T P, dK^T += Q^T dS: A from the transposed tiles, dim 16 dbk + c,
+      // slots qc*32 + 8g .. +7
 #pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          pb[t2][w] = Ops::pack2(pv[8 * t2 + 2 * w], pv[8 * t2 + 2 * w + 1]);
-          db[t2][w] = Ops::pack2(dsv[8 * t2 + 2 * w], dsv[8 * t2 + 2 * w + 1]);
-        }
-      // dV^T += dO^T P, dK^T += Q^T dS: A operands from the transposed tiles, slots
-      // qb*32 + 16 t2 + 8 hi .. +7 of dim 32 db + l32
-#pragma unroll
-      for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-        for (int dbk = 0; dbk < kDblocks; ++dbk) {
-          const int dim = dbk * 32 + l32, slot = qb * 32 + t2 * 16 + hi * 8;
-          const u32x4 da = lds_read<u32x4>(dtr, tr_byte<kBq>(dim, slot));
-          const u32x4 qa = lds_read<u32x4>(qtr, tr_byte<kBq>(dim, slot));
-          dvT[dbk] = Ops::mfma(da, pb[t2], dvT[dbk]);
-          dkT[dbk] = Ops::mfma(qa, db[t2], dkT[dbk]);
-        }
+      for (int dbk = 0; dbk < kDblocks; ++dbk) {
+        const int dim = dbk * 16 + c, slot = qc * 32 + g * 8;
+        const u32x4 da = lds_read<u32x4>(dtr, tr16_byte<kBq>(dim, slot));
+        const u32x4 qa = lds_read<u32x4>(qtr, tr16_byte<kBq>(dim, slot));
+        dvT[dbk] = mfma16<Ops>(da, pb, dvT[dbk]);
+        dkT[dbk] = mfma16<Ops>(qa, db, dkT[dbk]);
+      }
     }
     if (t + 1 < T) store_tile((t + 1) & 1);
     __syncthreads();
   }
 
-  // epilogue: lane holds dims 32db + 8g + 4hi + 0..3 of its key
+  // epilogue: lane holds dims 16dbk + 4g + 0..3 of its key
   if (key < N) {
     const size_t off = ((size_t)b * N + key) * kv_stride + (size_t)hk * D;
 #pragma unroll
-    for (int dbk = 0; dbk < kDblocks; ++dbk)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int dim = dbk * 32 + 8 * g + 4 * hi;
-        u32x2 wk, wv;
-        wk[0] = Ops::pack2(dkT[dbk][4 * g] * a.scale, dkT[dbk][4 * g + 1] * a.scale);
-        wk[1] = Ops::pack2(dkT[dbk][4 * g + 2] * a.scale, dkT[dbk][4 * g + 3] * a.scale);
-        wv[0] = Ops::pack2(dvT[dbk][4 * g], dvT[dbk][4 * g + 1]);
-        wv[1] = Ops::pack2(dvT[dbk][4 * g + 2], dvT[dbk][4 * g + 3]);
-        *(u32x2*)((uint16_t*)a.dk + off + dim) = wk;
-        *(u32x2*)((uint16_t*)a.dv + off + dim) = wv;
-      }
+    for (int dbk = 0; dbk < kDblocks; ++dbk) {
+      const int dim = dbk * 16 + 4 * g;
+      u32x2 wk, wv;
+      wk[0] = Ops::pack2(dkT[dbk][0] * a.scale, dkT[dbk][1] * a.scale);
+      wk[1] = Ops::pack2(dkT[dbk][2] * a.scale, dkT[dbk][3] * a.scale);
+      wv[0] = Ops::pack2(dvT[dbk][0], dvT[dbk][1]);
+      wv[1] = Ops::pack2(dvT[dbk][2], dvT[dbk][3]);
+      *(u32x2*)((uint16_t*)a.dk + off + dim) = wk;
+      *(u32x2*)((uint16_t*)a.dv + off + dim) = wv;
+    }
   }
 }
 
@@ -514,7 +536,7 @@ fa_status launch_bwd(BwdArgs args, hipStream_t s) {
   hipLaunchKernelGGL((bwd_delta_kernel<Ops, D>), dim3((rows + per_block - 1) / per_block), dim3(kThreads), 0, s, args);
   if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
   BwdArgs kv = args;
-  kv.tiles = (args.N + 32 * kWavesKV - 1) / (32 * kWavesKV);
+  kv.tiles = (args.N + 16 * kWavesKV - 1) / (16 * kWavesKV);
   kv.total = kv.tiles * args.Hkv * args.B;
   hipLaunchKernelGGL((bwd_dkdv_kernel<Ops, D, CAUSAL>), dim3(kv.total), dim3(64 * kWavesKV), 0, s, kv);
   if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
