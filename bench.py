@@ -31,25 +31,29 @@ import synth_inputs  # noqa: E402
 DEFAULT_WORKLOAD = "mha_bf16_b16_h16_n2048_d128"
 # Dense MFMA peak of MI355X: 256 CUs x 4 SIMDs x 2.4 GHz x (1024 bf16/f16 or 2048 fp8 FLOP/clk/SIMD)
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2}
-KERNEL_SRC = os.path.join(ROOT, "exact_tiled_attention_03_amd", "csrc", "fa_fwd.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 METRIC = "attention fwd TFLOP/s (4*B*H*N^2*d, causal halved) and % MFMA peak, bf16 d=128"
 
 
-def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(os.path.join(ROOT, path), "rb").read()).hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken
-    on this exact kernel source and workload; else None."""
+    """HBM bytes per step from the committed rocprofv3 counter summary, if it was taken on
+    the current sources of every kernel the step runs; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
     entry = t.get("workloads", {}).get(workload)
-    if not entry or entry.get("kernel_source_sha256_16") != kernel_source_hash():
+    if not entry:
+        return None
+    try:
+        if any(source_hash(path) != sha for path, sha in entry.get("kernel_sources", {}).items()):
+            return None
+    except OSError:
         return None
     return entry.get("hbm_bytes_per_launch")
 

@@ -251,9 +251,12 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
   const int sg = su / kChunks, sc = su % kChunks;
   u32x4 rows[4];
   float lse_st = 0.0f;
+  // query tiles from the last one down, so that the workgroups of one K/V head (which
+  // start at different tiles under the causal mask) read the same Q/dO tile at about the
+  // same time and share it in L2
   auto tile_coords = [&](int t, int& h, int& q0) __attribute__((always_inline)) {
     h = hk * a.group + t / per_head;
-    q0 = (qt0 + t % per_head) * kBq;
+    q0 = (nqt - 1 - t % per_head) * kBq;
   };
   auto load_tile = [&](int t) __attribute__((always_inline)) {
     int h, q0;
