@@ -925,6 +925,10 @@ fa_status check_sizes(int B, int H, int Hkv, int N, int d, int causal, fa_dtype 
   const long long grid = ((long long)N + kBr - 1) / kBr * H * B;
   if (grid > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // K and V of one batch are addressed through buffer descriptors with 32-bit offsets and
+  // a signed 32-bit extent
+  const long long kv_batch_bytes = (long long)N * Hkv * d * (dtype == FA_DTYPE_FP8_E4M3 ? 1 : 2);
+  if (kv_batch_bytes >= (1LL << 31)) return FA_ERR_UNSUPPORTED;
   return FA_OK;
 }
 

@@ -69,7 +69,8 @@ typedef enum {
  *   o         device pointer, [B][N][H][d] of the output type, 16-byte aligned.
  *   lse       device pointer, [B][H][N] float32, 4-byte aligned.
  *   B, H, Hkv, N, d   sizes: B >= 1, N >= 1, 1 <= Hkv <= H, H % Hkv == 0,
- *             d in {64, 128}; every tensor must have fewer than 2^31 elements.
+ *             d in {64, 128}; every tensor must have fewer than 2^31 elements, and K (and
+ *             V) of one batch fewer than 2^31 bytes (else FA_ERR_UNSUPPORTED).
  *   causal    0 (no mask) or 1 (key j visible to query i iff j <= i).
  *   scale     finite, > 0; multiplies q.k before the softmax (1/sqrt(d) is usual).
  *   dtype     element type of q, k, v (see above).

@@ -36,6 +36,13 @@ def test_version_and_status_strings():
     assert "unknown" in fa.status_string(99)
 
 
+def test_query_accepts_kv_just_under_2gib():
+    q = fa.fa_fwd_query(1, 8, 8, (1 << 20) - 1, 128, 0, fa.FA_DTYPE_BF16)
+    assert q["kv"] == ((1 << 20) - 1) * 8 * 128 * 2
+    q8 = fa.fa_fwd_query(1, 8, 8, 1 << 20, 128, 0, fa.FA_DTYPE_FP8_E4M3)   # 1 byte per element
+    assert q8["kv"] == (1 << 30)
+
+
 def test_query_sizes():
     q = fa.fa_fwd_query(4, 32, 8, 8192, 128, 1, fa.FA_DTYPE_BF16)
     assert q == {"q": 4 * 8192 * 32 * 128 * 2, "kv": 4 * 8192 * 8 * 128 * 2, "o": 4 * 8192 * 32 * 128 * 2,
@@ -55,6 +62,7 @@ def test_query_sizes():
     (dict(causal=2), fa.FA_ERR_INVALID_ARG),
     (dict(dtype=7), fa.FA_ERR_INVALID_ARG),
     (dict(B=1 << 20, N=1 << 12), fa.FA_ERR_INVALID_ARG),   # more than 2^31 elements
+    (dict(B=1, H=8, Hkv=8, N=1 << 20, d=128), fa.FA_ERR_UNSUPPORTED),   # K of one batch: 2^31 bytes
 ])
 def test_query_rejects(args, status):
     a = dict(B=1, H=4, Hkv=2, N=64, d=128, causal=0, dtype=fa.FA_DTYPE_BF16)
