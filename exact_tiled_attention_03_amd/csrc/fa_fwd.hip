@@ -12,7 +12,8 @@
 // workgroup's K/V tiles, so no partial output rows are reduced across wavefronts (item 3).
 // Non-matmul work is kept small (item 1): the scale is folded into one FMA before a
 // base-2 exponential, the output is normalised once at the end, and the accumulator is
-// only rescaled when a row maximum has grown by more than 2^8.
+// only rescaled when probabilities taken against the current maximum could overflow
+// their 16-bit storage (a lane's sum above 2^15), not whenever the maximum grows.
 //
 // gfx950 mapping (one wavefront = 64 lanes, MFMA 32x32x16):
 //   * The score tile is computed transposed, S^T = K Q^T, so that each lane holds one
@@ -21,9 +22,13 @@
 //   * The output is accumulated transposed, O^T += V^T P^T, so the per-query rescale is
 //     lane-local too. The probabilities leave the S^T accumulator already in the B-operand
 //     layout of the next MFMA (keys are consumed in a permuted order, matched on the V side).
-//   * V^T operands come straight from the row-major V tile with ds_read_b64_tr_b16.
-//   * K/V tiles are double-buffered in LDS with a 16-byte-chunk XOR swizzle; the next
-//     tile's global loads are in flight while the current tile is computed.
+//   * K tiles go from global memory straight into LDS (buffer loads with an LDS
+//     destination) in a 16-byte-chunk XOR swizzle; V tiles pass through registers, where
+//     they are transposed into V^T (the transposing LDS read, ds_read_b64_tr_b16, runs at
+//     a third of the rate of a plain read on gfx950).
+//   * Each wavefront overlaps the MFMAs of the next score tile with the softmax of the
+//     current one, and the P.V MFMAs with the staging of later tiles; K and V^T are
+//     double-buffered in LDS, one barrier per key tile.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -214,9 +219,35 @@ __device__ __forceinline__ T lds_load(const lds_byte* base, int byte_off) {
 template <int V>
 using ic = std::integral_constant<int, V>;
 
-// ---- the forward kernel for 16-bit inputs -------------------------------------------
+// ---- the forward kernel for 16-bit inputs -----------------------------------------------
+// One workgroup of 8 wavefronts per (batch, head, 256-query tile); wavefront w owns query
+// rows [32w, 32w+32) and all wavefronts share the K/V tiles staged in LDS. Each wavefront
+// software-pipelines its own work: while the MFMAs of S(j+1) = K(j+1) Q^T run it computes
+// the softmax of tile j, and while those of O^T += V^T(j) P^T(j) run it stages later tiles;
+// one barrier per key tile hands the LDS buffers over.
+// K tiles go from global memory straight into LDS (buffer loads with an LDS destination),
+// so only V passes through registers, where it is transposed. K and V^T have two LDS
+// slots each: during step j, K(j+2) goes to K slot j&1 and V(j+1) to V slot (j+1)&1, both
+// after the barrier that ended the last read of that slot.
+// s_waitcnt operand: vmcnt <= 8, expcnt and lgkmcnt not waited for
+constexpr int kVmcnt8 = 0x8 | (0x7 << 4) | (0xF << 8);
+
+// one 16-byte-per-lane buffer load into LDS: lane i writes dst + 16 i
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, lds_byte* dst, unsigned voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, voffset, 0, 0, 0);
+}
+// LDS address of a K-tile DMA destination, passed through an opaque register copy: the
+// compiler then keeps no alias record of the DMA (it would otherwise wait for every DMA
+// before every later LDS read), and the waits for it are the explicit vmcnt waits before
+// the barriers of the kernel below
+__device__ __forceinline__ lds_byte* lds_dma_dst(unsigned char* p) {
+  unsigned v = (unsigned)(uintptr_t)(lds_byte*)p;
+  asm volatile("" : "+s"(v));
+  return (lds_byte*)(uintptr_t)v;
+}
+
 template <typename Ops, int D, int MASK>
-__global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
   constexpr bool CAUSAL = MASK == kMaskCausal;
   constexpr bool BAND = MASK == kMaskBand;
   constexpr int kChunks = D / 8;                  // 16-byte chunks per K row
@@ -224,9 +255,10 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
   constexpr int kDblocks = D / 32;                // 32-row blocks of O^T
   constexpr int kKb = kBc / 32;                   // 32-key blocks per tile
   constexpr int kTileBytes = kBc * D * 2;
-  constexpr int kStageBytes = 2 * kTileBytes;     // K tile then V^T tile
+  constexpr int kVBase = 2 * kTileBytes;
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kStageBytes];
+  // K slot 0, K slot 1, V^T slot 0, V^T slot 1
+  __shared__ __attribute__((aligned(16))) unsigned char lds[4 * kTileBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -239,11 +271,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
   const int hk = h / a.group;
   const int N = a.N;
   const int q0 = qt * kBr;
-  const int qw0 = q0 + wave * 32;                 // this wavefront's first query
-  const int qi = qw0 + l32;                       // this lane's query
-  // Keys are addressed from kv0, the first key of the first tile this query tile can see
-  // (under the band mask the left end of its first query's window, rounded down to a
-  // tile; else 0); nk keys follow it up to the end of the sequence.
+  const int qw0 = q0 + wave * 32;
+  const int qi = qw0 + l32;
   const int kv0 = BAND ? max(0, q0 - a.wl) / kBc * kBc : 0;
   const int nk = N - kv0;
 
@@ -253,8 +282,6 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
   const uint16_t* kp = (const uint16_t*)a.k + ((size_t)b * N + kv0) * kv_row_stride + (size_t)hk * D;
   const uint16_t* vp = (const uint16_t*)a.v + ((size_t)b * N + kv0) * kv_row_stride + (size_t)hk * D;
 
-  // Q^T operand: lane holds q[qi][ks*16 + hi*8 .. +7] for every k-step; rows past the
-  // end are read from row N-1 (in bounds) and never stored
   u32x4 qreg[kKsteps];
   const int qi_ld = min(qi, N - 1);
 #pragma unroll
@@ -264,175 +291,112 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
   const int kv_end = BAND ? min(N, q0 + kBr + a.wr) : CAUSAL ? min(N, q0 + kBr) : N;
   const int ntiles = (kv_end - kv0 + kBc - 1) / kBc;
 
-  // per-lane LDS byte offsets of the MFMA operands (stage 0, key block 0); the key block,
-  // the half and the stage only add compile-time constants
   int koff[kKsteps];
 #pragma unroll
   for (int ks = 0; ks < kKsteps; ++ks) koff[ks] = k_byte<D>(l32, ks * 16 + hi * 8);
   int voff[kDblocks];
 #pragma unroll
-  for (int db = 0; db < kDblocks; ++db) voff[db] = kTileBytes + vt_byte<D>(0, db * 32 + l32, hi);
+  for (int db = 0; db < kDblocks; ++db) voff[db] = kVBase + vt_byte<D>(0, db * 32 + l32, hi);
 
-  // ---- staging of one LDS slot ----------------------------------------------------------
-  // Slot j holds the K tile of key tile j and the V^T tile of key tile j-1 (see the
-  // schedule below). Wavefront w stages keys [8w, 8w+8) of each tile:
-  //   K: rows 8w.., each lane one 16-byte chunk per load (kKRows rows per load), kept in
-  //      memory order;
-  //   V: the 8 keys of stored chunk (w&1) of key group w>>1, i.e. keys
-  //      16(w>>1) + 4(w&1) + {0,1,2,3,8,9,10,11}; lane l holds dims 2l and 2l+1 of each
-  //      and transposes them into two 16-byte V^T chunks (one per dim).
-  // Row addresses are wavefront-uniform; only a ragged last tile clamps rows past the end
-  // to row N-1 per lane (such keys are masked to -inf, so they add exp2(-inf) = 0 times a
-  // finite V row).
+  // ---- staging ------------------------------------------------------------------------
+  // Wavefront w stages keys [8w, 8w+8) of K and one V^T chunk of a tile:
+  //   K: straight from global memory into LDS (buffer loads with an LDS destination, four
+  //      rows of 1 KiB per instruction, lane i writing bytes 16i..16i+15 of them); the lane
+  //      whose destination is chunk position c of row r loads logical chunk c ^ kswz(r),
+  //      which gives the swizzled layout of k_byte;
+  //   V: the 8 keys of stored chunk w&1 of key group w>>1, i.e. keys
+  //      16(w>>1) + 4(w&1) + {0,1,2,3,8,9,10,11}; lane l loads dims 2l and 2l+1 of each
+  //      (lanes past D/2 repeat the last pair) and transposes them into two V^T chunks.
+  // Rows past the end of the sequence are read as zeros (the buffer descriptor's extent
+  // is the sequence; their keys are masked), so no row index is clamped.
   constexpr int kKRows = kWave / kChunks;         // K rows per wavefront load
   constexpr int kKLoads = 8 / kKRows;             // K loads per lane per tile
-  static_assert(kBc == 8 * kWaves, "each wavefront stages 8 keys");
   const int wv = __builtin_amdgcn_readfirstlane(wave);
-  // K and V of this (batch, K/V head) are read through buffer descriptors (scalar base,
-  // 32-bit lane offset, scalar row offset), so that staging needs no per-lane 64-bit
-  // addresses; the descriptor's extent is exactly N rows, a hardware bound on top of
-  // the row clamping below
   const unsigned row_bytes = (unsigned)(kv_row_stride * 2);
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, (int)(row_bytes * (unsigned)nk), kBufferWord3);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vp, 0, (int)(row_bytes * (unsigned)nk), kBufferWord3);
   const int k_lane_row = lane / kChunks;
-  const unsigned k_lane_col = (unsigned)(lane % kChunks) * 16u;
-  const unsigned k_lane_off = (unsigned)k_lane_row * row_bytes + k_lane_col;
-  const unsigned v_lane_off = (unsigned)min(2 * lane, D - 2) * 2u;  // lanes past D/2 repeat
-  u32x4 kst[kKLoads];
+  unsigned k_lane_off[kKLoads];   // lane part of the K source offset of DMA u (row 8w + u kKRows + lane/kChunks)
+#pragma unroll
+  for (int u = 0; u < kKLoads; ++u)
+    k_lane_off[u] = (unsigned)(k_lane_row * row_bytes) +
+                    (unsigned)(((lane % kChunks) ^ kswz<D>(8 * wv + u * kKRows + k_lane_row)) * 16);
+  const int vlane = min(lane, D / 2 - 1);
+  const unsigned v_lane_off = (unsigned)vlane * 4u;
   unsigned vst[8];
-  auto load_k = [&](int j) __attribute__((always_inline)) {
-    const int j0 = j * kBc;
-    if (j0 + kBc <= nk) {
+  auto dma_k = [&](int j, int slot) __attribute__((always_inline)) {
 #pragma unroll
-      for (int u = 0; u < kKLoads; ++u)
-        kst[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, k_lane_off, (j0 + 8 * wv + u * kKRows) * row_bytes, 0);
-    } else {
-#pragma unroll
-      for (int u = 0; u < kKLoads; ++u) {
-        const int key = min(j0 + 8 * wv + u * kKRows + k_lane_row, nk - 1);
-        kst[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, (unsigned)key * row_bytes + k_lane_col, 0, 0);
-      }
+    for (int u = 0; u < kKLoads; ++u) {
+      const unsigned row0 = (unsigned)(j * kBc + 8 * wv + u * kKRows);
+      lds_byte* dst = lds_dma_dst(lds + slot * kTileBytes + (8 * wv + u * kKRows) * D * 2);
+      dma16(krs, dst, row0 * row_bytes + k_lane_off[u]);
     }
   };
   auto load_v = [&](int j) __attribute__((always_inline)) {
-    const int j0 = j * kBc;
-    const bool full = j0 + kBc <= nk;
+    const unsigned r0 = (unsigned)(j * kBc + 16 * (wv >> 1) + 4 * (wv & 1));
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      int key = j0 + 16 * (wv >> 1) + 4 * (wv & 1) + (r & 3) + (r >> 2) * 8;
-      if (!full) key = min(key, nk - 1);
-      vst[r] = __builtin_amdgcn_raw_buffer_load_b32(vrs, v_lane_off, key * row_bytes, 0);
-    }
+    for (int r = 0; r < 8; ++r)
+      vst[r] = __builtin_amdgcn_raw_buffer_load_b32(vrs, (r0 + (r & 3) + (r >> 2) * 8) * row_bytes + v_lane_off, 0, 0);
   };
-  auto store_k = [&](int buf) __attribute__((always_inline)) {
-    unsigned char* st = lds + buf * kStageBytes;
-#pragma unroll
-    for (int u = 0; u < kKLoads; ++u)
-      *(u32x4*)(st + k_byte<D>(8 * wv + u * kKRows + lane / kChunks, (lane % kChunks) * 8)) = kst[u];
-  };
-  auto store_v = [&](int buf) __attribute__((always_inline)) {
-    unsigned char* st = lds + buf * kStageBytes;
+  // V^T stores: store e writes, for each lane, dim 2l + ((e + bit 1 of l) & 1): then every
+  // 8 consecutive lanes write 8 different 16-byte bank groups
+  const unsigned v_sel_bit = (unsigned)((vlane >> 1) & 1);
+  auto store_v = [&](int slot) __attribute__((always_inline)) {
+    unsigned char* st = lds + kVBase + slot * kTileBytes;
     if (2 * lane < D) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const unsigned sel = e ? 0x07060302u : 0x05040100u;
+        const unsigned dd = (unsigned)e ^ v_sel_bit;
+        const unsigned sel = dd ? 0x07060302u : 0x05040100u;
         u32x4 t;
 #pragma unroll
         for (int q = 0; q < 4; ++q) t[q] = __builtin_amdgcn_perm(vst[2 * q + 1], vst[2 * q], sel);
-        *(u32x4*)(st + kTileBytes + vt_byte<D>(wv >> 1, 2 * lane + e, wv & 1)) = t;
+        *(u32x4*)(st + vt_byte<D>(wv >> 1, 2 * lane + (int)dd, wv & 1)) = t;
       }
     }
   };
 
-  // ---- per-wavefront state ----------------------------------------------------------------
+  // ---- per-wavefront state ------------------------------------------------------------
   f32x16 oacc[kDblocks];
 #pragma unroll
   for (int i = 0; i < kDblocks; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[i][e] = 0.0f;
-  f32x16 s[kKb];             // S^T of the tile between its MFMA block and its softmax block
-  u32x4 p[kKb][2];           // probabilities of the tile between its softmax and its P.V
-#pragma unroll
-  for (int kb = 0; kb < kKb; ++kb)
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) p[kb][hf] = u32x4{0u, 0u, 0u, 0u};
-  // running max, base-2 exponent units (score * c); it starts at -FLT_MAX rather than
+  f32x16 sA[kKb], sB[kKb];   // S^T of consecutive tiles alternate between these
+  u32x4 p[kKb][2];
+  // running max in base-2 exponent units (score * c); it starts at -FLT_MAX rather than
   // -inf so that a row whose keys in a tile are all masked gets exp2(-inf - m) = 0, never
   // exp2(-inf + inf)
   float m_run = -__FLT_MAX__;
   float l_run = 0.0f;        // this lane's part of the running denominator
 
-  // wavefront-uniform: key tile j has a key visible to some query of this wavefront; the
-  // tiles for which this holds are consecutive
-  auto wave_active = [&](int j) __attribute__((always_inline)) {
-    if constexpr (BAND) {
-      const int k0 = kv0 + j * kBc;
-      return j >= 0 && j < ntiles && k0 <= qw0 + 31 + a.wr && k0 + kBc - 1 >= qw0 - a.wl;
-    } else {
-      return !CAUSAL || j * kBc <= qw0 + 31;
-    }
-  };
-
-  // MFMA block of step j: O^T += V^T(j-1) P^T(j-1), then S^T(j) = K(j) Q^T. Both read slot j.
-  auto pv_part = [&](const lds_byte* st) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kk = 0; kk < 2 * kKb; ++kk) {
-#pragma unroll
-      for (int db = 0; db < kDblocks; ++db) {
-        const u32x4 va = lds_load<u32x4>(st, voff[db] + kk * (D * 32));
-        oacc[db] = Ops::mfma(va, p[kk >> 1][kk & 1], oacc[db]);
-      }
-    }
-  };
-  auto s_part = [&](const lds_byte* st) __attribute__((always_inline)) {
+  auto s_mfma = [&](f32x16 (&s)[kKb], int slot) __attribute__((always_inline)) {
+    const lds_byte* st = (const lds_byte*)lds + slot * kTileBytes;
 #pragma unroll
     for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[kb][e] = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < kKsteps; ++ks) {
+    for (int ks = 0; ks < kKsteps; ++ks)
 #pragma unroll
-      for (int kb = 0; kb < kKb; ++kb) {
-        const u32x4 ka = lds_load<u32x4>(st, koff[ks] + kb * 32 * D * 2);
-        s[kb] = Ops::mfma(ka, qreg[ks], s[kb]);
-      }
-    }
+      for (int kb = 0; kb < kKb; ++kb)
+        s[kb] = Ops::mfma(lds_load<u32x4>(st, koff[ks] + kb * 32 * D * 2), qreg[ks], s[kb]);
   };
-  // One variant only, so that the register allocator sees a single path: the first step
-  // (j = 0) multiplies the zero probabilities by the zero-filled V^T region of slot 0, and
-  // the last step (j = T) computes an S^T from stale K that nothing reads. A wavefront with
-  // no visible key in tile j-1 has none in tile j either and skips the block; under the
-  // band mask it may see keys of tile j only, and then multiplies its probabilities, still
-  // the initial zeros, by the V^T of tile j-1.
-  auto mfma_block = [&](auto buf_c, int j) __attribute__((always_inline)) {
-    constexpr int buf = decltype(buf_c)::value;
-    const lds_byte* st = (const lds_byte*)lds + buf * kStageBytes;
-    if (j <= ntiles && (wave_active(j - 1) || (BAND && wave_active(j)))) {
-      s_part(st);
-      pv_part(st);
-      // keep operand reads kLead MFMAs ahead of their use: this wavefront is the only one
-      // issuing MFMAs on its SIMD during the step, so LDS latency must be hidden inside it
-      constexpr int kOps = kDblocks * 2 * kKb + kKsteps * kKb;
-      constexpr int kLead = 8;
-      __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);   // DS reads
+  auto pv_mfma = [&](int slot) __attribute__((always_inline)) {
+    const lds_byte* st = (const lds_byte*)lds + slot * kTileBytes;   // voff holds kVBase
 #pragma unroll
-      for (int i = 0; i < kOps - kLead; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);     // one DS read
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, kLead, 0);
-    }
+    for (int kk = 0; kk < 2 * kKb; ++kk)
+#pragma unroll
+      for (int db = 0; db < kDblocks; ++db)
+        oacc[db] = Ops::mfma(lds_load<u32x4>(st, voff[db] + kk * (D * 32)), p[kk >> 1][kk & 1], oacc[db]);
   };
-
-  // softmax block of tile j: mask, running max (lazy rescale of O), exponentials, row sum,
-  // and the probabilities packed as the B operand of the next P.V
-  auto softmax_block = [&](int j) __attribute__((always_inline)) {
-    if (j >= ntiles || !wave_active(j)) return;
-    const int k0 = kv0 + j * kBc;                  // first key of the tile
-    bool need_mask = (k0 + kBc > N) || (CAUSAL && k0 + kBc - 1 > qw0);
-    if constexpr (BAND) need_mask = need_mask || k0 + kBc - 1 > qw0 + a.wr || k0 < qw0 + 31 - a.wl;
-    if (need_mask) {
+  // masks the scores of tile j where some key of the tile is invisible to some query of
+  // this wavefront (all of them for a tile the wavefront does not see at all)
+  auto mask_tile = [&](f32x16 (&s)[kKb], int j) __attribute__((always_inline)) {
+    const int k0 = kv0 + j * kBc;
+    bool need = (k0 + kBc > N) || (CAUSAL && k0 + kBc - 1 > qw0);
+    if constexpr (BAND) need = need || k0 + kBc - 1 > qw0 + a.wr || k0 < qw0 + 31 - a.wl;
+    if (need) {
 #pragma unroll
       for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
@@ -443,33 +407,15 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
           s[kb][e] = dead ? -INFINITY : s[kb][e];
         }
     }
-    // Probabilities against the running maximum m_run as it stands. Every p is at most this
-    // lane's partial sum, so while that sum is <= Ops::kPMax no p can overflow the storage
-    // type of P and no rescale is needed (exact in real arithmetic for any m_run). Otherwise
-    // (a score grew past m_run by more than log2(kPMax), or m_run is still -FLT_MAX before
-    // the first visible key, which makes the sum inf) take the tile's true maximum, rescale
-    // the accumulators and recompute.
-    f32x16 pe[kKb];
-    auto exponentials = [&]() __attribute__((always_inline)) {
-#pragma unroll
-      for (int kb = 0; kb < kKb; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) pe[kb][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], a.c, -m_run));
-      return tree_sum<kKb>(pe);
-    };
-    float lsum = exponentials();
-    if (__builtin_amdgcn_ballot_w64(!(lsum <= Ops::kPMax)) != 0) {
-      const float mx = pair_max(tree_max<kKb>(s)) * a.c;
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run = -FLT_MAX
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < kDblocks; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
-      lsum = exponentials();
-    }
+  };
+  // Probabilities of a tile against the running maximum m_run as it stands, packed as the
+  // B operand of P.V; returns this lane's sum of them. Every p is at most that sum, so while
+  // the sum is <= Ops::kPMax no p can overflow the storage type of P and no rescale is
+  // needed (exact in real arithmetic for any m_run). Otherwise a score grew past m_run by
+  // more than log2(kPMax): the step below takes the tile's maximum, rescales the
+  // accumulators and computes the probabilities again.
+  auto exponentials = [&](const f32x16 (&s)[kKb]) __attribute__((always_inline)) {
+    float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
@@ -477,70 +423,117 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           const int e = hf * 8 + e2 * 2;
-          p[kb][hf][e2] = Ops::pack2(pe[kb][e], pe[kb][e + 1]);
+          const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], a.c, -m_run));
+          const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e + 1], a.c, -m_run));
+          part[e2] += x0 + x1;
+          p[kb][hf][e2] = Ops::pack2(x0, x1);
         }
-    l_run += lsum;
+    return (part[0] + part[1]) + (part[2] + part[3]);
   };
 
-  // ---- schedule ------------------------------------------------------------------------
-  // The two halves of the workgroup (wavefronts 0-3 and 4-7, one of each per SIMD) run half
-  // a step apart, so that on every SIMD one wavefront issues MFMAs while the other
-  // computes the softmax. Step t (0 <= t < 2T+2, T key tiles) for a wavefront of half g:
-  //   u = t - g; u even: MFMA block of j = u/2 (P.V of tile j-1, S of tile j);
-  //              u odd:  softmax block of tile j = u/2;
-  // every step ends with a workgroup barrier. Slot j (LDS buffer j&1) is read at steps 2j
-  // and 2j+1; its global loads go out at the end of step 2j-3 and it is written to LDS at
-  // the end of step 2j-1, after the last reader of slot j-2 (same buffer) has finished.
-  const int half = wv >> 2;
-  load_k(0);
-  store_k(0);
-  {  // the V^T region of slot 0 (no tile -1) is zero, so step 0's P.V adds 0 * 0
-    unsigned char* vz = lds + kTileBytes;
-    for (int i = tid; i < kTileBytes / 16; i += kThreads) *(u32x4*)(vz + i * 16) = u32x4{0u, 0u, 0u, 0u};
-  }
-  // drain every outstanding load (Q included) so that no wait for Q is left inside the
-  // loop, where it would also wait for the prefetch in flight
-  __builtin_amdgcn_s_waitcnt(0);
-  if (1 < ntiles) load_k(1);
-  if (1 <= ntiles) load_v(0);
-  __syncthreads();
+  // S^T of tile j computed again from K in global memory (the rare path below: K slot j&1
+  // may already hold K(j+2) from another wavefront). The operands are the ones staged to
+  // LDS, so the scores are bit for bit the first ones, except for rows past the end of
+  // the sequence (read here as row nk-1, there as zeros), whose keys are masked.
+  auto s_global = [&](f32x16 (&s)[kKb], int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < kKb; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[kb][e] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < kKsteps; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < kKb; ++kb) {
+        const int key = min(j * kBc + kb * 32 + l32, nk - 1);
+        const u32x4 ka = __builtin_amdgcn_raw_buffer_load_b128(krs, (unsigned)key * row_bytes + (unsigned)(ks * 16 + hi * 8) * 2u, 0, 0);
+        s[kb] = Ops::mfma(ka, qreg[ks], s[kb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // raise m_run to cover the maximum of the tile's scores, rescaling O and l
+  auto rescale_to = [&](const f32x16 (&s)[kKb]) __attribute__((always_inline)) {
+    const float mx = pair_max(tree_max<kKb>(s)) * a.c;
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run = -FLT_MAX
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < kDblocks; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+  };
 
-  // the halves run separate copies of the step loop, so that inside each copy the kind of
-  // block of every step is a compile-time fact (no state is merged across branches)
-  auto step = [&](auto phase_c, auto half_c, int t) __attribute__((always_inline)) {
-    constexpr int phase = decltype(phase_c)::value;      // t % 4
-    constexpr int hf = decltype(half_c)::value;          // this wavefront's half
-    if constexpr (hf == (phase & 1)) {
-      mfma_block(ic<(phase >> 1) & 1>(), (t - hf) >> 1);
-    } else {
-      if (t - hf >= 0) softmax_block((t - hf) >> 1);
+  // One step: the DMA of K(j+2), tile j's softmax beside S(j+1)'s MFMAs, then P(j).V(j)
+  // beside the LDS stores of V(j+1) and the global loads of V(j+2), then the barrier.
+  auto step = [&](f32x16 (&sc)[kKb], f32x16 (&sn)[kKb], auto par_c, int j) __attribute__((always_inline)) {
+    constexpr int par = decltype(par_c)::value;   // j & 1
+    dma_k(j + 2, par);      // K slot j&1 was last read by S(j), before the previous barrier
+    mask_tile(sc, j);
+    // a row that has seen no visible key yet (m_run = -FLT_MAX) takes the tile's maximum
+    // before its exponentials
+    if (__builtin_amdgcn_ballot_w64(m_run == -__FLT_MAX__) != 0) rescale_to(sc);
+    s_mfma(sn, par ^ 1);
+    float lsum = exponentials(sc);
+    // operand reads run kLead ahead of their MFMA; each MFMA is followed by softmax work
+    constexpr int kLead = 4;
+    constexpr int kSOps = kKsteps * kKb;
+    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+#pragma unroll
+    for (int i = 0; i < kSOps; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < kSOps - kLead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
     }
-    // At the end of every odd step t the staged slot jn = (t+1)/2 goes to LDS and the
-    // global loads of slot jn+1 go out at once, so that they have the next two blocks to
-    // land (slot jn+1 is stored at the end of step t+2).
-    if constexpr ((phase & 1) == 1) {
-      const int jn = (t + 1) / 2;
-      constexpr int buf = phase == 1 ? 1 : 0;             // == jn & 1
-      if (jn < ntiles) store_k(buf);
-      if (jn <= ntiles) store_v(buf);
-      if (jn + 1 < ntiles) load_k(jn + 1);
-      if (jn + 1 <= ntiles) load_v(jn);
+    if (__builtin_amdgcn_ballot_w64(!(lsum <= Ops::kPMax)) != 0) {
+      // a score grew past m_run by more than log2(kPMax): the scores were consumed in
+      // place, so they are computed again, then the tile's maximum and the probabilities
+      f32x16 sr[kKb];
+      s_global(sr, j);
+      mask_tile(sr, j);
+      rescale_to(sr);
+      lsum = exponentials(sr);
     }
+    l_run += lsum;
+    pv_mfma(par);
+    store_v(par ^ 1);
+    load_v(j + 2);
+    // P.V operand reads kLead ahead, the V staging spread between the MFMAs
+    constexpr int kPOps = kDblocks * 2 * kKb;
+    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+#pragma unroll
+    for (int i = 0; i < kPOps; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < kPOps - kLead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      if (i >= 8 && i < 12) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      if (i >= 8) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    // the K DMA of this step is complete (only the 8 V loads just issued may be pending)
+    // before the barrier that publishes it
+    __builtin_amdgcn_s_waitcnt(kVmcnt8);
     __syncthreads();
   };
-  auto run = [&](auto half_c) __attribute__((always_inline)) {
-    const int nsteps = 2 * ntiles + 2;
-    for (int t = 0; t < nsteps; t += 4) {
-      step(ic<0>(), half_c, t);
-      step(ic<1>(), half_c, t + 1);
-      step(ic<2>(), half_c, t + 2);
-      step(ic<3>(), half_c, t + 3);
-    }
-  };
-  if (half == 0) run(ic<0>());
-  else run(ic<1>());
 
-  // ---- epilogue: normalise once, write O and lse ----
+  // prologue: K(0), K(1) and V(0) in LDS, V(1) in registers, S(0) computed
+  dma_k(0, 0);
+  dma_k(1, 1);
+  load_v(0);
+  store_v(0);
+  load_v(1);
+  __builtin_amdgcn_s_waitcnt(kVmcnt8);
+  __syncthreads();
+  s_mfma(sA, 0);
+  __syncthreads();   // every wavefront has read K slot 0 before K(2) replaces it
+
+  // tiles go in pairs; an odd count gets one more tile, past kv_end, whose keys are all
+  // masked for every query of the workgroup (probability 0)
+  for (int j = 0; j < ntiles; j += 2) {
+    step(sA, sB, ic<0>(), j);
+    step(sB, sA, ic<1>(), j + 1);
+  }
+
+  // ---- epilogue -----------------------------------------------------------------------
   const float l_tot = pair_sum(l_run);
   if (qi < N) {
     const float inv = 1.0f / l_tot;
@@ -562,8 +555,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
 // ---- the forward kernel for OCP e4m3 inputs ----------------------------------------------
 // The low-precision mode of "FlashAttention-3: Fast and Accurate Attention with Asynchrony
 // and Low-precision" (abstract), with one descale per tensor: q, k, v are e4m3 codes whose
-// values are multiplied by their tensor's descale. Same schedule and online softmax as the
-// 16-bit kernel, with three differences forced by gfx950's arithmetic:
+// values are multiplied by their tensor's descale. The online softmax is that of the 16-bit
+// kernel, with three differences forced by gfx950's arithmetic:
 //   * S^T = K Q^T runs on the bf16 MFMA after an exact e4m3 -> bf16 conversion (K while it
 //     is staged, Q once): the e4m3 MFMAs sum each 64-term product with about 14 bits of
 //     internal precision, which, with outlier elements, moves scores (and lse) by far more
@@ -579,6 +572,14 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_kernel(FwdArgs a) {
 // the key of accumulator e%16 of S^T block e/16 held by that lane. V^T in LDS: rows (dims)
 // of 64 bytes, byte 32hi + e holding V[kfp8(hi, e)][dim], chunks XOR-permuted by
 // (dim >> 2) & 3.
+// Schedule (ping-pong): the two halves of the workgroup (wavefronts 0-3 and 4-7, one of
+// each per SIMD) run half a step apart, so that on every SIMD one wavefront issues MFMAs
+// while the other computes the softmax. Step t (0 <= t < 2T+2, T key tiles) for a
+// wavefront of half g: u = t - g; u even: MFMA block of j = u/2 (P.V of tile j-1, S of
+// tile j); u odd: softmax block of tile j = u/2; every step ends with a workgroup barrier.
+// Slot j (LDS buffer j&1, K tile then V^T tile) is read at steps 2j and 2j+1; its global
+// loads go out at the end of step 2j-3 and it is written to LDS at the end of step 2j-1,
+// after the last reader of slot j-2 (same buffer) has finished.
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ f32x16 mfma_fp8(u32x4 a0, u32x4 a1, u32x4 b0, u32x4 b1, f32x16 c) {
@@ -619,7 +620,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
   constexpr int kKsteps = D / 16;                 // bf16 MFMA k-steps for S^T
   constexpr int kDblocks = D / 32;
   constexpr int kKb = kBc / 32;                   // 2 blocks of 32 keys
-  constexpr int kTileK = kBc * D * 2;             // bf16 K tile, same layout as the 16-bit kernel
+  constexpr int kTileK = kBc * D * 2;             // bf16 K tile in the layout of k_byte
   constexpr int kTileV = D * 64;                  // e4m3 V^T tile
   constexpr int kStageBytes = kTileK + kTileV;
   static_assert(kBc == 64, "one P.V MFMA covers the 64 keys of a tile");
@@ -869,7 +870,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
     } else {
       if (t - hf >= 0) softmax_block((t - hf) >> 1);
     }
-    if constexpr ((phase & 1) == 1) {   // store slot jn, then load slot jn+1 (see above)
+    if constexpr ((phase & 1) == 1) {   // store slot jn, then load slot jn+1 (schedule above)
       const int jn = (t + 1) / 2;
       constexpr int buf = phase == 1 ? 1 : 0;
       if (jn < ntiles) store_k(buf);
@@ -934,7 +935,7 @@ fa_status check_sizes(int B, int H, int Hkv, int N, int d, int causal, fa_dtype 
 
 template <typename Ops, int D, int MASK>
 fa_status launch(const FwdArgs& args, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<Ops, D, MASK>), dim3(args.total), dim3(kThreads), 0, stream, args);
+  hipLaunchKernelGGL((fa_fwd_overlap_kernel<Ops, D, MASK>), dim3(args.total), dim3(kThreads), 0, stream, args);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
