@@ -13,22 +13,24 @@
 //     dK_j  = scale sum_i dS_ij q_i,   dQ_i = scale sum_j dS_ij k_j
 // With grouped-query attention dK and dV of a key/value head sum over its query heads.
 //
-// gfx950 mapping (64-lane wavefronts, v_mfma_f32_32x32x16_{bf16,f16}):
-//   * dK/dV kernel: one workgroup of 4 wavefronts per (batch, K/V head, 128 keys), each
-//     wavefront owning 32 keys, whose K and V rows stay in VGPRs as MFMA B operands. It
-//     walks every query tile (64 rows) of every query head of the group: S = Q K^T and
-//     dP = dO V^T come out with one key per lane (MFMA columns), so P and dS are
-//     lane-local elementwise work, and they leave the accumulator already in the B-operand
-//     layout of dV^T += dO^T P and dK^T += Q^T dS (queries consumed in a permuted order
-//     that the transposed Q^T / dO^T tiles in LDS are written in). dK and dV accumulate
-//     in registers over all query tiles: no atomics, deterministic.
-//   * dQ kernel: one workgroup of 8 wavefronts per (batch, head, 256 queries), the
-//     forward's orientation: S^T = K Q^T and dP^T = V dO^T with one query per lane, then
-//     dQ^T += K^T dS^T with K^T staged transposed in LDS.
+// gfx950 mapping (64-lane wavefronts):
+//   * dK/dV kernel (v_mfma_f32_16x16x32): one workgroup of 8 wavefronts per (batch, K/V
+//     head, 128 keys), each wavefront owning 16 keys, whose K and V rows stay in VGPRs as
+//     MFMA B operands. It walks every query tile (64 rows) of every query head of the
+//     group, last tile first: S = Q K^T and dP = dO V^T come out with one key per lane
+//     (MFMA columns), so P and dS are lane-local elementwise work, and they leave the
+//     accumulator already in the B-operand layout of dV^T += dO^T P and dK^T += Q^T dS
+//     (queries consumed in a permuted order that the transposed Q^T / dO^T tiles in LDS
+//     are written in). dK and dV accumulate in registers over all query tiles: no atomics,
+//     deterministic.
+//   * dQ kernel (v_mfma_f32_32x32x16): one workgroup of 8 wavefronts per (batch, head, 256
+//     queries), the forward's orientation: S^T = K Q^T and dP^T = V dO^T with one query
+//     per lane, then dQ^T += K^T dS^T with K^T staged transposed in LDS.
 //   * Tiles are double-buffered in LDS; the next tile's global loads are in flight while
 //     the current one is computed. Eight wavefronts share each LDS tile, two per SIMD, so
-//     that one's MFMAs overlap the other's exponentials and LDS reads. Row-major tiles use a 16-byte-chunk XOR swizzle, the
-//     transposed tiles a chunk swizzle by the low bits of the dim.
+//     that one's MFMAs overlap the other's exponentials and LDS reads. Row-major tiles use
+//     a 16-byte-chunk XOR swizzle, the transposed tiles a chunk swizzle by the low bits of
+//     the dim.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
