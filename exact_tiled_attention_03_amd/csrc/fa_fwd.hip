@@ -475,7 +475,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
     if (__builtin_amdgcn_ballot_w64(m_run == -__FLT_MAX__) != 0) rescale_to(sc);
     s_mfma(sn, par ^ 1);
     float lsum = exponentials(sc);
-    // operand reads run kLead ahead of their MFMA; each MFMA is followed by softmax work
+    // operand reads run kLead ahead of their MFMA; each MFMA is followed by 3 VALU
+    // instructions of the softmax (measured best among 1-8), the rest after the last MFMA
     constexpr int kLead = 4;
     constexpr int kSOps = kKsteps * kKb;
     __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
@@ -483,7 +484,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
     for (int i = 0; i < kSOps; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (i < kSOps - kLead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
     }
     if (__builtin_amdgcn_ballot_w64(!(lsum <= Ops::kPMax)) != 0) {
       // a score grew past m_run by more than log2(kPMax): the scores were consumed in
