@@ -14,11 +14,12 @@
 // wavefront streaming: one wavefront per unit, four independent wavefronts per workgroup
 // (no barriers), all the query rows of the K/V head's group (group x Nq <= 64) packed as
 // the columns of S^T = K Q^T on v_mfma_f32_32x32x16, so each K/V element read from HBM
-// serves every query head that shares it. K rows are the MFMA A operand straight from
-// global memory: the d index of the contraction is permuted (lane half h of the
-// wavefront takes dims h*d/2 + 8s .. +7 in k-step s) so that each lane reads contiguous
-// 16-byte runs. V goes through a per-wavefront LDS transpose to serve as the A operand of
-// O^T += V^T P^T. The online softmax is lane-local (one query row per lane pair).
+// serves every query head that shares it. Each 32-key block is read with whole rows per
+// load instruction (fully used cache lines) into a per-wavefront LDS tile: K row-major
+// with a 16-byte-chunk swizzle, from which the S^T operands are read; V row-major, from
+// which ds_read_b64_tr_b16 reads the V^T operands of O^T += V^T P^T already transposed.
+// The next block's loads are in flight while the current one is computed. The online
+// softmax is lane-local (one query row per lane pair).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -30,6 +31,7 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -74,28 +76,47 @@ struct SkvArgs {
   float c;               // scale * log2(e)
 };
 
-// slot of key x (0..31) in the P^T operand order: accumulator row 8(e/4) + 4(l/32) + e%4
-// of lane l feeds k index 8(l/32) + e of the next MFMA
-__device__ __forceinline__ int slot_of(int x) {
-  return (x & ~15) + (((x & 7) >> 2) << 3) + (((x & 15) >> 3) << 2) + (x & 3);
+// Per-wavefront LDS tiles of one 32-key block, both row-major (key rows of 2D bytes):
+//   K: 16-byte chunk c of row r at chunk position c ^ kswz(r), so that the 32 lanes reading
+//      one chunk of 32 consecutive rows (the S^T operand) spread over the banks;
+//   V: 32-byte segment s of row r at segment s ^ (r & 3), so that the 4 rows of one
+//      transposing read (ds_read_b64_tr_b16) fall on different banks.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  if constexpr (D == 128) {
+    const int x = r & 3;
+    return ((x << 1) ^ (x << 2)) ^ ((r >> 2) & 3);
+  } else {
+    return r & 7;
+  }
 }
-// V^T scratch of one wavefront: [D][32 slots] 16-bit, 16-byte chunks XOR-swizzled by dim
-__device__ __forceinline__ int vt_byte(int dim, int slot) {
-  return dim * 64 + ((((slot >> 3) ^ dim) & 3) << 4) + ((slot & 7) << 1);
+template <int D>
+__device__ __forceinline__ int kt_byte(int r, int chunk) {
+  return r * (2 * D) + ((chunk ^ kswz<D>(r)) << 4);
 }
+template <int D>
+__device__ __forceinline__ int vt_byte(int r, int byte) {     // byte offset inside the row
+  return r * (2 * D) + (byte ^ ((r & 3) << 5));
+}
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned char lds_byte;
 
 template <typename Ops, int D, int RB, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) void splitkv_partial_kernel(SkvArgs a) {
   constexpr int kKsteps = D / 16;
   constexpr int kDblocks = D / 32;
-  constexpr int kHalf = D / 2;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[4 * D * 64];
+  constexpr int kChunks = D / 8;           // 16-byte chunks per row
+  constexpr int kRowsLd = 64 / kChunks;     // rows per wavefront load
+  constexpr int kLds = kBlk / kRowsLd;      // loads per tensor per block
+  constexpr int kTile = kBlk * D * 2;       // one 32-key tile
+  __shared__ __attribute__((aligned(16))) unsigned char lds[4 * 2 * kTile];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int unit = blockIdx.x * 4 + wave;
   if (unit >= a.units) return;             // whole wavefront; the kernel has no barriers
-  unsigned char* vt = lds + wave * (D * 64);
+  unsigned char* kt = lds + wave * (2 * kTile);   // this wavefront's K tile, then its V tile
+  unsigned char* vt = kt + kTile;
   const int s = unit % a.S;
   const int bh = unit / a.S;               // b * Hkv + hk
   const int hk = bh % a.Hkv, b = bh / a.Hkv;
@@ -115,9 +136,9 @@ __global__ __launch_bounds__(kThreads) void splitkv_partial_kernel(SkvArgs a) {
     const int rr = qvalid[rb] ? r : 0;
     const int h = hk * a.group + rr / Nq, i = rr % Nq;
     qpos[rb] = Nk - Nq + i;
-    const uint16_t* qp = (const uint16_t*)a.q + (((size_t)b * Nq + i) * a.H + h) * D + kHalf * hi;
+    const uint16_t* qp = (const uint16_t*)a.q + (((size_t)b * Nq + i) * a.H + h) * D + 8 * hi;
 #pragma unroll
-    for (int ks = 0; ks < kKsteps; ++ks) qreg[rb][ks] = *(const u32x4*)(qp + 8 * ks);
+    for (int ks = 0; ks < kKsteps; ++ks) qreg[rb][ks] = *(const u32x4*)(qp + 16 * ks);
   }
 
   f32x16 oacc[RB][kDblocks];
@@ -135,43 +156,54 @@ __global__ __launch_bounds__(kThreads) void splitkv_partial_kernel(SkvArgs a) {
   }
 
   const size_t kv_row = (size_t)a.Hkv * D;
-  const uint16_t* kbase = (const uint16_t*)a.k + (size_t)b * Nk * kv_row + (size_t)hk * D + kHalf * hi;
-  const uint16_t* vbase = (const uint16_t*)a.v + (size_t)b * Nk * kv_row + (size_t)hk * D + kHalf * hi;
-  const int vslot = slot_of(l32);
+  const uint16_t* kbase = (const uint16_t*)a.k + (size_t)b * Nk * kv_row + (size_t)hk * D;
+  const uint16_t* vbase = (const uint16_t*)a.v + (size_t)b * Nk * kv_row + (size_t)hk * D;
 
-  // K and V of one block per lane (key l32, dims kHalf*hi + 8ks .. +7); the next block's
-  // loads are issued as soon as these registers have been consumed (S^T computed, V^T
-  // written), so they are in flight during the softmax and the P.V products
-  u32x4 kn[kKsteps], vn[kKsteps];
+  // K and V of one block, whole rows per load (lane: row u*kRowsLd + lane/kChunks, chunk
+  // lane%kChunks); the next block's loads go out as soon as these registers are in LDS,
+  // so they are in flight during S^T, the softmax and the P.V products
+  const int ld_row = lane / kChunks, ld_chunk = lane % kChunks;
+  u32x4 kn[kLds], vn[kLds];
   auto load = [&](int jb) __attribute__((always_inline)) {
-    const int kr = min(jb + l32, Nk - 1);
 #pragma unroll
-    for (int ks = 0; ks < kKsteps; ++ks) {
-      kn[ks] = *(const u32x4*)(kbase + (size_t)kr * kv_row + 8 * ks);
-      vn[ks] = *(const u32x4*)(vbase + (size_t)kr * kv_row + 8 * ks);
+    for (int u = 0; u < kLds; ++u) {
+      const size_t r = (size_t)min(jb + u * kRowsLd + ld_row, Nk - 1);
+      kn[u] = *(const u32x4*)(kbase + r * kv_row + 8 * ld_chunk);
+      vn[u] = *(const u32x4*)(vbase + r * kv_row + 8 * ld_chunk);
     }
   };
   if (j_begin < j_end) load(j_begin);
 
+  // V^T operand of the P.V MFMA for k-step t2 and dim block db: for k index 8hi + i the
+  // P^T operand holds key 16t2 + 8(i/4) + 4hi + i%4, so elements 0-3 and 4-7 are 4
+  // consecutive keys each, one transposing read apiece (lane j of a 16-lane group gets
+  // dim dbase + j of 4 rows; lane 4r + c supplies row r's dims dbase + 4c .. +3)
+  const int tr_row = (lane & 15) >> 2, tr_col = 8 * (lane & 3) + 32 * ((lane >> 4) & 1);   // bytes
+  auto vt_operand = [&](int t2, int db) __attribute__((always_inline)) {
+    const int r1 = 16 * t2 + 4 * hi + tr_row, r2 = r1 + 8;
+    const s16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)((lds_byte*)vt + vt_byte<D>(r1, 64 * db + tr_col)));
+    const s16x4 x2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)((lds_byte*)vt + vt_byte<D>(r2, 64 * db + tr_col)));
+    const u32x2 w1 = __builtin_bit_cast(u32x2, x1), w2 = __builtin_bit_cast(u32x2, x2);
+    return u32x4{w1[0], w1[1], w2[0], w2[1]};
+  };
+
   for (int jb = j_begin; jb < j_end; jb += kBlk) {
-    // V^T of this block into the wavefront's scratch: lane (key l32, half hi) holds dims
-    // kHalf*hi + 8ks + t
 #pragma unroll
-    for (int ks = 0; ks < kKsteps; ++ks)
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int dim = kHalf * hi + 8 * ks + t;
-        *(uint16_t*)(vt + vt_byte(dim, vslot)) = (uint16_t)(vn[ks][t >> 1] >> (16 * (t & 1)));
-      }
+    for (int u = 0; u < kLds; ++u) {
+      const int r = u * kRowsLd + ld_row;
+      *(u32x4*)(kt + kt_byte<D>(r, ld_chunk)) = kn[u];
+      *(u32x4*)(vt + vt_byte<D>(r, 16 * ld_chunk)) = vn[u];
+    }
+    if (jb + kBlk < j_end) load(jb + kBlk);
     f32x16 st[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) st[rb][e] = 0.0f;
 #pragma unroll
-      for (int ks = 0; ks < kKsteps; ++ks) st[rb] = Ops::mfma(kn[ks], qreg[rb][ks], st[rb]);
+      for (int ks = 0; ks < kKsteps; ++ks)
+        st[rb] = Ops::mfma(*(const u32x4*)(kt + kt_byte<D>(l32, 2 * ks + hi)), qreg[rb][ks], st[rb]);
     }
-    if (jb + kBlk < j_end) load(jb + kBlk);
 
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -213,8 +245,7 @@ __global__ __launch_bounds__(kThreads) void splitkv_partial_kernel(SkvArgs a) {
       for (int t2 = 0; t2 < 2; ++t2)
 #pragma unroll
         for (int db = 0; db < kDblocks; ++db) {
-          const u32x4 vta = *(const u32x4*)(vt + vt_byte(32 * db + l32, 16 * t2 + 8 * hi));
-          oacc[rb][db] = Ops::mfma(vta, pb[t2], oacc[rb][db]);
+          oacc[rb][db] = Ops::mfma(vt_operand(t2, db), pb[t2], oacc[rb][db]);
         }
     }
   }
