@@ -28,9 +28,13 @@
 //     per lane, then dQ^T += K^T dS^T with K^T staged transposed in LDS.
 //   * Tiles are double-buffered in LDS; the next tile's global loads are in flight while
 //     the current one is computed. Eight wavefronts share each LDS tile, two per SIMD, so
-//     that one's MFMAs overlap the other's exponentials and LDS reads. Row-major tiles use
-//     a 16-byte-chunk XOR swizzle, the transposed tiles a chunk swizzle by the low bits of
-//     the dim.
+//     that one's MFMAs overlap the other's exponentials and LDS reads.
+//   * LDS bank conflicts were measured per access pattern with SQ_LDS_BANK_CONFLICT; every
+//     tile read and staging write here is conflict-free. Writes behave as 32 banks x 4 B
+//     served to 8 consecutive lanes (16-byte writes) or 16 consecutive lanes (8-byte
+//     writes) at a time, so the transposed 8-byte writes need the 16 lanes of a group to
+//     cover all 32 banks: each group holds two row groups whose slots fill the two halves
+//     of a 16-byte chunk, times eight dims spread over the eight chunk positions.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -108,22 +112,46 @@ __device__ __forceinline__ T lds_read(const unsigned char* base, int byte) {
 }
 
 // LDS layouts of an R-row x D tile of 16-bit elements:
-//   row-major: 16-byte chunk c of row r at r*2D + ((c ^ (r & 7)) * 16);
-//   transposed: element (row x, dim t) at t*2R + chunk swizzle, with rows in slot order
-//     slot(x) = 16(x/16) + 8((x%8)/4) + 4((x%16)/8) + x%4, the order in which an MFMA
-//     accumulator (rows 8(i/4) + 4(l/32) + i%4 of lane l) hands its rows to the next
-//     MFMA's k index (8(l/32) + i).
+//   row-major (dQ kernel): 16-byte chunk c of row r at r*2D + ((c ^ rswz(r)) * 16), where
+//     rswz(r) takes distinct values on rows r, r+1, r+2, r+3 and on r, r+4, r+8, r+12,
+//     which keeps the 32-row reads of the 32x32x16 A operand conflict-free;
+//   transposed: element (row x, dim t) at t*2R + 16 * ((slot/8) ^ (t/2) ^ ((t/16) % 4)) +
+//     2 * (slot%8), with rows in slot order
+//     slot(x) = 16(x/16) + 8((x%8)/4) + 4((x%16)/8) + x%4 (dQ kernel) or
+//     slot32(x) (dK/dV kernel), the order in which an MFMA accumulator (rows
+//     8(i/4) + 4(l/32) + i%4 of lane l) hands its rows to the next MFMA's k index. Reads
+//     of 16 or 32 consecutive dims at one slot and the staging writes of dims 8c + e,
+//     c = 0..7, both land on distinct banks.
+__device__ __forceinline__ int rswz(int r) {
+  const int x = r & 3;
+  return ((x << 1) ^ (x << 2)) ^ ((r >> 2) & 3);
+}
 template <int D>
 __device__ __forceinline__ int rm_byte(int r, int chunk) {
-  return r * (2 * D) + ((chunk ^ (r & 7)) << 4);
+  return r * (2 * D) + (((chunk ^ rswz(r)) & (D / 8 - 1)) << 4);
 }
 template <int R>
 __device__ __forceinline__ int tr_byte(int dim, int slot) {
   constexpr int kChunks = R / 8;
-  return dim * (2 * R) + ((((slot >> 3) ^ (dim & 7)) & (kChunks - 1)) << 4) + ((slot & 7) << 1);
+  return dim * (2 * R) + ((((slot >> 3) ^ (dim >> 1) ^ ((dim >> 4) & 3)) & (kChunks - 1)) << 4) + ((slot & 7) << 1);
 }
 __device__ __forceinline__ int slot_of(int x) {
   return (x & ~15) + (((x & 7) >> 2) << 3) + (((x & 15) >> 3) << 2) + (x & 3);
+}
+
+// Staging unit (row group g = rows 4g..4g+3, chunk c = dims 8c..8c+7) of lane sl of
+// wavefront sw within a staging group of 16 * kChunks lanes. Lanes 8k..8k+7 take eight
+// consecutive chunks of one row (a whole 128-byte line per load), lanes 8..15 of each 16
+// the row group whose slots fill the other half of the same 16-byte chunks: bit kHalfBit
+// of g is the slot function's half bit (bit 1 for slot(), bit 2 for slot32()).
+template <int kChunks, int kHalfBit>
+__device__ __forceinline__ void staging_unit(int sl, int sw, int& g, int& c) {
+  static_assert(kChunks % 8 == 0 && (kHalfBit == 1 || kHalfBit == 2), "unit mapping");
+  constexpr int kWavesPerRow = kChunks / 8;
+  c = (sl & 7) + 8 * (sw % kWavesPerRow);
+  const int h = (sl >> 3) & 1, q = sl >> 4;
+  const int low = kHalfBit == 2 ? (q | (h << 2)) : ((q & 1) | (h << 1) | ((q >> 1) << 2));
+  g = low | ((sw / kWavesPerRow) << 3);
 }
 
 // Stage loaded rows (4 consecutive rows x 8 dims per unit) into LDS, row-major and/or
@@ -193,10 +221,6 @@ template <int D>
 __device__ __forceinline__ int rm16_byte(int r, int chunk) {       // row-major, 16-byte chunks
   return r * (2 * D) + ((chunk ^ (r & (D / 8 - 1))) << 4);
 }
-template <int R>
-__device__ __forceinline__ int tr16_byte(int dim, int slot) {      // transposed, rows in slot order
-  return dim * (2 * R) + ((((slot >> 3) ^ dim) & (R / 8 - 1)) << 4) + ((slot & 7) << 1);
-}
 
 template <typename Ops, int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
@@ -250,7 +274,8 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
   // staging: the first kUnits threads stage Q, the next kUnits dO; unit = rows 4sg..4sg+3,
   // dims 8sc..8sc+7
   const int su = tid % kUnits, which = tid / kUnits;   // which: 0 Q, 1 dO, 2+ none
-  const int sg = su / kChunks, sc = su % kChunks;
+  int sg, sc;
+  staging_unit<kChunks, 2>(su & 63, su >> 6, sg, sc);
   u32x4 rows[4];
   float lse_st = 0.0f;
   // query tiles from the last one down, so that the workgroups of one K/V head (which
@@ -292,7 +317,7 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
         u32x2 w;
         w[0] = __builtin_amdgcn_perm(rows[1][e >> 1], rows[0][e >> 1], sel);
         w[1] = __builtin_amdgcn_perm(rows[3][e >> 1], rows[2][e >> 1], sel);
-        *(u32x2*)(tr + tr16_byte<kBq>(8 * sc + e, s0)) = w;
+        *(u32x2*)(tr + tr_byte<kBq>(8 * sc + e, s0)) = w;
       }
     }
     if (tid < 2 * kBq) ((float*)(base + 4 * kTile))[tid] = lse_st;
@@ -355,8 +380,8 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
       for (int dbk = 0; dbk < kDblocks; ++dbk) {
         const int dim = dbk * 16 + c, slot = qc * 32 + g * 8;
-        const u32x4 da = lds_read<u32x4>(dtr, tr16_byte<kBq>(dim, slot));
-        const u32x4 qa = lds_read<u32x4>(qtr, tr16_byte<kBq>(dim, slot));
+        const u32x4 da = lds_read<u32x4>(dtr, tr_byte<kBq>(dim, slot));
+        const u32x4 qa = lds_read<u32x4>(qtr, tr_byte<kBq>(dim, slot));
         dvT[dbk] = mfma16<Ops>(da, pb, dvT[dbk]);
         dkT[dbk] = mfma16<Ops>(qa, db, dkT[dbk]);
       }
@@ -437,7 +462,8 @@ __global__ __launch_bounds__(64 * kWavesQ) void bwd_dq_kernel(BwdArgs a) {
   const int T = (kv_end + kBk - 1) / kBk;
 
   const bool stager = tid < kUnits;
-  const int sg = tid / kChunks, sc = tid % kChunks;
+  int sg, sc;
+  staging_unit<kChunks, 1>(lane, wave, sg, sc);
   u32x4 krows[4], vrows[4];
   auto load_tile = [&](int t) __attribute__((always_inline)) {
     if (stager) {
