@@ -22,7 +22,10 @@
 //     accumulator already in the B-operand layout of dV^T += dO^T P and dK^T += Q^T dS
 //     (queries consumed in a permuted order that the transposed Q^T / dO^T tiles in LDS
 //     are written in). dK and dV accumulate in registers over all query tiles: no atomics,
-//     deterministic.
+//     deterministic. A tile runs as six software-pipelined phases (the S/dP MFMAs of its
+//     four 16-query blocks, then the dV/dK MFMAs of its two 32-query chunks): each phase's
+//     MFMAs cover the LDS reads of the next phase and the softmax of the block before, and
+//     only tiles on the causal diagonal pay for the mask.
 //   * dQ kernel (v_mfma_f32_32x32x16): one workgroup of 8 wavefronts per (batch, head, 256
 //     queries), the forward's orientation: S^T = K Q^T and dP^T = V dO^T with one query
 //     per lane, then dQ^T += K^T dS^T with K^T staged transposed in LDS.
@@ -39,6 +42,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "fa.h"
 
@@ -53,7 +57,11 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 256;          // preprocess kernel
-constexpr int kWavesKV = 8;            // dK/dV kernel: wavefronts per workgroup, 16 keys each
+// dK/dV kernel: keys per wavefront and wavefronts per workgroup. The kernel is written for
+// any multiple of 16 keys; 32 keys halve the LDS reads per MFMA but need one wavefront per
+// SIMD for their registers, and measured 11% slower than two wavefronts of 16 keys.
+constexpr int kKeysPerWaveKV = 16;
+constexpr int kWavesKV = 128 / kKeysPerWaveKV;
 constexpr int kWavesQ = 8;             // dQ kernel: wavefronts per workgroup, 32 queries each
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -224,8 +232,8 @@ __device__ __forceinline__ int rm16_byte(int r, int chunk) {       // row-major,
 
 template <typename Ops, int D, bool CAUSAL>
 __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
-  constexpr int kKeysPerWave = 16;
-  constexpr int kBk = kKeysPerWave * kWavesKV;   // keys per workgroup
+  constexpr int kKb = kKeysPerWaveKV / 16;   // 16-key blocks per wavefront
+  constexpr int kBk = kKeysPerWaveKV * kWavesKV;   // keys per workgroup
   constexpr int kBq = 64;                  // queries per tile
   constexpr int kKsteps = D / 32;          // k-steps of the 16x16x32 MFMA over d
   constexpr int kDblocks = D / 16;         // 16-dim blocks of dK^T / dV^T
@@ -233,7 +241,11 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int kBuf = 4 * kTile + 2 * kBq * 4;   // Q, dO (row-major), Q^T, dO^T, lse2, D
   constexpr int kChunks = D / 8;
   constexpr int kUnits = (kBq / 4) * kChunks;      // staging units (4 rows x 8 dims) per tensor
-  static_assert(2 * kUnits <= 64 * kWavesKV && kUnits % 64 == 0, "each half stages one tensor");
+  // either every thread stages one unit of Q and one of dO, or the first kUnits threads
+  // stage Q and the next kUnits dO
+  constexpr bool kBoth = kUnits == 64 * kWavesKV;
+  constexpr int kUpt = kBoth ? 2 : 1;
+  static_assert(kUnits % 64 == 0 && (kBoth || 2 * kUnits <= 64 * kWavesKV), "staging units fill whole wavefronts");
   __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kBuf];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -244,39 +256,41 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
   const int hk = bh % a.Hkv, b = bh / a.Hkv;
   const int N = a.N;
   const int k0 = kt * kBk;
-  const int kw0 = k0 + kKeysPerWave * wave;  // this wavefront's first key
-  const int key = kw0 + c;                   // this lane's key (MFMA column)
+  const int kw0 = k0 + kKeysPerWaveKV * wave;  // this wavefront's first key
+  // this lane's keys (MFMA columns): kw0 + 16kb + c
   const size_t q_stride = (size_t)a.H * D, kv_stride = (size_t)a.Hkv * D;
 
-  // K and V rows of the lane's key as B operands: dims 32ks + 8g .. +7
-  u32x4 kreg[kKsteps], vreg[kKsteps];
-  {
-    const int kr = min(key, N - 1);
+  // K and V rows of the lane's keys as B operands: dims 32ks + 8g .. +7
+  u32x4 kreg[kKb][kKsteps], vreg[kKb][kKsteps];
+#pragma unroll
+  for (int kb = 0; kb < kKb; ++kb) {
+    const int kr = min(kw0 + 16 * kb + c, N - 1);
     const uint16_t* kp = (const uint16_t*)a.k + ((size_t)b * N + kr) * kv_stride + (size_t)hk * D + g * 8;
     const uint16_t* vp = (const uint16_t*)a.v + ((size_t)b * N + kr) * kv_stride + (size_t)hk * D + g * 8;
 #pragma unroll
     for (int ks = 0; ks < kKsteps; ++ks) {
-      kreg[ks] = *(const u32x4*)(kp + ks * 32);
-      vreg[ks] = *(const u32x4*)(vp + ks * 32);
+      kreg[kb][ks] = *(const u32x4*)(kp + ks * 32);
+      vreg[kb][ks] = *(const u32x4*)(vp + ks * 32);
     }
   }
-  f32x4 dkT[kDblocks], dvT[kDblocks];        // C[dim][key]
+  f32x4 dkT[kKb][kDblocks], dvT[kKb][kDblocks];   // C[dim][key]
 #pragma unroll
-  for (int i = 0; i < kDblocks; ++i)
+  for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) dkT[i][e] = dvT[i][e] = 0.0f;
+    for (int i = 0; i < kDblocks; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dkT[kb][i][e] = dvT[kb][i][e] = 0.0f;
 
   const int qt0 = CAUSAL ? k0 / kBq : 0;
   const int nqt = (N + kBq - 1) / kBq;
   const int per_head = nqt - qt0;
   const int T = per_head * a.group;
 
-  // staging: the first kUnits threads stage Q, the next kUnits dO; unit = rows 4sg..4sg+3,
-  // dims 8sc..8sc+7
-  const int su = tid % kUnits, which = tid / kUnits;   // which: 0 Q, 1 dO, 2+ none
+  // staging unit = rows 4sg..4sg+3, dims 8sc..8sc+7 of Q (which 0) or dO (which 1)
+  const int su = kBoth ? tid : tid % kUnits, which = kBoth ? 0 : tid / kUnits;   // which 2+: none
   int sg, sc;
   staging_unit<kChunks, 2>(su & 63, su >> 6, sg, sc);
-  u32x4 rows[4];
+  u32x4 rows[kUpt][4];
   float lse_st = 0.0f;
   // query tiles from the last one down, so that the workgroups of one K/V head (which
   // start at different tiles under the causal mask) read the same Q/dO tile at about the
@@ -288,12 +302,16 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
   auto load_tile = [&](int t) __attribute__((always_inline)) {
     int h, q0;
     tile_coords(t, h, q0);
-    if (which < 2) {
-      const uint16_t* src = (const uint16_t*)(which == 0 ? a.q : a.dout);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = min(q0 + 4 * sg + j, N - 1);
-        rows[j] = *(const u32x4*)(src + ((size_t)b * N + r) * q_stride + (size_t)h * D + sc * 8);
+    for (int u = 0; u < kUpt; ++u) {
+      const int wh = kBoth ? u : which;
+      if (wh < 2) {
+        const uint16_t* src = (const uint16_t*)(wh == 0 ? a.q : a.dout);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = min(q0 + 4 * sg + j, N - 1);
+          rows[u][j] = *(const u32x4*)(src + ((size_t)b * N + r) * q_stride + (size_t)h * D + sc * 8);
+        }
       }
     }
     if (tid < 2 * kBq) {                     // lse (scaled to base 2) then D
@@ -305,23 +323,114 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
   };
   auto store_tile = [&](int buf) __attribute__((always_inline)) {
     unsigned char* base = lds + buf * kBuf;
-    if (which < 2) {
-      unsigned char* rm = base + which * kTile;
-      unsigned char* tr = base + (2 + which) * kTile;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) *(u32x4*)(rm + rm16_byte<D>(4 * sg + j, sc)) = rows[j];
-      const int s0 = slot32_of(4 * sg);
+    for (int u = 0; u < kUpt; ++u) {
+      const int wh = kBoth ? u : which;
+      if (wh < 2) {
+        unsigned char* rm = base + wh * kTile;
+        unsigned char* tr = base + (2 + wh) * kTile;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        u32x2 w;
-        w[0] = __builtin_amdgcn_perm(rows[1][e >> 1], rows[0][e >> 1], sel);
-        w[1] = __builtin_amdgcn_perm(rows[3][e >> 1], rows[2][e >> 1], sel);
-        *(u32x2*)(tr + tr_byte<kBq>(8 * sc + e, s0)) = w;
+        for (int j = 0; j < 4; ++j) *(u32x4*)(rm + rm16_byte<D>(4 * sg + j, sc)) = rows[u][j];
+        const int s0 = slot32_of(4 * sg);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          u32x2 w;
+          w[0] = __builtin_amdgcn_perm(rows[u][1][e >> 1], rows[u][0][e >> 1], sel);
+          w[1] = __builtin_amdgcn_perm(rows[u][3][e >> 1], rows[u][2][e >> 1], sel);
+          *(u32x2*)(tr + tr_byte<kBq>(8 * sc + e, s0)) = w;
+        }
       }
     }
     if (tid < 2 * kBq) ((float*)(base + 4 * kTile))[tid] = lse_st;
   };
+
+  // Each 64-query tile runs as six phases whose MFMAs hide the next phase's LDS reads
+  // and the previous phase's softmax arithmetic (one wavefront per SIMD, so nothing else
+  // would): S(c,h) are the S/dP MFMAs of 16-query block h of 32-query chunk c, E(c,h) its
+  // probabilities and dS, V(c) the dV/dK MFMAs of chunk c:
+  //   S(0,0) | S(0,1) E(0,0) | S(1,0) E(0,1) | S(1,1) E(1,0) | V(0) E(1,1) | V(1) staging
+  auto s_read = [&](const unsigned char* base, int qc, int half, u32x4 (&qa)[kKsteps], u32x4 (&da)[kKsteps])
+      __attribute__((always_inline)) {
+    const int r = qc * 32 + half * 16 + c;
+#pragma unroll
+    for (int ks = 0; ks < kKsteps; ++ks) {
+      qa[ks] = lds_read<u32x4>(base, rm16_byte<D>(r, 4 * ks + g));
+      da[ks] = lds_read<u32x4>(base + kTile, rm16_byte<D>(r, 4 * ks + g));
+    }
+  };
+  auto s_mfma = [&](const u32x4 (&qa)[kKsteps], const u32x4 (&da)[kKsteps], f32x4 (&sacc)[kKb], f32x4 (&dpacc)[kKb])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb = 0; kb < kKb; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sacc[kb][e] = dpacc[kb][e] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < kKsteps; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < kKb; ++kb) {
+        sacc[kb] = mfma16<Ops>(qa[ks], kreg[kb][ks], sacc[kb]);
+        dpacc[kb] = mfma16<Ops>(da[ks], vreg[kb][ks], dpacc[kb]);
+      }
+  };
+  // P and dS of one 16-query block into k-slots 8g + 4*half + i of the chunk's B operands.
+  // Only the causal mask is applied: P and dS of a key past the end reach nothing but that
+  // key's own dK / dV rows, which are never stored, and query rows past the end have
+  // lse = +inf, so P = dS = 0 there.
+  // lse (base 2) and D of the lane's four query rows of a 16-query block
+  auto stats_read = [&](const unsigned char* base, int qc, int half, float4& l4, float4& d4) __attribute__((always_inline)) {
+    const float* lse2 = (const float*)(base + 4 * kTile);
+    const int q4 = qc * 32 + half * 16 + 4 * g;
+    l4 = *(const float4*)(lse2 + q4);
+    d4 = *(const float4*)(lse2 + kBq + q4);
+  };
+  auto softmax = [&](auto masked_c, int q0, int qc, int half, const float4& l4, const float4& d4,
+                     const f32x4 (&sacc)[kKb], const f32x4 (&dpacc)[kKb], u32x4 (&pb)[kKb], u32x4 (&db)[kKb])
+      __attribute__((always_inline)) {
+    constexpr bool kMasked = decltype(masked_c)::value;
+    // accumulator i: query row qc*32 + half*16 + 4g + i, key column c of block kb
+    const int q4 = qc * 32 + half * 16 + 4 * g;
+    const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+    const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+    for (int kb = 0; kb < kKb; ++kb) {
+      const int past = kw0 + 16 * kb + c - (q0 + q4);   // key - query of accumulator 0
+      float pv[4], dsv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], a.c, -lv[i]));
+        if (kMasked && past > i) p = 0.0f;
+        pv[i] = p;
+        dsv[i] = p * (dpacc[kb][i] - dv4[i]);
+      }
+      pb[kb][2 * half] = Ops::pack2(pv[0], pv[1]);
+      pb[kb][2 * half + 1] = Ops::pack2(pv[2], pv[3]);
+      db[kb][2 * half] = Ops::pack2(dsv[0], dsv[1]);
+      db[kb][2 * half + 1] = Ops::pack2(dsv[2], dsv[3]);
+    }
+  };
+  // A operands of dV^T += dO^T P and dK^T += Q^T dS: dim 16 dbk + c, slots qc*32 + 8g .. +7
+  auto v_read = [&](const unsigned char* base, int qc, int lo, int hi, u32x4 (&da)[kDblocks], u32x4 (&qa)[kDblocks])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int dbk = lo; dbk < hi; ++dbk) {
+      const int dim = dbk * 16 + c, slot = qc * 32 + g * 8;
+      da[dbk] = lds_read<u32x4>(base + 3 * kTile, tr_byte<kBq>(dim, slot));
+      qa[dbk] = lds_read<u32x4>(base + 2 * kTile, tr_byte<kBq>(dim, slot));
+    }
+  };
+  auto v_mfma = [&](const u32x4 (&da)[kDblocks], const u32x4 (&qa)[kDblocks], const u32x4 (&pb)[kKb], const u32x4 (&db)[kKb])
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int dbk = 0; dbk < kDblocks; ++dbk)
+#pragma unroll
+      for (int kb = 0; kb < kKb; ++kb) {
+        dvT[kb][dbk] = mfma16<Ops>(da[dbk], pb[kb], dvT[kb][dbk]);
+        dkT[kb][dbk] = mfma16<Ops>(qa[dbk], db[kb], dkT[kb][dbk]);
+      }
+  };
+  constexpr int kSM = 2 * kKsteps * kKb;     // MFMAs of an S phase
+  constexpr int kVM = 2 * kDblocks * kKb;    // MFMAs of a V phase
 
   load_tile(0);
   store_tile(0);
@@ -331,78 +440,119 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
     if (t + 1 < T) load_tile(t + 1);
     int h, q0;
     tile_coords(t, h, q0);
+    (void)h;
     const unsigned char* base = lds + (t & 1) * kBuf;
-    const unsigned char* qrm = base;
-    const unsigned char* drm = base + kTile;
-    const unsigned char* qtr = base + 2 * kTile;
-    const unsigned char* dtr = base + 3 * kTile;
-    const float* lse2 = (const float*)(base + 4 * kTile);
-    const float* dlt = lse2 + kBq;
+    auto tile_body = [&](auto masked_c) __attribute__((always_inline)) {
+      u32x4 sq0[kKsteps], sd0[kKsteps], sq1[kKsteps], sd1[kKsteps];
+      u32x4 va0[kDblocks], vb0[kDblocks], va1[kDblocks], vb1[kDblocks];
+      f32x4 sa0[kKb], sp0[kKb], sa1[kKb], sp1[kKb];
+      u32x4 pb0[kKb], db0[kKb], pb1[kKb], db1[kKb];
+      float4 l0, d0, l1, d1;                 // statistics of the next two softmax blocks
+      constexpr int kHalfD = kDblocks / 2;
+      // S(0,0), then E(0,0)'s statistics and S(0,1)'s reads in its second half
+      s_read(base, 0, 0, sq0, sd0);
+      s_mfma(sq0, sd0, sa0, sp0);
+      stats_read(base, 0, 0, l0, d0);
+      s_read(base, 0, 1, sq1, sd1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kKsteps, 0);
 #pragma unroll
-    for (int qc = 0; qc < kBq / 32; ++qc) {  // 32-query chunks
-      const int qc0 = q0 + qc * 32;
-      if (CAUSAL && kw0 > qc0 + 31) continue;
-      u32x4 pb, db;                          // P and dS of the chunk as B operands
-#pragma unroll
-      for (int half = 0; half < 2; ++half) { // 16-query blocks of the chunk
-        const int r = qc * 32 + half * 16 + c;
-        f32x4 sacc = {0.0f, 0.0f, 0.0f, 0.0f}, dpacc = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int ks = 0; ks < kKsteps; ++ks) {
-          const u32x4 qa = lds_read<u32x4>(qrm, rm16_byte<D>(r, 4 * ks + g));
-          const u32x4 da = lds_read<u32x4>(drm, rm16_byte<D>(r, 4 * ks + g));
-          sacc = mfma16<Ops>(qa, kreg[ks], sacc);
-          dpacc = mfma16<Ops>(da, vreg[ks], dpacc);
-        }
-        // accumulator i: query row qc*32 + half*16 + 4g + i, key column c
-        const int q4 = qc * 32 + half * 16 + 4 * g;
-        const float4 l4 = *(const float4*)(lse2 + q4);
-        const float4 d4 = *(const float4*)(dlt + q4);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-        const bool need_mask = (CAUSAL && kw0 + kKeysPerWave - 1 > q0 + q4) || key >= N;
-        float pv[4], dsv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[i], a.c, -lv[i]));
-          if (need_mask && ((CAUSAL && key > q0 + q4 + i) || key >= N)) p = 0.0f;
-          pv[i] = p;
-          dsv[i] = p * (dpacc[i] - dv4[i]);
-        }
-        // k-slots 8g + 4*half + i of the chunk's B operand
-        pb[2 * half] = Ops::pack2(pv[0], pv[1]);
-        pb[2 * half + 1] = Ops::pack2(pv[2], pv[3]);
-        db[2 * half] = Ops::pack2(dsv[0], dsv[1]);
-        db[2 * half + 1] = Ops::pack2(dsv[2], dsv[3]);
+      for (int i = 0; i < kSM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i == kSM / 2 - 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        if (i >= kSM / 2) __builtin_amdgcn_sched_group_barrier(0x100, 2 * kKsteps / (kSM / 2), 0);
       }
-      // dV^T += dO^T P, dK^T += Q^T dS: A from the transposed tiles, dim 16 dbk + c,
-      // slots qc*32 + 8g .. +7
+      __builtin_amdgcn_sched_barrier(0);
+      // S(0,1) | E(0,0) | E(0,1)'s statistics, reads of S(1,0)
+      s_mfma(sq1, sd1, sa1, sp1);
+      softmax(masked_c, q0, 0, 0, l0, d0, sa0, sp0, pb0, db0);
+      stats_read(base, 0, 1, l1, d1);
+      s_read(base, 1, 0, sq0, sd0);
 #pragma unroll
-      for (int dbk = 0; dbk < kDblocks; ++dbk) {
-        const int dim = dbk * 16 + c, slot = qc * 32 + g * 8;
-        const u32x4 da = lds_read<u32x4>(dtr, tr_byte<kBq>(dim, slot));
-        const u32x4 qa = lds_read<u32x4>(qtr, tr_byte<kBq>(dim, slot));
-        dvT[dbk] = mfma16<Ops>(da, pb, dvT[dbk]);
-        dkT[dbk] = mfma16<Ops>(qa, db, dkT[dbk]);
+      for (int i = 0; i < kSM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i == kSM / 2 - 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        if (i >= kSM / 2) __builtin_amdgcn_sched_group_barrier(0x100, 2 * kKsteps / (kSM / 2), 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      // S(1,0) | E(0,1) | E(1,0)'s statistics, reads of S(1,1)
+      s_mfma(sq0, sd0, sa0, sp0);
+      softmax(masked_c, q0, 0, 1, l1, d1, sa1, sp1, pb0, db0);
+      stats_read(base, 1, 0, l0, d0);
+      s_read(base, 1, 1, sq1, sd1);
+#pragma unroll
+      for (int i = 0; i < kSM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i == kSM / 2 - 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        if (i >= kSM / 2) __builtin_amdgcn_sched_group_barrier(0x100, 2 * kKsteps / (kSM / 2), 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // S(1,1) | E(1,0) | E(1,1)'s statistics, reads of the first half of V(0)
+      s_mfma(sq1, sd1, sa1, sp1);
+      softmax(masked_c, q0, 1, 0, l0, d0, sa0, sp0, pb1, db1);
+      stats_read(base, 1, 1, l1, d1);
+      v_read(base, 0, 0, kHalfD, va0, vb0);
+#pragma unroll
+      for (int i = 0; i < kSM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i == kSM / 2 - 1) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        if (i >= kSM / 2) __builtin_amdgcn_sched_group_barrier(0x100, 2 * kHalfD / (kSM / 2), 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // V(0) | E(1,1) | the second half of V(0)'s reads, then the first half of V(1)'s
+      v_read(base, 0, kHalfD, kDblocks, va0, vb0);
+      v_mfma(va0, vb0, pb0, db0);
+      softmax(masked_c, q0, 1, 1, l1, d1, sa1, sp1, pb1, db1);
+      v_read(base, 1, 0, kHalfD, va1, vb1);
+#pragma unroll
+      for (int i = 0; i < kVM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < 2 * kHalfD || i >= kVM / 2) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // V(1) | the second half of its reads | staging of the next tile
+      v_read(base, 1, kHalfD, kDblocks, va1, vb1);
+      v_mfma(va1, vb1, pb1, db1);
+      store_tile((t + 1) & 1);   // after the last tile: an unused buffer
+#pragma unroll
+      for (int i = 0; i < kVM; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < 2 * kHalfD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (!CAUSAL || kw0 + kKeysPerWaveKV - 1 <= q0) {
+      tile_body(std::false_type{});          // every key at or before every query of the tile
+    } else if (kw0 <= q0 + kBq - 1) {
+      tile_body(std::true_type{});
+    } else {
+      store_tile((t + 1) & 1);               // all queries precede the keys: nothing to add
     }
-    if (t + 1 < T) store_tile((t + 1) & 1);
     __syncthreads();
   }
 
-  // epilogue: lane holds dims 16dbk + 4g + 0..3 of its key
-  if (key < N) {
-    const size_t off = ((size_t)b * N + key) * kv_stride + (size_t)hk * D;
+  // epilogue: lane holds dims 16dbk + 4g + 0..3 of its keys
 #pragma unroll
-    for (int dbk = 0; dbk < kDblocks; ++dbk) {
-      const int dim = dbk * 16 + 4 * g;
-      u32x2 wk, wv;
-      wk[0] = Ops::pack2(dkT[dbk][0] * a.scale, dkT[dbk][1] * a.scale);
-      wk[1] = Ops::pack2(dkT[dbk][2] * a.scale, dkT[dbk][3] * a.scale);
-      wv[0] = Ops::pack2(dvT[dbk][0], dvT[dbk][1]);
-      wv[1] = Ops::pack2(dvT[dbk][2], dvT[dbk][3]);
-      *(u32x2*)((uint16_t*)a.dk + off + dim) = wk;
-      *(u32x2*)((uint16_t*)a.dv + off + dim) = wv;
+  for (int kb = 0; kb < kKb; ++kb) {
+    const int key = kw0 + 16 * kb + c;
+    if (key < N) {
+      const size_t off = ((size_t)b * N + key) * kv_stride + (size_t)hk * D;
+#pragma unroll
+      for (int dbk = 0; dbk < kDblocks; ++dbk) {
+        const int dim = dbk * 16 + 4 * g;
+        u32x2 wk, wv;
+        wk[0] = Ops::pack2(dkT[kb][dbk][0] * a.scale, dkT[kb][dbk][1] * a.scale);
+        wk[1] = Ops::pack2(dkT[kb][dbk][2] * a.scale, dkT[kb][dbk][3] * a.scale);
+        wv[0] = Ops::pack2(dvT[kb][dbk][0], dvT[kb][dbk][1]);
+        wv[1] = Ops::pack2(dvT[kb][dbk][2], dvT[kb][dbk][3]);
+        *(u32x2*)((uint16_t*)a.dk + off + dim) = wk;
+        *(u32x2*)((uint16_t*)a.dv + off + dim) = wv;
+      }
     }
   }
 }
@@ -567,7 +717,7 @@ fa_status launch_bwd(BwdArgs args, hipStream_t s) {
   hipLaunchKernelGGL((bwd_delta_kernel<Ops, D>), dim3((rows + per_block - 1) / per_block), dim3(kThreads), 0, s, args);
   if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
   BwdArgs kv = args;
-  kv.tiles = (args.N + 16 * kWavesKV - 1) / (16 * kWavesKV);
+  kv.tiles = (args.N + kKeysPerWaveKV * kWavesKV - 1) / (kKeysPerWaveKV * kWavesKV);
   kv.total = kv.tiles * args.Hkv * args.B;
   hipLaunchKernelGGL((bwd_dkdv_kernel<Ops, D, CAUSAL>), dim3(kv.total), dim3(64 * kWavesKV), 0, s, kv);
   if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
