@@ -162,23 +162,37 @@ __device__ __forceinline__ void staging_unit(int sl, int sw, int& g, int& c) {
   g = low | ((sw / kWavesPerRow) << 3);
 }
 
+// Per-lane bases of the staging writes of unit (g, c): since rswz(4g + j) =
+// rswz(j) ^ (g % 4) and the transposed swizzle of dim 8c + e is that of 8c XOR e/2, every
+// write is one base XOR a constant plus an immediate:
+//   rm_byte(4g + j, c)      = (rm_stage_base ^ 16 rswz(j)) + 2D j
+//   tr_byte(8c + e, slot_of(4g)) = (tr_stage_base ^ 16 (e/2)) + 2R e
+template <int D>
+__device__ __forceinline__ int rm_stage_base(int g, int c) {
+  return 4 * g * (2 * D) + (((c ^ (g & 3)) & (D / 8 - 1)) << 4);
+}
+template <int R>
+__device__ __forceinline__ int tr_stage_base(int g, int c) {
+  const int s0 = slot_of(4 * g);
+  return 8 * c * (2 * R) + ((((s0 >> 3) ^ (4 * (c & 1)) ^ ((c >> 1) & 3)) & (R / 8 - 1)) << 4) + ((s0 & 7) << 1);
+}
+
 // Stage loaded rows (4 consecutive rows x 8 dims per unit) into LDS, row-major and/or
-// transposed. rows[j] holds dims 8c..8c+7 of row 4g + j.
+// transposed, from the unit's write bases. rows[j] holds dims 8c..8c+7 of row 4g + j.
 template <int D, int R, bool ROWMAJOR, bool TRANSPOSED>
-__device__ __forceinline__ void stage_rows(unsigned char* rm, unsigned char* tr, int g, int c, const u32x4 (&rows)[4]) {
+__device__ __forceinline__ void stage_rows(unsigned char* rm, unsigned char* tr, int rmw, int trw, const u32x4 (&rows)[4]) {
   if constexpr (ROWMAJOR) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *(u32x4*)(rm + rm_byte<D>(4 * g + j, c)) = rows[j];
+    for (int j = 0; j < 4; ++j) *(u32x4*)(rm + ((rmw ^ ((rswz(j) & (D / 8 - 1)) << 4)) + j * (2 * D))) = rows[j];
   }
   if constexpr (TRANSPOSED) {
-    const int s0 = slot_of(4 * g);                        // rows 4g..4g+3 take slots s0..s0+3
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
       u32x2 w;
       w[0] = __builtin_amdgcn_perm(rows[1][e >> 1], rows[0][e >> 1], sel);
       w[1] = __builtin_amdgcn_perm(rows[3][e >> 1], rows[2][e >> 1], sel);
-      *(u32x2*)(tr + tr_byte<R>(8 * c + e, s0)) = w;
+      *(u32x2*)(tr + ((trw ^ ((e >> 1) << 4)) + e * (2 * R))) = w;
     }
   }
 }
@@ -626,11 +640,15 @@ __global__ __launch_bounds__(64 * kWavesQ) void bwd_dq_kernel(BwdArgs a) {
       }
     }
   };
+  const int rmw0 = rm_stage_base<D>(sg, sc), trw0 = tr_stage_base<kBk>(sg, sc);
   auto store_tile = [&](int buf) __attribute__((always_inline)) {
     unsigned char* base = lds + buf * kBuf;
     if (stager) {
-      stage_rows<D, kBk, true, true>(base, base + 2 * kTile, sg, sc, krows);
-      stage_rows<D, kBk, true, false>(base + kTile, nullptr, sg, sc, vrows);
+      // opaque copies: the write offsets are formed per call, not held across the loop
+      int rmw = rmw0, trw = trw0;
+      asm volatile("" : "+v"(rmw), "+v"(trw));
+      stage_rows<D, kBk, true, true>(base, base + 2 * kTile, rmw, trw, krows);
+      stage_rows<D, kBk, true, false>(base + kTile, nullptr, rmw, trw, vrows);
     }
   };
 
@@ -638,58 +656,139 @@ __global__ __launch_bounds__(64 * kWavesQ) void bwd_dq_kernel(BwdArgs a) {
   store_tile(0);
   __syncthreads();
 
-  for (int t = 0; t < T; ++t) {
-    if (t + 1 < T) load_tile(t + 1);
-    const unsigned char* base = lds + (t & 1) * kBuf;
-    const unsigned char* krm = base;
-    const unsigned char* vrm = base + kTile;
-    const unsigned char* ktr = base + 2 * kTile;
-    const int j0 = t * kBk;
-    const bool active = !CAUSAL || j0 <= qw0 + 31;
-    if (active) {
-      u32x4 db[kKb][2];                      // dS^T as B operands: [key block][k-step]
+  // LDS read offsets. The swizzles are XORs on bits that the buffer and block offsets leave
+  // clear, so every read is one per-lane base XOR a constant, plus an immediate:
+  //   rm_byte(32kb + l32, 2ks + hi)            = (rm_lane ^ 32ks) + 32kb * 2D
+  //   tr_byte(32dbk + l32, 32kb + 16t2 + 8hi) = (tr_lane ^ 16(4kb ^ 2(t2 ^ dbk%2))) + 4096dbk
+  const int rm_lane = l32 * (2 * D) + (((hi ^ rswz(l32)) & (kChunks - 1)) << 4);
+  const int tr_lane = l32 * (2 * kBk) + (((hi ^ ((l32 >> 1) & 7) ^ (l32 >> 4)) & 7) << 4);
+  // S^T and dP^T of a 32-key block, then P and dS^T of it as B operands of dQ^T += K^T dS^T
+  auto s_mfma = [&](int rmb, int kb, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < kKb; ++kb) {
-        f32x16 s, dp;
+    for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < kKsteps; ++ks) {
-          const int r = kb * 32 + l32;
-          const u32x4 ka = lds_read<u32x4>(krm, rm_byte<D>(r, 2 * ks + hi));
-          const u32x4 va = lds_read<u32x4>(vrm, rm_byte<D>(r, 2 * ks + hi));
-          s = Ops::mfma(ka, qreg[ks], s);
-          dp = Ops::mfma(va, dreg[ks], dp);
-        }
-        const bool need_mask = (j0 + kBk > N) || (CAUSAL && j0 + kBk - 1 > qw0);
-        float dsv[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], a.c, -lse2));
-          if (need_mask) {
-            const int kj = j0 + kb * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
-            if (kj >= N || (CAUSAL && kj > qi)) p = 0.0f;
-          }
-          dsv[e] = p * (dp[e] - dlt);
-        }
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) db[kb][t2][w] = Ops::pack2(dsv[8 * t2 + 2 * w], dsv[8 * t2 + 2 * w + 1]);
-      }
-      // dQ^T += K^T dS^T: A = K^T (dim 32 dbk + l32, slots kb*32 + 16 t2 + 8 hi .. +7)
-#pragma unroll
-      for (int kb = 0; kb < kKb; ++kb)
-#pragma unroll
-        for (int t2 = 0; t2 < 2; ++t2)
-#pragma unroll
-          for (int dbk = 0; dbk < kDblocks; ++dbk) {
-            const u32x4 ka = lds_read<u32x4>(ktr, tr_byte<kBk>(dbk * 32 + l32, kb * 32 + t2 * 16 + hi * 8));
-            dqT[dbk] = Ops::mfma(ka, db[kb][t2], dqT[dbk]);
-          }
+    for (int ks = 0; ks < kKsteps; ++ks) {
+      const int off = (rmb ^ (ks << 5)) + kb * 32 * (2 * D);
+      const u32x4 ka = lds_read<u32x4>(lds, off);
+      const u32x4 va = lds_read<u32x4>(lds + kTile, off);
+      s = Ops::mfma(ka, qreg[ks], s);
+      dp = Ops::mfma(va, dreg[ks], dp);
     }
-    if (t + 1 < T) store_tile((t + 1) & 1);
-    __syncthreads();
+  };
+  // Masks apply only where a key is past the end or (causal) after the lane's query.
+  const int key_last = CAUSAL ? min(qi, N - 1) : N - 1;
+  auto softmax = [&](auto masked_c, int j0, int kb, const f32x16& s, const f32x16& dp, u32x4 (&db)[2])
+      __attribute__((always_inline)) {
+    constexpr bool kMasked = decltype(masked_c)::value;
+    // accumulator e holds key j0 + 32kb + 4hi + 8(e/4) + e%4, visible up to key_last
+    const int thr = key_last - (j0 + kb * 32 + 4 * hi);
+    float dsv[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[e], a.c, -lse2));
+      if (kMasked && 8 * (e >> 2) + (e & 3) > thr) p = 0.0f;
+      dsv[e] = p * (dp[e] - dlt);
+    }
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) db[t2][w] = Ops::pack2(dsv[8 * t2 + 2 * w], dsv[8 * t2 + 2 * w + 1]);
+  };
+  // dQ^T += K^T dS^T: A = K^T (dim 32 dbk + l32, slots kb*32 + 16 t2 + 8 hi .. +7)
+  auto q_mfma = [&](int trb, int kb, const u32x4 (&db)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2)
+#pragma unroll
+      for (int dbk = 0; dbk < kDblocks; ++dbk) {
+        const int off = (trb ^ ((4 * kb ^ 2 * (t2 ^ (dbk & 1))) << 4)) + dbk * 32 * (2 * kBk);
+        const u32x4 ka = lds_read<u32x4>(lds + 2 * kTile, off);
+        dqT[dbk] = Ops::mfma(ka, db[t2], dqT[dbk]);
+      }
+  };
+  constexpr int kSM = 2 * kKsteps;           // MFMAs of an S phase, one LDS read each
+  constexpr int kQM = 2 * kDblocks;          // MFMAs of a dQ phase, one LDS read each
+  constexpr int kLead = 4;                   // operand reads ahead of their MFMA
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  // S(0) E(0) | S(1) | dQ(0) E(1) | dQ(1) staging, two 32-key blocks per tile (the first
+  // softmax overlaps the other wavefront of the SIMD: overlapping it with S(1) would hold
+  // both blocks' accumulators)
+  auto tile_body = [&](int t, auto masked_c) __attribute__((always_inline)) {
+    if (t + 1 < T) load_tile(t + 1);
+    // the tile's per-lane read bases, opaque to the compiler so that the offsets derived
+    // from them are formed per tile rather than held in registers across the loop
+    int rmb = (t & 1) * kBuf + rm_lane, trb = (t & 1) * kBuf + tr_lane;
+    asm volatile("" : "+v"(rmb), "+v"(trb));
+    const int j0 = t * kBk;
+    f32x16 s0, dp0, s1, dp1;
+    u32x4 db0[2], db1[2];
+    s_mfma(rmb, 0, s0, dp0);
+    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+#pragma unroll
+    for (int i = 0; i < kSM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < kSM - kLead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    softmax(masked_c, j0, 0, s0, dp0, db0);
+    __builtin_amdgcn_sched_barrier(0);
+    s_mfma(rmb, 1, s1, dp1);
+    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+#pragma unroll
+    for (int i = 0; i < kSM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < kSM - kLead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    q_mfma(trb, 0, db0);
+    softmax(masked_c, j0, 1, s1, dp1, db1);
+    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+#pragma unroll
+    for (int i = 0; i < kQM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < kQM - kLead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    q_mfma(trb, 1, db1);
+    store_tile((t + 1) & 1);   // after the last tile: an unused buffer
+    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+#pragma unroll
+    for (int i = 0; i < kQM; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < kQM - kLead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  if (!CAUSAL) {
+    // every tile but a ragged last one has all of its keys in range
+    const int T_full = N / kBk;
+    for (int t = 0; t < T_full; ++t) {
+      tile_body(t, std::false_type{});
+      __syncthreads();
+    }
+    for (int t = T_full; t < T; ++t) {
+      tile_body(t, std::true_type{});
+      __syncthreads();
+    }
+  } else {
+    for (int t = 0; t < T; ++t) {
+      const int j0 = t * kBk;
+      if (j0 + kBk <= N && j0 + kBk - 1 <= qw0) {      // no key masked
+        tile_body(t, std::false_type{});
+      } else if (j0 <= qw0 + 31) {                    // some key at or before a query
+        tile_body(t, std::true_type{});
+      } else {
+        if (t + 1 < T) load_tile(t + 1);
+        store_tile((t + 1) & 1);
+      }
+      __syncthreads();
+    }
   }
 
   if (qi < N) {
