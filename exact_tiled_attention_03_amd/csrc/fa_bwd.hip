@@ -335,27 +335,36 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
       else lse_st = r < N ? a.delta[off] : 0.0f;
     }
   };
+  // staging-write bases: rm16_byte(4sg + j, sc) = (rm_w0 ^ 16j) + 2D j and
+  // tr_byte(8sc + e, slot32(4sg)) = (tr_w0 ^ 16(e/2)) + 2 kBq e
+  const int rm_w0 = 4 * sg * (2 * D) + (((sc ^ (4 * (sg & 3))) & (kChunks - 1)) << 4);
+  const int tr_w0 = [&] {
+    const int s0 = slot32_of(4 * sg);
+    return 8 * sc * (2 * kBq) + ((((s0 >> 3) ^ (4 * (sc & 1)) ^ ((sc >> 1) & 3)) & 7) << 4) + ((s0 & 7) << 1);
+  }();
   auto store_tile = [&](int buf) __attribute__((always_inline)) {
-    unsigned char* base = lds + buf * kBuf;
+    // opaque per call: the write offsets are formed here, not held across the loop
+    int rmw = buf * kBuf + rm_w0, trw = buf * kBuf + tr_w0;
+    asm volatile("" : "+v"(rmw), "+v"(trw));
 #pragma unroll
     for (int u = 0; u < kUpt; ++u) {
       const int wh = kBoth ? u : which;
       if (wh < 2) {
-        unsigned char* rm = base + wh * kTile;
-        unsigned char* tr = base + (2 + wh) * kTile;
+        unsigned char* rm = lds + wh * kTile;
+        unsigned char* tr = lds + (2 + wh) * kTile;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) *(u32x4*)(rm + rm16_byte<D>(4 * sg + j, sc)) = rows[u][j];
-        const int s0 = slot32_of(4 * sg);
+        for (int j = 0; j < 4; ++j) *(u32x4*)(rm + ((rmw ^ (j << 4)) + j * (2 * D))) = rows[u][j];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
           u32x2 w;
           w[0] = __builtin_amdgcn_perm(rows[u][1][e >> 1], rows[u][0][e >> 1], sel);
           w[1] = __builtin_amdgcn_perm(rows[u][3][e >> 1], rows[u][2][e >> 1], sel);
-          *(u32x2*)(tr + tr_byte<kBq>(8 * sc + e, s0)) = w;
+          *(u32x2*)(tr + ((trw ^ ((e >> 1) << 4)) + e * (2 * kBq))) = w;
         }
       }
     }
+    unsigned char* base = lds + buf * kBuf;
     if (tid < 2 * kBq) ((float*)(base + 4 * kTile))[tid] = lse_st;
   };
 
@@ -364,13 +373,19 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
   // would): S(c,h) are the S/dP MFMAs of 16-query block h of 32-query chunk c, E(c,h) its
   // probabilities and dS, V(c) the dV/dK MFMAs of chunk c:
   //   S(0,0) | S(0,1) E(0,0) | S(1,0) E(0,1) | S(1,1) E(1,0) | V(0) E(1,1) | V(1) staging
-  auto s_read = [&](const unsigned char* base, int qc, int half, u32x4 (&qa)[kKsteps], u32x4 (&da)[kKsteps])
+  // Read bases (a tile's buffer offset plus these, formed per tile): the swizzles are XORs
+  // on bits that the block offsets leave clear, so
+  //   rm16_byte(32qc + 16half + c, 4ks + g)  = (s_lane ^ 64ks) + 2D (32qc + 16half)
+  //   tr_byte(16dbk + c, 32qc + 8g)          = (v_lane ^ 16(4qc ^ dbk%4)) + 2 kBq 16dbk
+  const int s_lane = c * (2 * D) + (((g ^ c) & (kChunks - 1)) << 4);
+  const int v_lane = c * (2 * kBq) + (((g ^ (c >> 1)) & 7) << 4);
+  auto s_read = [&](int sb, int qc, int half, u32x4 (&qa)[kKsteps], u32x4 (&da)[kKsteps])
       __attribute__((always_inline)) {
-    const int r = qc * 32 + half * 16 + c;
 #pragma unroll
     for (int ks = 0; ks < kKsteps; ++ks) {
-      qa[ks] = lds_read<u32x4>(base, rm16_byte<D>(r, 4 * ks + g));
-      da[ks] = lds_read<u32x4>(base + kTile, rm16_byte<D>(r, 4 * ks + g));
+      const int off = (sb ^ (ks << 6)) + (qc * 32 + half * 16) * (2 * D);
+      qa[ks] = lds_read<u32x4>(lds, off);
+      da[ks] = lds_read<u32x4>(lds + kTile, off);
     }
   };
   auto s_mfma = [&](const u32x4 (&qa)[kKsteps], const u32x4 (&da)[kKsteps], f32x4 (&sacc)[kKb], f32x4 (&dpacc)[kKb])
@@ -424,13 +439,13 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
   // A operands of dV^T += dO^T P and dK^T += Q^T dS: dim 16 dbk + c, slots qc*32 + 8g .. +7
-  auto v_read = [&](const unsigned char* base, int qc, int lo, int hi, u32x4 (&da)[kDblocks], u32x4 (&qa)[kDblocks])
+  auto v_read = [&](int vb, int qc, int lo, int hi, u32x4 (&da)[kDblocks], u32x4 (&qa)[kDblocks])
       __attribute__((always_inline)) {
 #pragma unroll
     for (int dbk = lo; dbk < hi; ++dbk) {
-      const int dim = dbk * 16 + c, slot = qc * 32 + g * 8;
-      da[dbk] = lds_read<u32x4>(base + 3 * kTile, tr_byte<kBq>(dim, slot));
-      qa[dbk] = lds_read<u32x4>(base + 2 * kTile, tr_byte<kBq>(dim, slot));
+      const int off = (vb ^ ((4 * qc ^ (dbk & 3)) << 4)) + dbk * 16 * (2 * kBq);
+      da[dbk] = lds_read<u32x4>(lds + 3 * kTile, off);
+      qa[dbk] = lds_read<u32x4>(lds + 2 * kTile, off);
     }
   };
   auto v_mfma = [&](const u32x4 (&da)[kDblocks], const u32x4 (&qa)[kDblocks], const u32x4 (&pb)[kKb], const u32x4 (&db)[kKb])
@@ -456,6 +471,8 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
     tile_coords(t, h, q0);
     (void)h;
     const unsigned char* base = lds + (t & 1) * kBuf;
+    int sb = (t & 1) * kBuf + s_lane, vb = (t & 1) * kBuf + v_lane;
+    asm volatile("" : "+v"(sb), "+v"(vb));
     auto tile_body = [&](auto masked_c) __attribute__((always_inline)) {
       u32x4 sq0[kKsteps], sd0[kKsteps], sq1[kKsteps], sd1[kKsteps];
       u32x4 va0[kDblocks], vb0[kDblocks], va1[kDblocks], vb1[kDblocks];
@@ -464,10 +481,10 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
       float4 l0, d0, l1, d1;                 // statistics of the next two softmax blocks
       constexpr int kHalfD = kDblocks / 2;
       // S(0,0), then E(0,0)'s statistics and S(0,1)'s reads in its second half
-      s_read(base, 0, 0, sq0, sd0);
+      s_read(sb, 0, 0, sq0, sd0);
       s_mfma(sq0, sd0, sa0, sp0);
       stats_read(base, 0, 0, l0, d0);
-      s_read(base, 0, 1, sq1, sd1);
+      s_read(sb, 0, 1, sq1, sd1);
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * kKsteps, 0);
 #pragma unroll
       for (int i = 0; i < kSM; ++i) {
@@ -480,7 +497,7 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
       s_mfma(sq1, sd1, sa1, sp1);
       softmax(masked_c, q0, 0, 0, l0, d0, sa0, sp0, pb0, db0);
       stats_read(base, 0, 1, l1, d1);
-      s_read(base, 1, 0, sq0, sd0);
+      s_read(sb, 1, 0, sq0, sd0);
 #pragma unroll
       for (int i = 0; i < kSM; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -493,7 +510,7 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
       s_mfma(sq0, sd0, sa0, sp0);
       softmax(masked_c, q0, 0, 1, l1, d1, sa1, sp1, pb0, db0);
       stats_read(base, 1, 0, l0, d0);
-      s_read(base, 1, 1, sq1, sd1);
+      s_read(sb, 1, 1, sq1, sd1);
 #pragma unroll
       for (int i = 0; i < kSM; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -506,7 +523,7 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
       s_mfma(sq1, sd1, sa1, sp1);
       softmax(masked_c, q0, 1, 0, l0, d0, sa0, sp0, pb1, db1);
       stats_read(base, 1, 1, l1, d1);
-      v_read(base, 0, 0, kHalfD, va0, vb0);
+      v_read(vb, 0, 0, kHalfD, va0, vb0);
 #pragma unroll
       for (int i = 0; i < kSM; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -516,10 +533,10 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
       // V(0) | E(1,1) | the second half of V(0)'s reads, then the first half of V(1)'s
-      v_read(base, 0, kHalfD, kDblocks, va0, vb0);
+      v_read(vb, 0, kHalfD, kDblocks, va0, vb0);
       v_mfma(va0, vb0, pb0, db0);
       softmax(masked_c, q0, 1, 1, l1, d1, sa1, sp1, pb1, db1);
-      v_read(base, 1, 0, kHalfD, va1, vb1);
+      v_read(vb, 1, 0, kHalfD, va1, vb1);
 #pragma unroll
       for (int i = 0; i < kVM; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -528,7 +545,7 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_sched_barrier(0);
       // V(1) | the second half of its reads | staging of the next tile
-      v_read(base, 1, kHalfD, kDblocks, va1, vb1);
+      v_read(vb, 1, kHalfD, kDblocks, va1, vb1);
       v_mfma(va1, vb1, pb1, db1);
       store_tile((t + 1) & 1);   // after the last tile: an unused buffer
 #pragma unroll
