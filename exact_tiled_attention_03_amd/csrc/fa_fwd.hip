@@ -535,31 +535,27 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
 
   // tiles go in pairs; an odd count gets one more tile, past kv_end, whose keys are all
   // masked for every query of the workgroup (probability 0)
-  if constexpr (!CAUSAL && !BAND) {
-    // the pairs of tiles with every key in range come first, then the ragged end
-    const int clear_pairs = ((N - kv0) / kBc) & ~1;
-    int j = 0;
-    for (; j < clear_pairs; j += 2) {
-      step(sA, sB, ic<0>(), j, std::false_type{});
-      __syncthreads();
-      step(sB, sA, ic<1>(), j + 1, std::false_type{});
-      __syncthreads();
-    }
-    for (; j < ntiles; j += 2) {
-      step(sA, sB, ic<0>(), j, std::true_type{});
-      __syncthreads();
-      step(sB, sA, ic<1>(), j + 1, std::true_type{});
-      __syncthreads();
-    }
-  } else {
-    // per-tile mask checks (a second, unmasked body chosen per wavefront measured 2%
-    // slower here)
-    for (int j = 0; j < ntiles; j += 2) {
-      step(sA, sB, ic<0>(), j, std::true_type{});
-      __syncthreads();
-      step(sB, sA, ic<1>(), j + 1, std::true_type{});
-      __syncthreads();
-    }
+  // Pairs of tiles that every wavefront of the workgroup sees whole (all keys in range
+  // and, under the causal mask, at or before the workgroup's first query) come first and
+  // run the unmasked body; the rest (the ragged end, the causal diagonal, the band) run
+  // the masked one. A choice per wavefront measured 2% slower than this uniform split.
+  int clear_pairs = 0;
+  if constexpr (!BAND) {
+    const int in_range = (N - kv0) / kBc;
+    clear_pairs = (CAUSAL ? min(in_range, (q0 + 1 - kv0) / kBc) : in_range) & ~1;
+  }
+  int j = 0;
+  for (; j < clear_pairs; j += 2) {
+    step(sA, sB, ic<0>(), j, std::false_type{});
+    __syncthreads();
+    step(sB, sA, ic<1>(), j + 1, std::false_type{});
+    __syncthreads();
+  }
+  for (; j < ntiles; j += 2) {
+    step(sA, sB, ic<0>(), j, std::true_type{});
+    __syncthreads();
+    step(sB, sA, ic<1>(), j + 1, std::true_type{});
+    __syncthreads();
   }
 
   // ---- epilogue -----------------------------------------------------------------------
