@@ -304,8 +304,11 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
   const int su = kBoth ? tid : tid % kUnits, which = kBoth ? 0 : tid / kUnits;   // which 2+: none
   int sg, sc;
   staging_unit<kChunks, 2>(su & 63, su >> 6, sg, sc);
-  u32x4 rows[kUpt][4];
-  float lse_st = 0.0f;
+  // two register sets of staged rows: the loads of tile t+2 go out when tile t starts, a
+  // whole tile before its rows are needed in LDS (the Q/dO tiles come from L2 or HBM, and
+  // one tile of lead left the staging waiting on them)
+  u32x4 rows[2][kUpt][4];
+  float lse_st[2] = {0.0f, 0.0f};
   // query tiles from the last one down, so that the workgroups of one K/V head (which
   // start at different tiles under the causal mask) read the same Q/dO tile at about the
   // same time and share it in L2
@@ -313,7 +316,8 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
     h = hk * a.group + t / per_head;
     q0 = (nqt - 1 - t % per_head) * kBq;
   };
-  auto load_tile = [&](int t) __attribute__((always_inline)) {
+  auto load_tile = [&](int t, auto set_c) __attribute__((always_inline)) {
+    constexpr int st = decltype(set_c)::value;
     int h, q0;
     tile_coords(t, h, q0);
 #pragma unroll
@@ -324,15 +328,15 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int r = min(q0 + 4 * sg + j, N - 1);
-          rows[u][j] = *(const u32x4*)(src + ((size_t)b * N + r) * q_stride + (size_t)h * D + sc * 8);
+          rows[st][u][j] = *(const u32x4*)(src + ((size_t)b * N + r) * q_stride + (size_t)h * D + sc * 8);
         }
       }
     }
     if (tid < 2 * kBq) {                     // lse (scaled to base 2) then D
       const int r = q0 + (tid % kBq);
       const size_t off = ((size_t)b * a.H + h) * N + min(r, N - 1);
-      if (tid < kBq) lse_st = r < N ? a.lse[off] * kLog2e : INFINITY;     // rows past the end: P = 0
-      else lse_st = r < N ? a.delta[off] : 0.0f;
+      if (tid < kBq) lse_st[st] = r < N ? a.lse[off] * kLog2e : INFINITY;     // rows past the end: P = 0
+      else lse_st[st] = r < N ? a.delta[off] : 0.0f;
     }
   };
   // staging-write bases: rm16_byte(4sg + j, sc) = (rm_w0 ^ 16j) + 2D j and
@@ -342,7 +346,10 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
     const int s0 = slot32_of(4 * sg);
     return 8 * sc * (2 * kBq) + ((((s0 >> 3) ^ (4 * (sc & 1)) ^ ((sc >> 1) & 3)) & 7) << 4) + ((s0 & 7) << 1);
   }();
-  auto store_tile = [&](int buf) __attribute__((always_inline)) {
+  // tile rows of register set st into LDS buffer st (a tile's buffer and set are both its
+  // parity)
+  auto store_tile = [&](auto set_c) __attribute__((always_inline)) {
+    constexpr int st = decltype(set_c)::value, buf = st;
     // opaque per call: the write offsets are formed here, not held across the loop
     int rmw = buf * kBuf + rm_w0, trw = buf * kBuf + tr_w0;
     asm volatile("" : "+v"(rmw), "+v"(trw));
@@ -353,19 +360,19 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
         unsigned char* rm = lds + wh * kTile;
         unsigned char* tr = lds + (2 + wh) * kTile;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) *(u32x4*)(rm + ((rmw ^ (j << 4)) + j * (2 * D))) = rows[u][j];
+        for (int j = 0; j < 4; ++j) *(u32x4*)(rm + ((rmw ^ (j << 4)) + j * (2 * D))) = rows[st][u][j];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const unsigned sel = (e & 1) ? 0x07060302u : 0x05040100u;
           u32x2 w;
-          w[0] = __builtin_amdgcn_perm(rows[u][1][e >> 1], rows[u][0][e >> 1], sel);
-          w[1] = __builtin_amdgcn_perm(rows[u][3][e >> 1], rows[u][2][e >> 1], sel);
+          w[0] = __builtin_amdgcn_perm(rows[st][u][1][e >> 1], rows[st][u][0][e >> 1], sel);
+          w[1] = __builtin_amdgcn_perm(rows[st][u][3][e >> 1], rows[st][u][2][e >> 1], sel);
           *(u32x2*)(tr + ((trw ^ ((e >> 1) << 4)) + e * (2 * kBq))) = w;
         }
       }
     }
     unsigned char* base = lds + buf * kBuf;
-    if (tid < 2 * kBq) ((float*)(base + 4 * kTile))[tid] = lse_st;
+    if (tid < 2 * kBq) ((float*)(base + 4 * kTile))[tid] = lse_st[st];
   };
 
   // Each 64-query tile runs as six phases whose MFMAs hide the next phase's LDS reads
@@ -461,17 +468,21 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int kSM = 2 * kKsteps * kKb;     // MFMAs of an S phase
   constexpr int kVM = 2 * kDblocks * kKb;    // MFMAs of a V phase
 
-  load_tile(0);
-  store_tile(0);
+  load_tile(0, std::integral_constant<int, 0>{});
+  store_tile(std::integral_constant<int, 0>{});
+  if (1 < T) load_tile(1, std::integral_constant<int, 1>{});
   __syncthreads();
 
-  for (int t = 0; t < T; ++t) {
-    if (t + 1 < T) load_tile(t + 1);
+  // tile t of parity par: loads of tile t+2 into register set par (stored at the end of
+  // tile t-1), reads from buffer par, tile t+1 staged from set par^1 into buffer par^1
+  auto tile_iter = [&](int t, auto par_c) __attribute__((always_inline)) {
+    constexpr int par = decltype(par_c)::value;
+    if (t + 2 < T) load_tile(t + 2, std::integral_constant<int, par>{});
     int h, q0;
     tile_coords(t, h, q0);
     (void)h;
-    const unsigned char* base = lds + (t & 1) * kBuf;
-    int sb = (t & 1) * kBuf + s_lane, vb = (t & 1) * kBuf + v_lane;
+    const unsigned char* base = lds + par * kBuf;
+    int sb = par * kBuf + s_lane, vb = par * kBuf + v_lane;
     asm volatile("" : "+v"(sb), "+v"(vb));
     auto tile_body = [&](auto masked_c) __attribute__((always_inline)) {
       u32x4 sq0[kKsteps], sd0[kKsteps], sq1[kKsteps], sd1[kKsteps];
@@ -547,7 +558,7 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
       // V(1) | the second half of its reads | staging of the next tile
       v_read(vb, 1, kHalfD, kDblocks, va1, vb1);
       v_mfma(va1, vb1, pb1, db1);
-      store_tile((t + 1) & 1);   // after the last tile: an unused buffer
+      store_tile(std::integral_constant<int, par ^ 1>{});   // after the last tile: an unused buffer
 #pragma unroll
       for (int i = 0; i < kVM; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -562,9 +573,13 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
     } else if (kw0 <= q0 + kBq - 1) {
       tile_body(std::true_type{});
     } else {
-      store_tile((t + 1) & 1);               // all queries precede the keys: nothing to add
+      store_tile(std::integral_constant<int, par ^ 1>{});               // all queries precede the keys: nothing to add
     }
     __syncthreads();
+  };
+  for (int t = 0; t < T; t += 2) {
+    tile_iter(t, std::integral_constant<int, 0>{});
+    if (t + 1 < T) tile_iter(t + 1, std::integral_constant<int, 1>{});
   }
 
   // epilogue: lane holds dims 16dbk + 4g + 0..3 of its keys
@@ -668,10 +683,6 @@ __global__ __launch_bounds__(64 * kWavesQ) void bwd_dq_kernel(BwdArgs a) {
       stage_rows<D, kBk, true, false>(base + kTile, nullptr, rmw, trw, vrows);
     }
   };
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
 
   // LDS read offsets. The swizzles are XORs on bits that the buffer and block offsets leave
   // clear, so every read is one per-lane base XOR a constant, plus an immediate:
