@@ -28,10 +28,16 @@
 //     only tiles on the causal diagonal pay for the mask.
 //   * dQ kernel (v_mfma_f32_32x32x16): one workgroup of 8 wavefronts per (batch, head, 256
 //     queries), the forward's orientation: S^T = K Q^T and dP^T = V dO^T with one query
-//     per lane, then dQ^T += K^T dS^T with K^T staged transposed in LDS.
-//   * Tiles are double-buffered in LDS; the next tile's global loads are in flight while
+//     per lane, then dQ^T += K^T dS^T with K^T staged transposed in LDS. A 64-key tile
+//     runs as phases over its two 32-key blocks, and only a ragged last tile or a causal
+//     diagonal tile runs the masked body.
+//   * Tiles are double-buffered in LDS with one barrier per tile. The global loads of the
+//     next tile (dQ) or of the tile after it (dK/dV, two register sets) are in flight while
 //     the current one is computed. Eight wavefronts share each LDS tile, two per SIMD, so
 //     that one's MFMAs overlap the other's exponentials and LDS reads.
+//   * Every swizzled LDS offset is one per-lane base XOR a constant plus an immediate; the
+//     bases are formed per tile behind an empty asm, so the compiler neither holds every
+//     offset in registers across the tile loop nor spills them.
 //   * LDS bank conflicts were measured per access pattern with SQ_LDS_BANK_CONFLICT; every
 //     tile read and staging write here is conflict-free. Writes behave as 32 banks x 4 B
 //     served to 8 consecutive lanes (16-byte writes) or 16 consecutive lanes (8-byte
