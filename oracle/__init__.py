@@ -87,6 +87,13 @@ def load(path: str):
     lib.oracle_attn_bwd_dq_rows_f64.restype = ctypes.c_int
     lib.oracle_attn_fwd_kv_f64.argtypes = [dp] * 5 + [ctypes.c_int] * 7 + [ctypes.c_double]
     lib.oracle_attn_fwd_kv_f64.restype = ctypes.c_int
+    lib.oracle_attn_fwd_block_f64.argtypes = ([dp, dp, dp, dp, dp] + [ctypes.c_int] * 6 +
+                                              [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_double])
+    lib.oracle_attn_fwd_block_f64.restype = ctypes.c_int
+    lib.oracle_attn_rows_block_f64.argtypes = ([dp, ctypes.c_int, dp, dp] + [ctypes.c_int] * 6 +
+                                               [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                                ctypes.c_int64, i64p, dp, dp])
+    lib.oracle_attn_rows_block_f64.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     return lib
@@ -224,6 +231,78 @@ def attn_rows(q_raw: np.ndarray, k_raw: np.ndarray, v_raw: np.ndarray, dtype: st
     q_sel = q_raw[rows[:, 0], rows[:, 2], rows[:, 1], :]
     return attn_rows_f64(decode(q_sel, dtype, dq), decode(k_raw, dtype, dk), decode(v_raw, dtype, dv),
                          H, rows, causal, scale, window)
+
+
+# ---- block-sparse attention (attn_oracle.c) ----
+# The block-sparse variant of the abstract of "FlashAttention: Fast and Memory-Efficient
+# Exact Attention with IO-Awareness": key j is visible to query i iff
+# mask[hm, i // block, j // block] != 0 (and j <= i when causal), hm = 0 for a mask
+# shared by all heads, else the query head; a row with no visible key gives O = 0 and
+# lse = -inf.
+
+def _block_mask(mask, H: int, N: int, block: int) -> np.ndarray:
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    nb = (N + block - 1) // block
+    if mask.ndim != 3 or mask.shape[1:] != (nb, nb) or mask.shape[0] not in (1, H):
+        raise ValueError(f"block mask must be [1 or H, {nb}, {nb}] for N={N}, block={block}")
+    return mask
+
+
+def attn_fwd_block_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: float,
+                       mask, block: int = 64):
+    """Block-sparse attention forward on fp64 inputs (layouts as attn_fwd_f64); mask is
+    [mask_heads, nb, nb] (0 = block skipped). Returns (o, lse) in float64."""
+    q, k, v = (np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v))
+    B, N, H, Hkv, d = _shape(q, k, v)
+    mask = _block_mask(mask, H, N, block)
+    o = np.empty_like(q)
+    lse = np.empty((B, H, N), dtype=np.float64)
+    rc = _lib().oracle_attn_fwd_block_f64(_dptr(q), _dptr(k), _dptr(v), _dptr(o), _dptr(lse), B, H, Hkv, N, d,
+                                          int(bool(causal)), mask.ctypes.data, mask.shape[0], int(block),
+                                          float(scale))
+    if rc:
+        raise ValueError(f"oracle_attn_fwd_block_f64 failed ({rc})")
+    return o, lse
+
+
+def attn_rows_block_f64(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, H: int, rows: np.ndarray,
+                        causal: bool, scale: float, mask, block: int = 64):
+    """Selected rows (b, h, i) of the block-sparse forward; q_rows [R,d] fp64."""
+    q_rows = np.ascontiguousarray(q_rows, dtype=np.float64)
+    k = np.ascontiguousarray(k, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+    B, N, Hkv, d = k.shape
+    mask = _block_mask(mask, H, N, block)
+    R = rows.shape[0]
+    if q_rows.shape != (R, d):
+        raise ValueError("q_rows must be [len(rows), d]")
+    o = np.empty((R, d), dtype=np.float64)
+    lse = np.empty((R,), dtype=np.float64)
+    rc = _lib().oracle_attn_rows_block_f64(_dptr(q_rows), 1, _dptr(k), _dptr(v), B, H, Hkv, N, d,
+                                           int(bool(causal)), mask.ctypes.data, mask.shape[0], int(block),
+                                           float(scale), R, rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                           _dptr(o), _dptr(lse))
+    if rc:
+        raise ValueError(f"oracle_attn_rows_block_f64 failed ({rc})")
+    return o, lse
+
+
+def attn_fwd_block(q_raw: np.ndarray, k_raw: np.ndarray, v_raw: np.ndarray, dtype: str, causal: bool,
+                   scale: float, mask, block: int = 64):
+    """Block-sparse forward on stored f16/bf16 inputs exactly as handed to the library."""
+    return attn_fwd_block_f64(decode(q_raw, dtype), decode(k_raw, dtype), decode(v_raw, dtype), causal, scale,
+                              mask, block)
+
+
+def attn_rows_block(q_raw: np.ndarray, k_raw: np.ndarray, v_raw: np.ndarray, dtype: str, causal: bool,
+                    scale: float, rows: np.ndarray, mask, block: int = 64):
+    """Selected rows of the block-sparse forward on stored inputs."""
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+    B, N, H, d = q_raw.shape
+    q_sel = q_raw[rows[:, 0], rows[:, 2], rows[:, 1], :]
+    return attn_rows_block_f64(decode(q_sel, dtype), decode(k_raw, dtype), decode(v_raw, dtype), H, rows, causal,
+                               scale, mask, block)
 
 
 # ---- block quantisation to e4m3 (fp8_quant_oracle.c) ----

@@ -281,6 +281,123 @@ int oracle_attn_fwd_kv_f64(const double* q, const double* k, const double* v, do
   return failed ? 2 : 0;
 }
 
+/* ---- block-sparse attention ----
+ * The approximate variant named in the abstract of "FlashAttention: Fast and Memory-
+ * Efficient Exact Attention with IO-Awareness" (block-sparse FlashAttention), which the
+ * pages do not define further. Reading: a 0/1 mask over blocks of `block` queries x
+ * `block` keys says which blocks are computed; key j is visible to query i iff
+ *     mask[hm][i / block][j / block] != 0   (and j <= i when causal),
+ * hm = 0 when the mask is shared by every head (mask_heads = 1), else the query head h
+ * (mask_heads = H). The attention over the visible keys is then exact. A row with no
+ * visible key has no softmax; its output is taken as O = 0 and lse = -inf.
+ * mask is [mask_heads][nb][nb] bytes, nb = ceil(N / block). */
+
+/* One row over the keys with keep[j] != 0 (any subset of 0..N-1). */
+static void attn_row_keep(const double* qi, const double* k, const double* v, int Hkv, int N, int d,
+                          const unsigned char* keep, double scale, int b, int hk, double* s,
+                          double* o_row, double* lse) {
+  double m = -INFINITY;
+  for (int j = 0; j < N; ++j) {
+    if (!keep[j]) continue;
+    const double* kj = k + (((size_t)b * N + j) * Hkv + hk) * d;
+    double dot = 0.0;
+    for (int t = 0; t < d; ++t) dot += qi[t] * kj[t];
+    s[j] = scale * dot;
+    if (s[j] > m) m = s[j];
+  }
+  for (int t = 0; t < d; ++t) o_row[t] = 0.0;
+  if (m == -INFINITY) {                      /* no visible key */
+    *lse = -INFINITY;
+    return;
+  }
+  double l = 0.0;
+  for (int j = 0; j < N; ++j) {
+    if (!keep[j]) continue;
+    const double e = exp(s[j] - m);
+    const double* vj = v + (((size_t)b * N + j) * Hkv + hk) * d;
+    l += e;
+    for (int t = 0; t < d; ++t) o_row[t] += e * vj[t];
+  }
+  for (int t = 0; t < d; ++t) o_row[t] /= l;
+  *lse = m + log(l);
+}
+
+static void block_keep(const unsigned char* mask, int mask_heads, int block, int N, int causal, int h,
+                       int i, unsigned char* keep) {
+  const int nb = (N + block - 1) / block;
+  const unsigned char* row = mask + ((size_t)(mask_heads == 1 ? 0 : h) * nb + i / block) * nb;
+  for (int j = 0; j < N; ++j) keep[j] = row[j / block] != 0 && (!causal || j <= i);
+}
+
+int oracle_attn_fwd_block_f64(const double* q, const double* k, const double* v, double* o,
+                              double* lse, int B, int H, int Hkv, int N, int d, int causal,
+                              const unsigned char* mask, int mask_heads, int block, double scale) {
+  if (check_shape(B, H, Hkv, N, d) || !q || !k || !v || !o || !lse || !mask || block < 1) return 1;
+  if (mask_heads != 1 && mask_heads != H) return 1;
+  const int64_t rows = (int64_t)B * H * N;
+  const int group = H / Hkv;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)N);
+    unsigned char* keep = (unsigned char*)malloc((size_t)N);
+    if (!s || !keep) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 8)
+    for (int64_t r = 0; r < rows; ++r) {
+      if (!s || !keep) continue;
+      const int i = (int)(r % N), h = (int)((r / N) % H), b = (int)(r / ((int64_t)N * H));
+      const size_t qo = (((size_t)b * N + i) * H + h) * d;
+      block_keep(mask, mask_heads, block, N, causal, h, i, keep);
+      attn_row_keep(q + qo, k, v, Hkv, N, d, keep, scale, b, h / group, s, o + qo,
+                    lse + ((size_t)b * H + h) * N + i);
+    }
+    free(s);
+    free(keep);
+  }
+  return failed ? 2 : 0;
+}
+
+/* Selected rows (as oracle_attn_rows_local_f64) under a block mask. */
+int oracle_attn_rows_block_f64(const double* q, int q_is_rows, const double* k, const double* v,
+                               int B, int H, int Hkv, int N, int d, int causal,
+                               const unsigned char* mask, int mask_heads, int block, double scale,
+                               int64_t nrows, const int64_t* rows, double* o_rows, double* lse_rows) {
+  if (check_shape(B, H, Hkv, N, d) || !q || !k || !v || !rows || !o_rows || !lse_rows || !mask ||
+      block < 1)
+    return 1;
+  if (mask_heads != 1 && mask_heads != H) return 1;
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t b = rows[3 * r], h = rows[3 * r + 1], i = rows[3 * r + 2];
+    if (b < 0 || b >= B || h < 0 || h >= H || i < 0 || i >= N) return 1;
+  }
+  const int group = H / Hkv;
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)N);
+    unsigned char* keep = (unsigned char*)malloc((size_t)N);
+    if (!s || !keep) {
+#pragma omp atomic write
+      failed = 1;
+    }
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+      if (!s || !keep) continue;
+      const int b = (int)rows[3 * r], h = (int)rows[3 * r + 1], i = (int)rows[3 * r + 2];
+      const double* qi = q_is_rows ? q + (size_t)r * d : q + (((size_t)b * N + i) * H + h) * d;
+      block_keep(mask, mask_heads, block, N, causal, h, i, keep);
+      attn_row_keep(qi, k, v, Hkv, N, d, keep, scale, b, h / group, s, o_rows + (size_t)r * d,
+                    lse_rows + r);
+    }
+    free(s);
+    free(keep);
+  }
+  return failed ? 2 : 0;
+}
+
 int oracle_num_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

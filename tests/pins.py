@@ -430,6 +430,105 @@ def pin_window_reductions():
         _close(l2[:, :, 0], lse[:, :, i], 1e-13, f"causal window row {i} = slice attention (lse)")
 
 
+# Block-sparse attention (the block-sparse FlashAttention of the abstract of
+# "FlashAttention: Fast and Memory-Efficient Exact Attention with IO-Awareness", which
+# the pages name without defining). Reading pinned here: key j is visible to query i iff
+# mask[hm, i // block, j // block] != 0 (and j <= i when causal); a row with no visible
+# key gives O = 0 and lse = -inf.
+def _block_element_mask(mask, h, N, block, causal):
+    """Boolean [N, N] visibility expanded from the block mask with np.kron (independent of
+    the oracle's per-key index arithmetic)."""
+    m = mask[0 if mask.shape[0] == 1 else h].astype(bool)
+    keep = np.kron(m, np.ones((block, block), dtype=bool))[:N, :N]
+    if causal:
+        keep &= np.tril(np.ones((N, N), dtype=bool))
+    return keep
+
+
+# P26 -- block masks against brute force in 50 digits and against torch's attention with
+# an explicit boolean mask (float64, CPU); rows with no visible key give O = 0, lse = -inf.
+def pin_block_sparse_bruteforce_and_sdpa():
+    rng = np.random.default_rng(41)
+    mpmath.mp.dps = 50
+    N, H, Hkv, d, block = 10, 2, 1, 3, 3               # nb = 4, ragged last block
+    q, k, v = _qkv(rng, 1, N, H, Hkv, d)
+    mask = (rng.random((H, 4, 4)) < 0.5).astype(np.uint8)
+    mask[0, 1, :] = 0                                  # an empty block row in head 0
+    for causal in (False, True):
+        o, lse = oracle.attn_fwd_block_f64(q, k, v, causal, 0.6, mask, block)
+        for h in range(H):
+            keep = _block_element_mask(mask, h, N, block, causal)
+            for i in range(N):
+                J = [j for j in range(N) if keep[i, j]]
+                if not J:
+                    assert np.all(o[0, i, h] == 0.0) and lse[0, h, i] == -np.inf, f"empty row {h},{i}"
+                    continue
+                s = [mpmath.mpf(0.6) * mpmath.fsum(mpmath.mpf(q[0, i, h, t]) * mpmath.mpf(k[0, j, 0, t])
+                                                   for t in range(d)) for j in J]
+                L = mpmath.log(mpmath.fsum(mpmath.exp(x) for x in s))
+                ref = [float(mpmath.fsum(mpmath.exp(x - L) * mpmath.mpf(v[0, j, 0, t]) for x, j in zip(s, J)))
+                       for t in range(d)]
+                _close(o[0, i, h], ref, 1e-13, f"block mask (causal={causal}) mpmath O h{h} i{i}")
+                _close(lse[0, h, i], float(L), 1e-13, f"block mask (causal={causal}) mpmath lse")
+    B, N, H, Hkv, d, block = 2, 150, 4, 2, 16, 64      # nb = 3
+    q, k, v = _qkv(rng, B, N, H, Hkv, d)
+    t = lambda x: torch.from_numpy(x).permute(0, 2, 1, 3)
+    for heads in (1, H):
+        mask = (rng.random((heads, 3, 3)) < 0.6).astype(np.uint8)
+        mask[:, :, 0] = 1                              # every row sees key block 0: no empty rows
+        for causal in (False, True):
+            o, lse = oracle.attn_fwd_block_f64(q, k, v, causal, 0.25, mask, block)
+            emask = torch.from_numpy(np.stack([_block_element_mask(mask, h, N, block, causal) for h in range(H)]))
+            ref = F.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=emask, scale=0.25,
+                                                 enable_gqa=True).permute(0, 2, 1, 3).numpy()
+            _close(o, ref, 1e-12, f"block mask heads={heads} causal={causal} vs sdpa with mask")
+            ref_lse = np.stack([_sdpa_lse_masked(q[:, :, h], k[:, :, h // (H // Hkv)], emask[h].numpy(), 0.25)
+                                for h in range(H)], axis=1)
+            _close(lse, ref_lse, 1e-12, f"block mask heads={heads} causal={causal} lse")
+
+
+def _sdpa_lse_masked(qh, kh, keep, scale):
+    """ln sum_j exp(scale <q_i, k_j>) over the visible keys, via torch.logsumexp."""
+    s = scale * torch.einsum("bid,bjd->bij", torch.from_numpy(qh), torch.from_numpy(kh))
+    s = s.masked_fill(~torch.from_numpy(keep), -float("inf"))
+    return torch.logsumexp(s, dim=-1).numpy()
+
+
+# P27 -- block masks reduce to the dense cases: an all-ones mask is the full (or causal)
+# attention, a lower-triangular block mask with the causal flag is the causal mask, and
+# a block-diagonal mask is independent attention inside each block (bit-identical: the
+# same sums in the same order); with Q = 0 a row is the mean of its visible V rows.
+def pin_block_sparse_reductions():
+    rng = np.random.default_rng(42)
+    B, N, H, Hkv, d, block = 1, 100, 2, 1, 8, 16       # nb = 7
+    q, k, v = _qkv(rng, B, N, H, Hkv, d)
+    nb = 7
+    for causal in (False, True):
+        o, lse = oracle.attn_fwd_f64(q, k, v, causal, 0.5)
+        o2, l2 = oracle.attn_fwd_block_f64(q, k, v, causal, 0.5, np.ones((1, nb, nb), np.uint8), block)
+        assert np.array_equal(o, o2) and np.array_equal(lse, l2), f"all-ones mask (causal={causal})"
+    oc, lc = oracle.attn_fwd_f64(q, k, v, True, 0.5)
+    o2, l2 = oracle.attn_fwd_block_f64(q, k, v, True, 0.5, np.tril(np.ones((nb, nb), np.uint8))[None], block)
+    assert np.array_equal(oc, o2) and np.array_equal(lc, l2), "lower-triangular block mask + causal"
+    o, lse = oracle.attn_fwd_block_f64(q, k, v, False, 0.5, np.eye(nb, dtype=np.uint8)[None], block)
+    for qb in range(nb):
+        lo, hi = qb * block, min(N, (qb + 1) * block)
+        o2, l2 = oracle.attn_fwd_f64(q[:, lo:hi], k[:, lo:hi], v[:, lo:hi], False, 0.5)
+        assert np.array_equal(o[:, lo:hi], o2) and np.array_equal(lse[:, :, lo:hi], l2), f"diagonal block {qb}"
+    mask = (rng.random((H, nb, nb)) < 0.4).astype(np.uint8)
+    q0 = np.zeros_like(q)
+    for causal in (False, True):
+        o, lse = oracle.attn_fwd_block_f64(q0, k, v, causal, 0.9, mask, block)
+        for h in range(H):
+            keep = _block_element_mask(mask, h, N, block, causal).astype(np.float64)
+            count = keep.sum(axis=1)
+            seen = count > 0
+            _close(o[0, seen, h], (keep @ v[0, :, 0])[seen] / count[seen, None], 1e-13,
+                   f"block mask Q=0 local mean (causal={causal}) h{h}")
+            _close(lse[0, h, seen], np.log(count[seen]), 1e-13, f"block mask Q=0 ln(count) h{h}")
+            assert np.all(o[0, ~seen, h] == 0.0) and np.all(lse[0, h, ~seen] == -np.inf), "empty rows"
+
+
 # Block quantisation to e4m3 and incoherent processing. The abstract of "FlashAttention-3:
 # Fast and Accurate Attention with Asynchrony and Low-precision" names both without
 # defining them; the readings pinned here: one power-of-two scale per 64-row slab of each
@@ -651,4 +750,5 @@ ALL_PINS = [pin_mpmath_bruteforce, pin_torch_sdpa, pin_zero_query, pin_single_ke
             pin_causal_prefix, pin_split_merge, pin_hardmax_and_range, pin_decoders, pin_golden_fixtures,
             pin_window_bruteforce_and_sdpa, pin_window_closed_forms, pin_window_reductions,
             pin_e4m3_encode, pin_fwht, pin_block_quantize, pin_rotation_identity,
-            pin_bwd_finite_differences, pin_bwd_torch_autograd, pin_bwd_invariants, pin_decode_rectangular]
+            pin_bwd_finite_differences, pin_bwd_torch_autograd, pin_bwd_invariants, pin_decode_rectangular,
+            pin_block_sparse_bruteforce_and_sdpa, pin_block_sparse_reductions]

@@ -50,6 +50,12 @@ MUTANTS = {
     "decode_ignores_descale": ("dst[i] = x * mult;", "dst[i] = x;"),
     "kv_causal_top_left": ("const int pos = Nk - Nq + i;", "const int pos = i;"),
     "kv_causal_one_short": ("const int pos = Nk - Nq + i;", "const int pos = Nk - Nq + i - 1;"),
+    "block_key_index_shifted": ("keep[j] = row[j / block] != 0", "keep[j] = row[(j + 1) / block] != 0"),
+    "block_query_index_shifted": ("+ i / block) * nb;", "+ (i + 1 < N ? i + 1 : i) / block) * nb;"),
+    "block_mask_heads_ignored": ("(mask_heads == 1 ? 0 : h)", "0"),
+    "block_causal_ignored": ("!= 0 && (!causal || j <= i);", "!= 0;"),
+    "block_empty_row_unguarded": ("if (m == -INFINITY) {                      /* no visible key */",
+                                  "if (0) {"),
 }
 
 # mutants of the block-quantisation oracle (fp8_quant_oracle.c)
