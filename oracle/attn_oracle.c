@@ -299,7 +299,7 @@ static void attn_row_keep(const double* qi, const double* k, const double* v, in
   double m = -INFINITY;
   for (int j = 0; j < N; ++j) {
     if (!keep[j]) continue;
-    const double* kj = k + (((size_t)b * N + j) * Hkv + hk) * d;
+    const double* kj = k + (((size_t)b * N + (size_t)j) * Hkv + hk) * d;
     double dot = 0.0;
     for (int t = 0; t < d; ++t) dot += qi[t] * kj[t];
     s[j] = scale * dot;
@@ -314,7 +314,7 @@ static void attn_row_keep(const double* qi, const double* k, const double* v, in
   for (int j = 0; j < N; ++j) {
     if (!keep[j]) continue;
     const double e = exp(s[j] - m);
-    const double* vj = v + (((size_t)b * N + j) * Hkv + hk) * d;
+    const double* vj = v + (((size_t)b * N + (size_t)j) * Hkv + hk) * d;
     l += e;
     for (int t = 0; t < d; ++t) o_row[t] += e * vj[t];
   }
