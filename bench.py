@@ -1,9 +1,10 @@
 """Benchmark of the attention forward hot path on one MI355X.
 
 A step is one attention forward (one fa_fwd launch through the C ABI, fa_fwd_local for
-a key-window workload) over the whole workload, inputs resident in HBM. Prints one JSON
-line with TFLOP/s counted as 4*B*H*N^2*d (halved under the causal mask; for a key window,
-4*B*H*d times the visible (query, key) pairs), the roofline of the kernel (achieved
+a key-window workload, fa_fwd_block_sparse for a block-sparse one) over the whole
+workload, inputs resident in HBM. Prints one JSON line with TFLOP/s counted as
+4*B*H*N^2*d (halved under the causal mask; for a key window or a block mask, 4*B*d times
+the visible (query, key) pairs over the heads), the roofline of the kernel (achieved
 TFLOP/s from HIP events on the launch stream against the dense bf16/f16 MFMA peak) and
 the fp64 CPU oracle timed on the host cores on a bounded sample of the same workload.
 
@@ -95,7 +96,8 @@ def cpu_baseline(w: synth_inputs.Workload, inp: dict, budget_s: float = 12.0):
         return oracle.block_dequantize(*oracle.block_quantize(x, 64, sg))
     g = w.H // w.Hkv
     per_head = w.flops / (w.B * w.H)
-    heads, elapsed = 0, 0.0
+    bmask = synth_inputs.workload_block_mask(w) if w.sparse_density else None
+    heads, elapsed, flops = 0, 0.0, 0.0
     for b in range(w.B):
         if elapsed >= budget_s:
             break
@@ -112,11 +114,15 @@ def cpu_baseline(w: synth_inputs.Workload, inp: dict, budget_s: float = 12.0):
             if w.backward:
                 ds = oracle.decode(dout[b:b + 1, :, hk * g:(hk + 1) * g], w.dtype)
                 oracle.attn_bwd_f64(qs, ks, vs, ds, w.causal, w.scale)
+            elif bmask is not None:
+                mh = bmask[hk * g:(hk + 1) * g]
+                oracle.attn_fwd_block_f64(qs, ks, vs, w.causal, w.scale, mh)
             else:
                 oracle.attn_fwd_f64(qs, ks, vs, w.causal, w.scale / (w.d if w.fp8_block else 1), w.window)
             elapsed += time.perf_counter() - t0
             heads += g
-    flops = per_head * heads
+            flops += (4.0 * w.d * synth_inputs.block_mask_pairs(mh, w.N, w.causal, g) if bmask is not None
+                      else per_head * g)
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": f"first {heads} of {w.B * w.H} (batch, head) slices of {w.name} in memory order, "
@@ -188,6 +194,12 @@ def main():
 
         def step(o=None, lse=None):
             return fa.fwd_splitkv(q, k, v, causal=w.causal, scale=w.scale, out=o, lse=lse, workspace=ws)
+    elif w.sparse_density:
+        # block-sparse: a step is one fa_fwd_block_sparse call; the mask is resident
+        bmask = torch.from_numpy(synth_inputs.workload_block_mask(w)).cuda()
+
+        def step(o=None, lse=None):
+            return fa.fwd_block_sparse(q, k, v, bmask, causal=w.causal, scale=w.scale, out=o, lse=lse)
     elif w.backward:
         # the gradient pass: the forward's o and lse are computed once, outside the timed
         # region; a step is one fa_bwd call (three launches)
@@ -254,6 +266,10 @@ def main():
                    **({"Nq": w.decode_nq, "Nk": w.N, "pass": "split-KV decode"} if w.decode_nq else {}),
                    "causal": w.causal, "scale": w.scale, "flop_per_step": w.flops,
                    **({"window": list(w.window)} if w.window else {}),
+                   **({"block_sparse": {"block": synth_inputs.SPARSE_BLOCK, "mask_heads": w.H,
+                                        "kept_blocks": round(float(synth_inputs.workload_block_mask(w).mean()), 4),
+                                        "pattern": "local + global + random key blocks per 256-query group"}}
+                      if w.sparse_density else {}),
                    **({"fp8": "block scales (64 rows, E8M0), Hadamard-rotated q/k"} if w.fp8_block else {})},
         "roofline": roof,
     }

@@ -77,6 +77,10 @@ struct FwdArgs {
   const uint8_t* k_scales;
   const uint8_t* v_scales;
   int nb;
+  // block-sparse mask: [mask_heads][nblk][nblk] bytes over blocks of kSparseBlock queries x
+  // kSparseBlock keys, nonzero = computed; mask_heads is 1 (shared) or H
+  const uint8_t* block_mask;
+  int mask_heads, nblk;
 };
 
 // Masks, one kernel instance each: none; causal (key j visible to query i iff j <= i);
@@ -85,6 +89,12 @@ struct FwdArgs {
 constexpr int kMaskNone = 0;
 constexpr int kMaskCausal = 1;
 constexpr int kMaskBand = 2;
+// block-sparse (iff the block mask keeps the (query block, key block) pair), alone or
+// with the causal mask
+constexpr int kMaskBlock = 3;
+constexpr int kMaskBlockCausal = 4;             // block-sparse intersected with the causal mask
+constexpr int kSparseBlock = 64;                // rows of a mask block, queries and keys
+constexpr int kMaxSparseBlocks = 2048;          // key blocks per row of the mask: N <= 131072
 
 // Workgroups are handed to the 8 XCDs round-robin (workgroup L runs on XCD L % 8), and
 // each XCD has its own L2. Reorder so that XCD x receives one contiguous range of the
@@ -248,8 +258,10 @@ __device__ __forceinline__ lds_byte* lds_dma_dst(unsigned char* p) {
 
 template <typename Ops, int D, int MASK>
 __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
-  constexpr bool CAUSAL = MASK == kMaskCausal;
+  constexpr bool CAUSAL = MASK == kMaskCausal || MASK == kMaskBlockCausal;
   constexpr bool BAND = MASK == kMaskBand;
+  constexpr bool BLOCKS = MASK == kMaskBlock || MASK == kMaskBlockCausal;
+  static_assert(kSparseBlock == kBc && kBr % kSparseBlock == 0 && kBr / kSparseBlock <= 4, "mask blocks");
   constexpr int kChunks = D / 8;                  // 16-byte chunks per K row
   constexpr int kKsteps = D / 16;                 // MFMA k-steps over d for S^T
   constexpr int kDblocks = D / 32;                // 32-row blocks of O^T
@@ -259,6 +271,9 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
 
   // K slot 0, K slot 1, V^T slot 0, V^T slot 1
   __shared__ __attribute__((aligned(16))) unsigned char lds[4 * kTileBytes];
+  // block-sparse: the workgroup's active key blocks, each entry kb | (q-block bits << 16)
+  __shared__ int blk_list[BLOCKS ? kMaxSparseBlocks : 1];
+  __shared__ int blk_count;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -289,7 +304,44 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
     qreg[ks] = *(const u32x4*)(qp + (size_t)qi_ld * q_row_stride + ks * 16 + hi * 8);
 
   const int kv_end = BAND ? min(N, q0 + kBr + a.wr) : CAUSAL ? min(N, q0 + kBr) : N;
-  const int ntiles = (kv_end - kv0 + kBc - 1) / kBc;
+  // Block-sparse: wavefront 0 lists the key blocks that some query block of the workgroup
+  // keeps (under the causal mask, only those up to the workgroup's last query), with the
+  // query blocks that keep each (bit r: rows q0 + 64r ..); the tiles are these blocks.
+  int nact = 0;
+  if constexpr (BLOCKS) {
+    const int nb = a.nblk, qb0 = q0 / kSparseBlock;
+    const uint8_t* mrow = a.block_mask + ((size_t)(a.mask_heads == 1 ? 0 : h) * nb + qb0) * nb;
+    const int kb_end = CAUSAL ? min(nb, (q0 + kBr) / kBc) : nb;
+    if (wave == 0) {
+      int count = 0;
+      for (int base = 0; base < kb_end; base += kWave) {
+        const int kb = base + lane;
+        int bits = 0;
+        if (kb < kb_end) {
+#pragma unroll
+          for (int r = 0; r < kBr / kSparseBlock; ++r)
+            if (qb0 + r < nb && mrow[(size_t)r * nb + kb] != 0) bits |= 1 << r;
+        }
+        const unsigned long long act = __ballot(bits != 0);
+        if (bits) blk_list[count + __popcll(act & ((1ull << lane) - 1))] = kb | (bits << 16);
+        count += __popcll(act);
+      }
+      if (lane == 0) blk_count = count;
+    }
+    __syncthreads();
+    nact = blk_count;
+  }
+  const int ntiles = BLOCKS ? nact : (kv_end - kv0 + kBc - 1) / kBc;
+  // first key (relative to kv0) of tile j; block-sparse tiles past the list start at the
+  // end of the sequence, so their loads read zeros and their keys are masked
+  auto tile_k0 = [&](int j) __attribute__((always_inline)) {
+    if constexpr (BLOCKS) return j < nact ? (blk_list[j] & 0xffff) * kBc : nk;
+    else return j * kBc;
+  };
+  // whether this wavefront's query block keeps tile j (block-sparse)
+  auto tile_kept = [&](int j) __attribute__((always_inline)) {
+    return j < nact && ((blk_list[j] >> (16 + (qw0 - q0) / kSparseBlock)) & 1) != 0;
+  };
 
   int koff[kKsteps];
 #pragma unroll
@@ -327,13 +379,13 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
   auto dma_k = [&](int j, int slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kKLoads; ++u) {
-      const unsigned row0 = (unsigned)(j * kBc + 8 * wv + u * kKRows);
+      const unsigned row0 = (unsigned)(tile_k0(j) + 8 * wv + u * kKRows);
       lds_byte* dst = lds_dma_dst(lds + slot * kTileBytes + (8 * wv + u * kKRows) * D * 2);
       dma16(krs, dst, row0 * row_bytes + k_lane_off[u]);
     }
   };
   auto load_v = [&](int j) __attribute__((always_inline)) {
-    const unsigned r0 = (unsigned)(j * kBc + 16 * (wv >> 1) + 4 * (wv & 1));
+    const unsigned r0 = (unsigned)(tile_k0(j) + 16 * (wv >> 1) + 4 * (wv & 1));
 #pragma unroll
     for (int r = 0; r < 8; ++r)
       vst[r] = __builtin_amdgcn_raw_buffer_load_b32(vrs, (r0 + (r & 3) + (r >> 2) * 8) * row_bytes + v_lane_off, 0, 0);
@@ -393,20 +445,22 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
   // masks the scores of tile j where some key of the tile is invisible to some query of
   // this wavefront (all of them for a tile the wavefront does not see at all)
   auto tile_needs_mask = [&](int j) __attribute__((always_inline)) {
-    const int k0 = kv0 + j * kBc;
+    const int k0 = kv0 + tile_k0(j);
     bool need = (k0 + kBc > N) || (CAUSAL && k0 + kBc - 1 > qw0);
     if constexpr (BAND) need = need || k0 + kBc - 1 > qw0 + a.wr || k0 < qw0 + 31 - a.wl;
+    if constexpr (BLOCKS) need = need || !tile_kept(j);
     return need;
   };
   auto mask_tile = [&](f32x16 (&s)[kKb], int j) __attribute__((always_inline)) {
-    const int k0 = kv0 + j * kBc;
+    const int k0 = kv0 + tile_k0(j);
     if (tile_needs_mask(j)) {
+      const bool kept = !BLOCKS || tile_kept(j);
 #pragma unroll
       for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = k0 + kb * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
-          bool dead = key >= N || (CAUSAL && key > qi);
+          bool dead = key >= N || (CAUSAL && key > qi) || !kept;
           if constexpr (BAND) dead = dead || key > qi + a.wr || key < qi - a.wl;
           s[kb][e] = dead ? -INFINITY : s[kb][e];
         }
@@ -448,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
     for (int ks = 0; ks < kKsteps; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < kKb; ++kb) {
-        const int key = min(j * kBc + kb * 32 + l32, nk - 1);
+        const int key = min(tile_k0(j) + kb * 32 + l32, nk - 1);
         const u32x4 ka = __builtin_amdgcn_raw_buffer_load_b128(krs, (unsigned)key * row_bytes + (unsigned)(ks * 16 + hi * 8) * 2u, 0, 0);
         s[kb] = Ops::mfma(ka, qreg[ks], s[kb]);
       }
@@ -540,7 +594,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
   // run the unmasked body; the rest (the ragged end, the causal diagonal, the band) run
   // the masked one. A choice per wavefront measured 2% slower than this uniform split.
   int clear_pairs = 0;
-  if constexpr (!BAND) {
+  if constexpr (!BAND && !BLOCKS) {
     const int in_range = (N - kv0) / kBc;
     clear_pairs = (CAUSAL ? min(in_range, (q0 + 1 - kv0) / kBc) : in_range) & ~1;
   }
@@ -561,7 +615,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
   // ---- epilogue -----------------------------------------------------------------------
   const float l_tot = pair_sum(l_run);
   if (qi < N) {
-    const float inv = 1.0f / l_tot;
+    const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;   // a row with no visible key: O = 0
     uint16_t* op = (uint16_t*)a.o + ((size_t)b * N + qi) * q_row_stride + (size_t)h * D;
 #pragma unroll
     for (int db = 0; db < kDblocks; ++db)
@@ -1020,6 +1074,9 @@ void fill_common(FwdArgs& args, const void* q, const void* k, const void* v, voi
   args.total = args.num_qtiles * H * B;
   args.q_scales = args.k_scales = args.v_scales = nullptr;
   args.nb = (N + FA_FP8_BLOCK_ROWS - 1) / FA_FP8_BLOCK_ROWS;
+  args.block_mask = nullptr;
+  args.mask_heads = 1;
+  args.nblk = (N + kSparseBlock - 1) / kSparseBlock;
 }
 
 fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -1059,6 +1116,11 @@ fa_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* 
   }
 }
 
+template <typename Ops, int D>
+fa_status launch_block_sparse(const FwdArgs& args, int causal, hipStream_t stream) {
+  return causal ? launch<Ops, D, kMaskBlockCausal>(args, stream) : launch<Ops, D, kMaskBlock>(args, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -1075,6 +1137,31 @@ fa_status fa_fwd_local(const void* q, const void* k, const void* v, void* o, flo
                        void* stream) {
   return fwd_impl(q, k, v, o, lse, B, H, Hkv, N, d, causal, window_left, window_right, scale, dtype,
                   descale_qkv, stream);
+}
+
+fa_status fa_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                              int H, int Hkv, int N, int d, int causal, const unsigned char* block_mask,
+                              int mask_heads, float scale, fa_dtype dtype, void* stream) {
+  fa_status st = check_sizes(B, H, Hkv, N, d, causal, dtype);
+  if (st != FA_OK) return st;
+  if (dtype == FA_DTYPE_FP8_E4M3) return FA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !o || !lse || !block_mask) return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
+    return FA_ERR_INVALID_ARG;
+  if (mask_heads != 1 && mask_heads != H) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  if ((N + kSparseBlock - 1) / kSparseBlock > kMaxSparseBlocks) return FA_ERR_UNSUPPORTED;
+  FwdArgs args;
+  fill_common(args, q, k, v, o, lse, B, H, Hkv, N);
+  args.c = (float)((double)scale * 1.4426950408889634);
+  args.v_scale = 1.0f;
+  args.wl = args.wr = N;
+  args.block_mask = block_mask;
+  args.mask_heads = mask_heads;
+  hipStream_t s = (hipStream_t)stream;
+  if (dtype == FA_DTYPE_BF16)
+    return d == 128 ? launch_block_sparse<Bf16Ops, 128>(args, causal, s) : launch_block_sparse<Bf16Ops, 64>(args, causal, s);
+  return d == 128 ? launch_block_sparse<F16Ops, 128>(args, causal, s) : launch_block_sparse<F16Ops, 64>(args, causal, s);
 }
 
 fa_status fa_fwd_fp8_block(const void* q, const void* k, const void* v, const unsigned char* q_scales,
@@ -1124,6 +1211,6 @@ const char* fa_status_string(fa_status s) {
   return "unknown fa_status";
 }
 
-int fa_version(void) { return 10100; }
+int fa_version(void) { return 10200; }
 
 }  // extern "C"

@@ -43,6 +43,8 @@ def lib() -> ctypes.CDLL:
             L.fa_fwd_local.argtypes = [vp, vp, vp, vp, vp] + [c_int] * 8 + [c_float, c_int,
                                                                             ctypes.POINTER(c_float), vp]
             L.fa_fwd_local.restype = c_int
+            L.fa_fwd_block_sparse.argtypes = [vp] * 5 + [c_int] * 6 + [vp, c_int, c_float, c_int, vp]
+            L.fa_fwd_block_sparse.restype = c_int
             L.fa_quantize_e4m3_block.argtypes = [vp, c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp]
             L.fa_quantize_e4m3_block.restype = c_int
             L.fa_fwd_fp8_block.argtypes = [vp] * 8 + [c_int] * 6 + [c_float, vp]
@@ -190,6 +192,51 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, descale=None,
                           Hkv, N, d, int(bool(causal)), int(window[0]), int(window[1]), scale, code,
                           descale, stream)
     _check(st)
+    return out, lse
+
+
+SPARSE_BLOCK = 64   # FA_SPARSE_BLOCK: queries and keys per block of a block-sparse mask
+
+
+def fa_fwd_block_sparse(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int, Hkv: int,
+                        N: int, d: int, causal: int, mask_ptr: int, mask_heads: int, scale: float, dtype: int,
+                        stream: int = 0) -> int:
+    """Direct call of fa_fwd_block_sparse with raw pointers; returns the status code."""
+    return int(lib().fa_fwd_block_sparse(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Hkv, N, d, int(causal),
+                                         mask_ptr, int(mask_heads), float(scale), int(dtype), stream))
+
+
+def fwd_block_sparse(q, k, v, block_mask, causal: bool = False, scale: float | None = None, out=None, lse=None,
+                     stream=None):
+    """Block-sparse attention forward on device tensors (float16 or bfloat16): query i of
+    head h sees key j iff block_mask[hm, i // 64, j // 64] != 0 (hm = 0 for a mask of one
+    head, else h; and j <= i when causal). block_mask is a contiguous uint8 device tensor
+    [1 or H, nb, nb], nb = ceil(N / 64). Rows with no visible key get O = 0, lse = -inf.
+    Returns (o [B,N,H,d], lse [B,H,N] float32) without synchronising."""
+    import torch
+    code = _dtype_code(q, None)
+    B, N, H, d = q.shape
+    Hkv = k.shape[2]
+    nb = (N + SPARSE_BLOCK - 1) // SPARSE_BLOCK
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    for t in (q, k, v, out, lse, block_mask):
+        if not t.is_contiguous() or t.device != q.device:
+            raise ValueError("tensors must be contiguous and on the same device")
+    if block_mask.dtype != torch.uint8 or block_mask.dim() != 3 or tuple(block_mask.shape[1:]) != (nb, nb) \
+            or block_mask.shape[0] not in (1, H):
+        raise ValueError(f"block_mask must be uint8 [1 or {H}, {nb}, {nb}]")
+    if tuple(k.shape) != (B, N, Hkv, d) or tuple(v.shape) != (B, N, Hkv, d):
+        raise ValueError("k and v must be [B,N,Hkv,d] matching q")
+    if tuple(out.shape) != (B, N, H, d) or out.dtype != q.dtype or tuple(lse.shape) != (B, H, N):
+        raise ValueError("out/lse have the wrong shape or type")
+    _check(fa_fwd_block_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Hkv,
+                               N, d, int(bool(causal)), block_mask.data_ptr(), block_mask.shape[0], scale, code,
+                               _stream(q, stream)))
     return out, lse
 
 

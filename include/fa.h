@@ -101,6 +101,31 @@ fa_status fa_fwd_local(const void* q, const void* k, const void* v, void* o, flo
                        int window_right, float scale, fa_dtype dtype,
                        const float* descale_qkv, void* stream);
 
+/* Queries and keys per block of a block-sparse mask. */
+#define FA_SPARSE_BLOCK 64
+
+/*
+ * Block-sparse attention: the block-sparse variant named in the abstract of
+ * "FlashAttention: Fast and Memory-Efficient Exact Attention with IO-Awareness", which
+ * the pages do not define further. The library's reading: `block_mask` is a device
+ * buffer of [mask_heads][nb][nb] bytes, nb = ceil(N / FA_SPARSE_BLOCK), row-major; key j
+ * is visible to query i of head h iff
+ *     block_mask[hm][i / FA_SPARSE_BLOCK][j / FA_SPARSE_BLOCK] != 0,
+ * hm = 0 when mask_heads = 1 (one mask for every head) and hm = h when mask_heads = H;
+ * causal = 1 further keeps only j <= i. Attention over the visible keys is exact. A
+ * query with no visible key has no softmax: its output row is 0 and its lse is -inf.
+ * The kernel visits, per query tile, only the key blocks that some query of the tile
+ * keeps, so the work scales with the number of kept blocks.
+ * F16 and BF16 only (FP8_E4M3 is FA_ERR_UNSUPPORTED); N <= 131072 (FA_ERR_UNSUPPORTED
+ * beyond); mask_heads must be 1 or H and block_mask non-null (else
+ * FA_ERR_INVALID_ARG). The mask is only read. Every other argument, layout, ownership
+ * rule and error is as for fa_fwd.
+ */
+fa_status fa_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int H, int Hkv, int N, int d, int causal,
+                              const unsigned char* block_mask, int mask_heads, float scale,
+                              fa_dtype dtype, void* stream);
+
 /* Rows (sequence positions) per block of the e4m3 block quantisation. */
 #define FA_FP8_BLOCK_ROWS 64
 
@@ -207,7 +232,7 @@ fa_status fa_fwd_query(int B, int H, int Hkv, int N, int d, int causal, fa_dtype
 /* Static, human-readable text for a status code. */
 const char* fa_status_string(fa_status s);
 
-/* Library version, encoded as major * 10000 + minor * 100 + patch (10100: fa_fwd_local). */
+/* Library version, encoded as major * 10000 + minor * 100 + patch (10200: fa_fwd_block_sparse). */
 int fa_version(void);
 
 #ifdef __cplusplus

@@ -42,6 +42,7 @@ class Workload:
     fp8_block: bool = False         # e4m3 block-quantised on the GPU (drawn as bf16, rotated Q/K)
     backward: bool = False          # the gradient pass (upstream dO drawn with seed + 100)
     decode_nq: int = 0              # split-KV decode: Nq queries against N keys (0: square)
+    sparse_density: float = 0.0     # block-sparse: share of random key blocks kept (0: dense)
 
     @property
     def flops(self) -> float:
@@ -54,6 +55,9 @@ class Workload:
             nq, nk = self.decode_nq, self.N
             pairs = nq * nk - (nq * (nq - 1) // 2 if self.causal else 0)
             return 4.0 * self.B * self.H * self.d * pairs
+        if self.sparse_density:
+            return 4.0 * self.B * self.d * float(block_mask_pairs(workload_block_mask(self), self.N, self.causal,
+                                                                   self.H))
         if self.window is None:
             f = 4.0 * self.B * self.H * self.N * self.N * self.d
             return f / 2 if self.causal else f
@@ -94,8 +98,62 @@ WORKLOADS = {
         _w("bwd_bf16_b16_h16_n2048_d128", 16, 16, 16, 2048, 128, False, "bf16", 1002, backward=True),
         _w("bwd_causal_gqa_bf16_b4_h32_kv8_n8192_d128", 4, 32, 8, 8192, 128, True, "bf16", 1004, backward=True),
         _w("decode_bf16_b8_h32_kv8_nq1_nk16384_d128", 8, 32, 8, 16384, 128, False, "bf16", 1007, decode_nq=1),
+        _w("block_sparse_bf16_b1_h16_n16384_d128", 1, 16, 16, 16384, 128, False, "bf16", 1008,
+           sparse_density=0.1),
     ]
 }
+
+SPARSE_BLOCK = 64      # queries and keys per block of a block-sparse mask
+
+
+def random_block_mask(heads: int, N: int, density: float, seed: int, block: int = SPARSE_BLOCK) -> np.ndarray:
+    """uint8 [heads, nb, nb] mask with each block kept with probability `density`
+    (nb = ceil(N / block)), from numpy PCG64(seed)."""
+    nb = (N + block - 1) // block
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return (rng.random((heads, nb, nb)) < density).astype(np.uint8)
+
+
+def bigbird_block_mask(heads: int, N: int, density: float, seed: int, group: int = 4,
+                       block: int = SPARSE_BLOCK) -> np.ndarray:
+    """uint8 [heads, nb, nb] block mask in the local + global + random pattern of
+    long-context sparse attention: for every group of `group` query blocks (the rows of a
+    256-query tile at 64-row blocks), the key blocks of the three neighbouring groups, the
+    first group of key blocks, and each other key block with probability `density`; rows
+    of one group share their key blocks. From numpy PCG64(seed)."""
+    nb = (N + block - 1) // block
+    ng = (nb + group - 1) // group
+    rng = np.random.Generator(np.random.PCG64(seed))
+    keep_g = rng.random((heads, ng, nb)) < density
+    kb_group = np.arange(nb) // group
+    for g in range(ng):
+        keep_g[:, g, (np.abs(kb_group - g) <= 1) | (kb_group == 0)] = True
+    return np.repeat(keep_g, group, axis=1)[:, :nb].astype(np.uint8)
+
+
+def block_mask_pairs(mask: np.ndarray, N: int, causal: bool, H: int, block: int = SPARSE_BLOCK) -> int:
+    """Visible (query, key) pairs summed over the H query heads (a mask of one head
+    applies to all): rows x keys of every kept block, ragged last block included, and under
+    the causal mask only the pairs with key <= query."""
+    nb = mask.shape[1]
+    sizes = np.minimum(block, N - np.arange(nb) * block).astype(np.int64)
+    per = mask.astype(np.int64) * np.outer(sizes, sizes)[None]
+    if causal:
+        qi = np.arange(N)
+        below = np.zeros((nb, nb), dtype=np.int64)            # pairs with key <= query per block pair
+        for qb in range(nb):
+            rows = qi[qb * block:(qb + 1) * block]
+            for kb in range(qb + 1):
+                lo, hi = kb * block, min(N, (kb + 1) * block) - 1
+                below[qb, kb] = int(np.sum(np.clip(np.minimum(rows, hi) - lo + 1, 0, None)))
+        per = mask.astype(np.int64) * below[None]
+    total = int(per.sum())
+    return total * (H // mask.shape[0])
+
+
+def workload_block_mask(w: Workload) -> np.ndarray:
+    """The block mask of a block-sparse workload (one per query head)."""
+    return bigbird_block_mask(w.H, w.N, w.sparse_density, w.seed + 200)
 
 E4M3_MAX = 448.0
 

@@ -23,7 +23,8 @@ def declared_functions():
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert set(names) >= {"fa_fwd", "fa_fwd_local", "fa_fwd_query", "fa_status_string", "fa_version"}
+    assert set(names) >= {"fa_fwd", "fa_fwd_local", "fa_fwd_block_sparse", "fa_fwd_query", "fa_status_string",
+                          "fa_version"}
     lib = ctypes.CDLL(binding.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), f"libfa.so does not export {n}"
@@ -122,6 +123,28 @@ def test_fwd_local_rejects_before_launch(over, status, window):
     a.update(over)
     st = fa.fa_fwd_local(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"], a["d"],
                          a["causal"], window[0], window[1], a["scale"], a["dtype"], a["descale"])
+    assert st == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(mask=0), fa.FA_ERR_INVALID_ARG),
+    (dict(mask_heads=2), fa.FA_ERR_INVALID_ARG),       # neither 1 nor H
+    (dict(mask_heads=0), fa.FA_ERR_INVALID_ARG),
+    (dict(o=FAKE + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=3), fa.FA_ERR_INVALID_ARG),
+    (dict(dtype=fa.FA_DTYPE_FP8_E4M3), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(N=131072 + 64, H=1, Hkv=1), fa.FA_ERR_UNSUPPORTED),   # more than 2048 mask blocks per row
+])
+def test_fwd_block_sparse_rejects_before_launch(over, status):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=4, Hkv=2, N=300, d=128, causal=0, mask=FAKE,
+             mask_heads=1, scale=0.125, dtype=fa.FA_DTYPE_BF16)
+    a.update(over)
+    st = fa.fa_fwd_block_sparse(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["N"],
+                                a["d"], a["causal"], a["mask"], a["mask_heads"], a["scale"], a["dtype"])
     assert st == status
 
 
