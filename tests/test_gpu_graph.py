@@ -1,5 +1,5 @@
-"""The library inside HIP graphs and on a non-default stream (GPU): forward, gradient and
-split-KV decode are captured once into a torch CUDA graph (hipGraph) with preallocated
+"""The library inside HIP graphs and on a non-default stream (GPU): forward (plain,
+key-window and block-sparse), gradient and split-KV decode are captured once into a torch CUDA graph (hipGraph) with preallocated
 outputs and workspaces, replayed several times with eager work in between, and every
 replay must equal the eager result bit for bit. The kernels enqueue no memset and
 allocate nothing, so capture needs no special path."""
@@ -33,11 +33,16 @@ def test_graph_replays_match_eager():
     od = torch.empty_like(dq_)
     lsed = torch.empty(2, 8, 2, device="cuda")
     wsd = torch.empty(fa.fa_fwd_splitkv_workspace_bytes(2, 8, 2, 2, 500, d, 4) // 4, device="cuda")
+    ow, lsew = torch.empty_like(q), torch.empty(B, H, N, device="cuda")
+    os_, lses = torch.empty_like(q), torch.empty(B, H, N, device="cuda")
+    bmask = torch.from_numpy(synth_inputs.random_block_mask(H, N, 0.5, seed=24)).cuda()
 
     def work():
         fa.fwd(q, k, v, causal=True, out=o, lse=lse)
         fa.bwd(q, k, v, o, lse, do, causal=True, dq=grads[0], dk=grads[1], dv=grads[2], workspace=ws)
         fa.fwd_splitkv(dq_, dk_, dv_, causal=True, num_splits=4, out=od, lse=lsed, workspace=wsd)
+        fa.fwd(q, k, v, causal=True, window=(100, -1), out=ow, lse=lsew)
+        fa.fwd_block_sparse(q, k, v, bmask, causal=False, out=os_, lse=lses)
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -45,18 +50,19 @@ def test_graph_replays_match_eager():
         work()                                   # warm-up on the capture stream
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    eager = [t.clone() for t in (o, lse, *grads, od, lsed)]
+    eager = [t.clone() for t in (o, lse, *grads, od, lsed, ow, lsew, os_, lses)]
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         work()
     for rep in range(3):
-        for t in (o, lse, *grads, od, lsed):
+        for t in (o, lse, *grads, od, lsed, ow, lsew, os_, lses):
             t.fill_(float("nan")) if t.dtype == torch.float32 else t.zero_()
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        for name, a, b in zip(("o", "lse", "dq", "dk", "dv", "o_dec", "lse_dec"), (o, lse, *grads, od, lsed), eager):
+        names = ("o", "lse", "dq", "dk", "dv", "o_dec", "lse_dec", "o_win", "lse_win", "o_sparse", "lse_sparse")
+        for name, a, b in zip(names, (o, lse, *grads, od, lsed, ow, lsew, os_, lses), eager):
             assert torch.equal(_bits(a), _bits(b)), f"replay {rep}: {name} differs from eager"
         _ = (q.float() * 2).sum().item()         # unrelated eager work between replays
 
