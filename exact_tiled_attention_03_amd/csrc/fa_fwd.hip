@@ -271,8 +271,9 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
 
   // K slot 0, K slot 1, V^T slot 0, V^T slot 1
   __shared__ __attribute__((aligned(16))) unsigned char lds[4 * kTileBytes];
-  // block-sparse: the workgroup's active key blocks, each entry kb | (q-block bits << 16)
-  __shared__ int blk_list[BLOCKS ? kMaxSparseBlocks : 1];
+  // block-sparse: the workgroup's active key blocks, each entry kb | (q-block bits << 16),
+  // then four entries -1 (past the end)
+  __shared__ __attribute__((aligned(16))) int blk_list[BLOCKS ? kMaxSparseBlocks + 4 : 1];
   __shared__ int blk_count;
 
   const int tid = threadIdx.x;
@@ -327,20 +328,41 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
         count += __popcll(act);
       }
       if (lane == 0) blk_count = count;
+      if (lane < 4) blk_list[count + lane] = -1;
     }
     __syncthreads();
     nact = blk_count;
   }
   const int ntiles = BLOCKS ? nact : (kv_end - kv0 + kBc - 1) / kBc;
-  // first key (relative to kv0) of tile j; block-sparse tiles past the list start at the
-  // end of the sequence, so their loads read zeros and their keys are masked
-  auto tile_k0 = [&](int j) __attribute__((always_inline)) {
-    if constexpr (BLOCKS) return j < nact ? (blk_list[j] & 0xffff) * kBc : nk;
+  // Block-sparse: the list entry of tile j (-1 past the end, up to tile nact + 3) in a
+  // uniform register. The loops below read the four entries of a pair of steps at once,
+  // so that no list read waits among the operand reads of a step.
+  auto tile_entry = [&](int j) __attribute__((always_inline)) {
+    if constexpr (BLOCKS) return __builtin_amdgcn_readfirstlane(blk_list[j]);
+    else return 0;
+  };
+  auto pair_entries = [&](int j, int (&e)[4]) __attribute__((always_inline)) {   // j even
+    if constexpr (BLOCKS) {
+      const int2 x = *(const int2*)&blk_list[j];
+      const int2 y = *(const int2*)&blk_list[j + 2];
+      e[0] = __builtin_amdgcn_readfirstlane(x.x);
+      e[1] = __builtin_amdgcn_readfirstlane(x.y);
+      e[2] = __builtin_amdgcn_readfirstlane(y.x);
+      e[3] = __builtin_amdgcn_readfirstlane(y.y);
+    } else {
+      e[0] = e[1] = e[2] = e[3] = 0;
+    }
+  };
+  // first key (relative to kv0) of tile j with list entry e; block-sparse tiles past the
+  // list start at the end of the sequence, so their loads read zeros and their keys are
+  // masked
+  auto tile_k0 = [&](int j, int e) __attribute__((always_inline)) {
+    if constexpr (BLOCKS) return e < 0 ? nk : (e & 0xffff) * kBc;
     else return j * kBc;
   };
-  // whether this wavefront's query block keeps tile j (block-sparse)
-  auto tile_kept = [&](int j) __attribute__((always_inline)) {
-    return j < nact && ((blk_list[j] >> (16 + (qw0 - q0) / kSparseBlock)) & 1) != 0;
+  // whether this wavefront's query block keeps the tile with list entry e (block-sparse)
+  auto tile_kept = [&](int e) __attribute__((always_inline)) {
+    return e >= 0 && ((e >> (16 + (qw0 - q0) / kSparseBlock)) & 1) != 0;
   };
 
   int koff[kKsteps];
@@ -376,16 +398,16 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
   const int vlane = min(lane, D / 2 - 1);
   const unsigned v_lane_off = (unsigned)vlane * 4u;
   unsigned vst[8];
-  auto dma_k = [&](int j, int slot) __attribute__((always_inline)) {
+  auto dma_k = [&](int k0, int slot) __attribute__((always_inline)) {   // k0: first key of the tile
 #pragma unroll
     for (int u = 0; u < kKLoads; ++u) {
-      const unsigned row0 = (unsigned)(tile_k0(j) + 8 * wv + u * kKRows);
+      const unsigned row0 = (unsigned)(k0 + 8 * wv + u * kKRows);
       lds_byte* dst = lds_dma_dst(lds + slot * kTileBytes + (8 * wv + u * kKRows) * D * 2);
       dma16(krs, dst, row0 * row_bytes + k_lane_off[u]);
     }
   };
-  auto load_v = [&](int j) __attribute__((always_inline)) {
-    const unsigned r0 = (unsigned)(tile_k0(j) + 16 * (wv >> 1) + 4 * (wv & 1));
+  auto load_v = [&](int k0) __attribute__((always_inline)) {
+    const unsigned r0 = (unsigned)(k0 + 16 * (wv >> 1) + 4 * (wv & 1));
 #pragma unroll
     for (int r = 0; r < 8; ++r)
       vst[r] = __builtin_amdgcn_raw_buffer_load_b32(vrs, (r0 + (r & 3) + (r >> 2) * 8) * row_bytes + v_lane_off, 0, 0);
@@ -442,25 +464,25 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
       for (int db = 0; db < kDblocks; ++db)
         oacc[db] = Ops::mfma(lds_load<u32x4>(st, voff[db] + kk * (D * 32)), p[kk >> 1][kk & 1], oacc[db]);
   };
-  // masks the scores of tile j where some key of the tile is invisible to some query of
-  // this wavefront (all of them for a tile the wavefront does not see at all)
-  auto tile_needs_mask = [&](int j) __attribute__((always_inline)) {
-    const int k0 = kv0 + tile_k0(j);
+  // masks the scores of the tile starting at key kv0 + k0r where some key of the tile is
+  // invisible to some query of this wavefront (all of them for a tile the wavefront does
+  // not see at all; KEPT is whether its query block keeps the tile, block-sparse)
+  auto tile_needs_mask = [&](int k0r, bool kept) __attribute__((always_inline)) {
+    const int k0 = kv0 + k0r;
     bool need = (k0 + kBc > N) || (CAUSAL && k0 + kBc - 1 > qw0);
     if constexpr (BAND) need = need || k0 + kBc - 1 > qw0 + a.wr || k0 < qw0 + 31 - a.wl;
-    if constexpr (BLOCKS) need = need || !tile_kept(j);
+    if constexpr (BLOCKS) need = need || !kept;
     return need;
   };
-  auto mask_tile = [&](f32x16 (&s)[kKb], int j) __attribute__((always_inline)) {
-    const int k0 = kv0 + tile_k0(j);
-    if (tile_needs_mask(j)) {
-      const bool kept = !BLOCKS || tile_kept(j);
+  auto mask_tile = [&](f32x16 (&s)[kKb], int k0r, bool kept) __attribute__((always_inline)) {
+    const int k0 = kv0 + k0r;
+    if (tile_needs_mask(k0r, kept)) {
 #pragma unroll
       for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int key = k0 + kb * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
-          bool dead = key >= N || (CAUSAL && key > qi) || !kept;
+          bool dead = key >= N || (CAUSAL && key > qi) || (BLOCKS && !kept);
           if constexpr (BAND) dead = dead || key > qi + a.wr || key < qi - a.wl;
           s[kb][e] = dead ? -INFINITY : s[kb][e];
         }
@@ -493,7 +515,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
   // may already hold K(j+2) from another wavefront). The operands are the ones staged to
   // LDS, so the scores are bit for bit the first ones, except for rows past the end of
   // the sequence (read here as row nk-1, there as zeros), whose keys are masked.
-  auto s_global = [&](f32x16 (&s)[kKb], int j) __attribute__((always_inline)) {
+  auto s_global = [&](f32x16 (&s)[kKb], int k0r) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
@@ -502,7 +524,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
     for (int ks = 0; ks < kKsteps; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < kKb; ++kb) {
-        const int key = min(tile_k0(j) + kb * 32 + l32, nk - 1);
+        const int key = min(k0r + kb * 32 + l32, nk - 1);
         const u32x4 ka = __builtin_amdgcn_raw_buffer_load_b128(krs, (unsigned)key * row_bytes + (unsigned)(ks * 16 + hi * 8) * 2u, 0, 0);
         s[kb] = Ops::mfma(ka, qreg[ks], s[kb]);
       }
@@ -526,11 +548,14 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
   // beside the LDS stores of V(j+1) and the global loads of V(j+2); the caller then takes
   // the barrier. MASKED_C selects the body that masks tile j; a tile that needs no mask
   // skips the per-score compares and selects altogether.
-  auto step = [&](f32x16 (&sc)[kKb], f32x16 (&sn)[kKb], auto par_c, int j, auto masked_c) __attribute__((always_inline)) {
+  auto step = [&](f32x16 (&sc)[kKb], f32x16 (&sn)[kKb], auto par_c, int j, auto masked_c, int ej, int en)
+      __attribute__((always_inline)) {   // ej, en: the list entries of tiles j and j+2
     constexpr int par = decltype(par_c)::value;   // j & 1
     constexpr bool kMasked = decltype(masked_c)::value;
-    dma_k(j + 2, par);      // K slot j&1 was last read by S(j), before the previous barrier
-    if constexpr (kMasked) mask_tile(sc, j);
+    const int k0j = tile_k0(j, ej), k0n = tile_k0(j + 2, en);
+    const bool kept = !BLOCKS || tile_kept(ej);
+    dma_k(k0n, par);        // K slot j&1 was last read by S(j), before the previous barrier
+    if constexpr (kMasked) mask_tile(sc, k0j, kept);
     // a row that has seen no visible key yet (m_run = -FLT_MAX) takes the tile's maximum
     // before its exponentials
     if (__builtin_amdgcn_ballot_w64(m_run == -__FLT_MAX__) != 0) rescale_to(sc);
@@ -551,15 +576,15 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
       // a score grew past m_run by more than log2(kPMax): the scores were consumed in
       // place, so they are computed again, then the tile's maximum and the probabilities
       f32x16 sr[kKb];
-      s_global(sr, j);
-      if constexpr (kMasked) mask_tile(sr, j);
+      s_global(sr, k0j);
+      if constexpr (kMasked) mask_tile(sr, k0j, kept);
       rescale_to(sr);
       lsum = exponentials(sr);
     }
     l_run += lsum;
     pv_mfma(par);
     store_v(par ^ 1);
-    load_v(j + 2);
+    load_v(k0n);
     // P.V operand reads kLead ahead, the V staging spread between the MFMAs
     constexpr int kPOps = kDblocks * 2 * kKb;
     __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
@@ -577,11 +602,14 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
   };
 
   // prologue: K(0), K(1) and V(0) in LDS, V(1) in registers, S(0) computed
-  dma_k(0, 0);
-  dma_k(1, 1);
-  load_v(0);
-  store_v(0);
-  load_v(1);
+  {
+    const int k00 = tile_k0(0, tile_entry(0)), k01 = tile_k0(1, tile_entry(1));
+    dma_k(k00, 0);
+    dma_k(k01, 1);
+    load_v(k00);
+    store_v(0);
+    load_v(k01);
+  }
   __builtin_amdgcn_s_waitcnt(kVmcnt8);
   __syncthreads();
   s_mfma(sA, 0);
@@ -590,26 +618,60 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
   // tiles go in pairs; an odd count gets one more tile, past kv_end, whose keys are all
   // masked for every query of the workgroup (probability 0)
   // Pairs of tiles that every wavefront of the workgroup sees whole (all keys in range
-  // and, under the causal mask, at or before the workgroup's first query) come first and
-  // run the unmasked body; the rest (the ragged end, the causal diagonal, the band) run
-  // the masked one. A choice per wavefront measured 2% slower than this uniform split.
-  int clear_pairs = 0;
-  if constexpr (!BAND && !BLOCKS) {
-    const int in_range = (N - kv0) / kBc;
-    clear_pairs = (CAUSAL ? min(in_range, (q0 + 1 - kv0) / kBc) : in_range) & ~1;
-  }
+  // and, under the causal mask, at or before the workgroup's first query) run the
+  // unmasked body: a prefix of the loop for the dense masks, pairs chosen at run time
+  // (uniformly for the workgroup) from the block-sparse list. The rest (the ragged end,
+  // the causal diagonal, the band, tiles some query block does not keep) run the masked
+  // one. A choice per wavefront measured 2% slower than this uniform split.
   int j = 0;
-  for (; j < clear_pairs; j += 2) {
-    step(sA, sB, ic<0>(), j, std::false_type{});
-    __syncthreads();
-    step(sB, sA, ic<1>(), j + 1, std::false_type{});
-    __syncthreads();
-  }
-  for (; j < ntiles; j += 2) {
-    step(sA, sB, ic<0>(), j, std::true_type{});
-    __syncthreads();
-    step(sB, sA, ic<1>(), j + 1, std::true_type{});
-    __syncthreads();
+  int e[4];
+  if constexpr (BLOCKS) {
+    // a listed tile is clear when every query block of the workgroup keeps it, it is whole
+    // and, under the causal mask, it ends at or before the workgroup's first query
+    const int qb_valid = min(kBr / kSparseBlock, a.nblk - q0 / kSparseBlock);
+    const int all_bits = (1 << qb_valid) - 1;
+    auto clear = [&](int ent) __attribute__((always_inline)) {
+      const int k0 = (ent & 0xffff) * kBc;
+      return ent >= 0 && ((ent >> 16) & all_bits) == all_bits && k0 + kBc <= N && (!CAUSAL || k0 + kBc - 1 <= q0);
+    };
+    // runs of clear pairs and of the other pairs alternate
+    while (j < ntiles) {
+      for (; j < ntiles; j += 2) {
+        pair_entries(j, e);
+        if (!(clear(e[0]) && clear(e[1]))) break;
+        step(sA, sB, ic<0>(), j, std::false_type{}, e[0], e[2]);
+        __syncthreads();
+        step(sB, sA, ic<1>(), j + 1, std::false_type{}, e[1], e[3]);
+        __syncthreads();
+      }
+      for (; j < ntiles; j += 2) {
+        pair_entries(j, e);
+        if (clear(e[0]) && clear(e[1])) break;
+        step(sA, sB, ic<0>(), j, std::true_type{}, e[0], e[2]);
+        __syncthreads();
+        step(sB, sA, ic<1>(), j + 1, std::true_type{}, e[1], e[3]);
+        __syncthreads();
+      }
+    }
+  } else {
+    pair_entries(0, e);
+    int clear_pairs = 0;
+    if constexpr (!BAND) {
+      const int in_range = (N - kv0) / kBc;
+      clear_pairs = (CAUSAL ? min(in_range, (q0 + 1 - kv0) / kBc) : in_range) & ~1;
+    }
+    for (; j < clear_pairs; j += 2) {
+      step(sA, sB, ic<0>(), j, std::false_type{}, e[0], e[2]);
+      __syncthreads();
+      step(sB, sA, ic<1>(), j + 1, std::false_type{}, e[1], e[3]);
+      __syncthreads();
+    }
+    for (; j < ntiles; j += 2) {
+      step(sA, sB, ic<0>(), j, std::true_type{}, e[0], e[2]);
+      __syncthreads();
+      step(sB, sA, ic<1>(), j + 1, std::true_type{}, e[1], e[3]);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue -----------------------------------------------------------------------
