@@ -66,6 +66,13 @@ constexpr int kThreads = 256;          // preprocess kernel
 // dK/dV kernel: keys per wavefront and wavefronts per workgroup. The kernel is written for
 // any multiple of 16 keys; 32 keys halve the LDS reads per MFMA but need one wavefront per
 // SIMD for their registers, and measured 11% slower than two wavefronts of 16 keys.
+// s_waitcnt operand: vmcnt(0), expcnt and lgkmcnt not waited for. Both gradient kernels
+// wait for all of their prologue loads before the tile loop. Without that wait the
+// compiler's wait analysis merges the loop's entry state, in which the loads of the
+// operands kept in registers may still be in flight, into the loop head, and then waits
+// inside every tile for those loads and for every load issued after them, the next
+// tile's staging loads included (3% of the gradient's time at B16 H16 N2048 d128).
+constexpr int kVmcnt0 = 0x0F70;
 constexpr int kKeysPerWaveKV = 16;
 constexpr int kWavesKV = 128 / kKeysPerWaveKV;
 constexpr int kWavesQ = 8;             // dQ kernel: wavefronts per workgroup, 32 queries each
@@ -477,6 +484,7 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
   load_tile(0, std::integral_constant<int, 0>{});
   store_tile(std::integral_constant<int, 0>{});
   if (1 < T) load_tile(1, std::integral_constant<int, 1>{});
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
 
   // tile t of parity par: loads of tile t+2 into register set par (stored at the end of
@@ -745,6 +753,7 @@ __global__ __launch_bounds__(64 * kWavesQ) void bwd_dq_kernel(BwdArgs a) {
 
   load_tile(0);
   store_tile(0);
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
   __syncthreads();
 
   // S(0) E(0) | S(1) | dQ(0) E(1) | dQ(1) staging, two 32-key blocks per tile (the first
