@@ -284,12 +284,16 @@ __global__ __launch_bounds__(kThreads) void splitkv_merge_kernel(SkvArgs a) {
   const int nrows = a.B * a.H * a.Nq;
   if (row >= nrows) return;
   const size_t plane = (size_t)nrows;                    // rows per split
+  // the loops over the ranges are unrolled so that several ranges' loads are in flight
+  // at once (one range at a time left the kernel waiting on one load latency per range)
   float m = -INFINITY;
+#pragma unroll 8
   for (int s = 0; s < a.S; ++s) m = fmaxf(m, a.part_lse[s * plane + row]);
   float w_sum = 0.0f;
   float acc[kPer];
 #pragma unroll
   for (int t = 0; t < kPer; ++t) acc[t] = 0.0f;
+#pragma unroll 8
   for (int s = 0; s < a.S; ++s) {
     const float ls = a.part_lse[s * plane + row];
     const float w = ls == -INFINITY ? 0.0f : __expf(ls - m);
