@@ -704,17 +704,30 @@ __global__ __launch_bounds__(64 * kWavesQ) void bwd_dq_kernel(BwdArgs a) {
   //   tr_byte(32dbk + l32, 32kb + 16t2 + 8hi) = (tr_lane ^ 16(4kb ^ 2(t2 ^ dbk%2))) + 4096dbk
   const int rm_lane = l32 * (2 * D) + (((hi ^ rswz(l32)) & (kChunks - 1)) << 4);
   const int tr_lane = l32 * (2 * kBk) + (((hi ^ ((l32 >> 1) & 7) ^ (l32 >> 4)) & 7) << 4);
-  // S^T and dP^T of a 32-key block, then P and dS^T of it as B operands of dQ^T += K^T dS^T
+  // S^T and dP^T of a 32-key block, then P and dS^T of it as B operands of dQ^T += K^T dS^T.
+  // In both MFMA loops below the operand reads run ahead of their MFMAs (four reads for
+  // S/dP, three for dQ) in the source order, and a scheduling barrier after each MFMA
+  // keeps that order: left to itself, the scheduler put each read right before its MFMA
+  // behind a full LDS wait (the dQ kernel 4-6% slower).
   auto s_mfma = [&](int rmb, int kb, f32x16& s, f32x16& dp) __attribute__((always_inline)) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) s[e] = dp[e] = 0.0f;
+    auto off = [&](int ks) { return (rmb ^ (ks << 5)) + kb * 32 * (2 * D); };
+    u32x4 ka[kKsteps], va[kKsteps];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      ka[ks] = lds_read<u32x4>(lds, off(ks));
+      va[ks] = lds_read<u32x4>(lds + kTile, off(ks));
+    }
 #pragma unroll
     for (int ks = 0; ks < kKsteps; ++ks) {
-      const int off = (rmb ^ (ks << 5)) + kb * 32 * (2 * D);
-      const u32x4 ka = lds_read<u32x4>(lds, off);
-      const u32x4 va = lds_read<u32x4>(lds + kTile, off);
-      s = Ops::mfma(ka, qreg[ks], s);
-      dp = Ops::mfma(va, dreg[ks], dp);
+      if (ks + 2 < kKsteps) {
+        ka[ks + 2] = lds_read<u32x4>(lds, off(ks + 2));
+        va[ks + 2] = lds_read<u32x4>(lds + kTile, off(ks + 2));
+      }
+      s = Ops::mfma(ka[ks], qreg[ks], s);
+      dp = Ops::mfma(va[ks], dreg[ks], dp);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   // Masks apply only where a key is past the end or (causal) after the lane's query.
@@ -738,18 +751,21 @@ __global__ __launch_bounds__(64 * kWavesQ) void bwd_dq_kernel(BwdArgs a) {
   };
   // dQ^T += K^T dS^T: A = K^T (dim 32 dbk + l32, slots kb*32 + 16 t2 + 8 hi .. +7)
   auto q_mfma = [&](int trb, int kb, const u32x4 (&db)[2]) __attribute__((always_inline)) {
+    constexpr int kN = 2 * kDblocks;
+    auto off = [&](int i) {
+      const int t2 = i / kDblocks, dbk = i % kDblocks;
+      return (trb ^ ((4 * kb ^ 2 * (t2 ^ (dbk & 1))) << 4)) + dbk * 32 * (2 * kBk);
+    };
+    u32x4 ka[kN];
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2)
+    for (int i = 0; i < 3; ++i) ka[i] = lds_read<u32x4>(lds + 2 * kTile, off(i));
 #pragma unroll
-      for (int dbk = 0; dbk < kDblocks; ++dbk) {
-        const int off = (trb ^ ((4 * kb ^ 2 * (t2 ^ (dbk & 1))) << 4)) + dbk * 32 * (2 * kBk);
-        const u32x4 ka = lds_read<u32x4>(lds + 2 * kTile, off);
-        dqT[dbk] = Ops::mfma(ka, db[t2], dqT[dbk]);
-      }
+    for (int i = 0; i < kN; ++i) {
+      if (i + 3 < kN) ka[i + 3] = lds_read<u32x4>(lds + 2 * kTile, off(i + 3));
+      dqT[i % kDblocks] = Ops::mfma(ka[i], db[i / kDblocks], dqT[i % kDblocks]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
-  constexpr int kSM = 2 * kKsteps;           // MFMAs of an S phase, one LDS read each
-  constexpr int kQM = 2 * kDblocks;          // MFMAs of a dQ phase, one LDS read each
-  constexpr int kLead = 4;                   // operand reads ahead of their MFMA
 
   load_tile(0);
   store_tile(0);
@@ -769,43 +785,16 @@ __global__ __launch_bounds__(64 * kWavesQ) void bwd_dq_kernel(BwdArgs a) {
     f32x16 s0, dp0, s1, dp1;
     u32x4 db0[2], db1[2];
     s_mfma(rmb, 0, s0, dp0);
-    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
-#pragma unroll
-    for (int i = 0; i < kSM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < kSM - kLead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
     __builtin_amdgcn_sched_barrier(0);
     softmax(masked_c, j0, 0, s0, dp0, db0);
     __builtin_amdgcn_sched_barrier(0);
     s_mfma(rmb, 1, s1, dp1);
-    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
-#pragma unroll
-    for (int i = 0; i < kSM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < kSM - kLead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
     __builtin_amdgcn_sched_barrier(0);
     q_mfma(trb, 0, db0);
     softmax(masked_c, j0, 1, s1, dp1, db1);
-    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
-#pragma unroll
-    for (int i = 0; i < kQM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < kQM - kLead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
-    }
     __builtin_amdgcn_sched_barrier(0);
     q_mfma(trb, 1, db1);
     store_tile((t + 1) & 1);   // after the last tile: an unused buffer
-    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
-#pragma unroll
-    for (int i = 0; i < kQM; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < kQM - kLead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);
-    }
     __builtin_amdgcn_sched_barrier(0);
   };
   if (!CAUSAL) {
