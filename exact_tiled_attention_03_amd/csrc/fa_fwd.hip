@@ -914,26 +914,41 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
     }
   };
 
+  // In both parts the operand reads run ahead of their MFMAs in the source order (four K
+  // reads; the V reads of two d-blocks), and a scheduling barrier after each MFMA keeps
+  // that order; the scheduler otherwise put each read right before its MFMA.
   auto s_part = [&](const lds_byte* st) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < kKb; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[kb][e] = 0.0f;
+    constexpr int kN = kKsteps * kKb, kAhead = 4;
+    u32x4 ka[kN];
 #pragma unroll
-    for (int ks = 0; ks < kKsteps; ++ks)
+    for (int i = 0; i < kAhead; ++i) ka[i] = lds_load<u32x4>(st, koff[i / kKb] + (i % kKb) * 32 * D * 2);
 #pragma unroll
-      for (int kb = 0; kb < kKb; ++kb) {
-        const u32x4 ka = lds_load<u32x4>(st, koff[ks] + kb * 32 * D * 2);
-        s[kb] = Bf16Ops::mfma(ka, qreg[ks], s[kb]);
-      }
+    for (int i = 0; i < kN; ++i) {
+      if (i + kAhead < kN) ka[i + kAhead] = lds_load<u32x4>(st, koff[(i + kAhead) / kKb] + ((i + kAhead) % kKb) * 32 * D * 2);
+      s[i % kKb] = Bf16Ops::mfma(ka[i], qreg[i / kKb], s[i % kKb]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   auto pv_part = [&](const lds_byte* st) __attribute__((always_inline)) {
+    u32x4 a0[kDblocks], a1[kDblocks];
+#pragma unroll
+    for (int db = 0; db < 2 && db < kDblocks; ++db) {
+      a0[db] = lds_load<u32x4>(st, voff[db][0]);
+      a1[db] = lds_load<u32x4>(st, voff[db][1]);
+    }
 #pragma unroll
     for (int db = 0; db < kDblocks; ++db) {
-      const u32x4 a0 = lds_load<u32x4>(st, voff[db][0]);
-      const u32x4 a1 = lds_load<u32x4>(st, voff[db][1]);
-      if constexpr (BLOCK) oacc[db] = mfma_fp8_scaled(a0, a1, p[0], p[1], oacc[db], v_sc);
-      else oacc[db] = mfma_fp8(a0, a1, p[0], p[1], oacc[db]);
+      if (db + 2 < kDblocks) {
+        a0[db + 2] = lds_load<u32x4>(st, voff[db + 2][0]);
+        a1[db + 2] = lds_load<u32x4>(st, voff[db + 2][1]);
+      }
+      if constexpr (BLOCK) oacc[db] = mfma_fp8_scaled(a0[db], a1[db], p[0], p[1], oacc[db], v_sc);
+      else oacc[db] = mfma_fp8(a0[db], a1[db], p[0], p[1], oacc[db]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     lacc = mfma_fp8(ones, ones, p[0], p[1], lacc);
   };
