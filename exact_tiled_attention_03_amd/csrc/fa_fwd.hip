@@ -315,13 +315,17 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
     const int kb_end = CAUSAL ? min(nb, (q0 + kBr) / kBc) : nb;
     if (wave == 0) {
       int count = 0;
+      // every lane loads from a valid address (clamped to the mask) and discards what lies
+      // outside it without a branch, so the four loads of an iteration go out together
+      // rather than one per wait
       for (int base = 0; base < kb_end; base += kWave) {
         const int kb = base + lane;
+        const int kbc = min(kb, nb - 1);
         int bits = 0;
-        if (kb < kb_end) {
 #pragma unroll
-          for (int r = 0; r < kBr / kSparseBlock; ++r)
-            if (qb0 + r < nb && mrow[(size_t)r * nb + kb] != 0) bits |= 1 << r;
+        for (int r = 0; r < kBr / kSparseBlock; ++r) {
+          const uint8_t v = mrow[(size_t)min(r, nb - 1 - qb0) * nb + kbc];
+          bits |= (int)((kb < kb_end) & (qb0 + r < nb) & (v != 0)) << r;
         }
         const unsigned long long act = __ballot(bits != 0);
         if (bits) blk_list[count + __popcll(act & ((1ull << lane) - 1))] = kb | (bits << 16);
