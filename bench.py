@@ -7,6 +7,9 @@ workload, inputs resident in HBM. Prints one JSON line with TFLOP/s counted as
 the visible (query, key) pairs over the heads), the roofline of the kernel (achieved
 TFLOP/s from HIP events on the launch stream against the dense bf16/f16 MFMA peak) and
 the fp64 CPU oracle timed on the host cores on a bounded sample of the same workload.
+The default workload is causal grouped-query attention, bf16, B4 Hq32 Hkv8 N8192 d128.
+The timed steps run as 5 event-timed windows; the roofline uses their median (the min is
+reported too), and the driver's current shader clock is sampled during them.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --mode copy      # plain device copy of known size, for counter scaling
@@ -29,7 +32,8 @@ import torch  # noqa: E402
 
 import synth_inputs  # noqa: E402
 
-DEFAULT_WORKLOAD = "mha_bf16_b16_h16_n2048_d128"
+DEFAULT_WORKLOAD = "gqa_causal_bf16_b4_h32_kv8_n8192_d128"
+WINDOWS = 5          # the timed steps are split into this many event-timed windows
 # Dense MFMA peak of MI355X: 256 CUs x 4 SIMDs x 2.4 GHz x (1024 bf16/f16 or 2048 fp8 FLOP/clk/SIMD)
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "e4m3": 5033.2}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -88,6 +92,7 @@ def cpu_baseline(w: synth_inputs.Workload, inp: dict, budget_s: float = 12.0):
         el = time.perf_counter() - t0
         fl = w.flops * bs / w.B
         return {"value": fl / el / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+                "cpu_model": cpu_model(),
                 "sample": f"first {bs} of {w.B} batches of {w.name} ({fl / 1e9:.2f} GFLOP, {el:.1f} s in fp64)"}
 
     def prep(x, sg):
@@ -124,9 +129,73 @@ def cpu_baseline(w: synth_inputs.Workload, inp: dict, budget_s: float = 12.0):
             flops += (4.0 * w.d * synth_inputs.block_mask_pairs(mh, w.N, w.causal, g) if bmask is not None
                       else per_head * g)
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"first {heads} of {w.B * w.H} (batch, head) slices of {w.name} in memory order, "
                       f"whole slices ({flops / 1e9:.1f} GFLOP, {elapsed:.1f} s in fp64)"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class ClockSampler:
+    """Samples the GPU shader clock from the driver's sysfs files while running (the
+    current DPM level of pp_dpm_sclk, else hwmon freq1_input), every ~10 ms on a host
+    thread. The samples are the driver's reported current clock, not a counter."""
+
+    def __init__(self):
+        import glob
+        import threading
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.hwmon = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/freq1_input"))
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def read(self):
+        for p in self.paths:
+            try:
+                for line in open(p):
+                    if "*" in line:
+                        return float(line.split(":")[1].strip().rstrip("*").strip().lower().replace("mhz", ""))
+            except (OSError, ValueError, IndexError):
+                continue
+        for p in self.hwmon:
+            try:
+                return float(open(p).read()) / 1e6
+            except (OSError, ValueError):
+                continue
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self.read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(0.01)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        a = np.array(self.samples)
+        src = "pp_dpm_sclk" if self.paths else "hwmon freq1_input"
+        return {"median_MHz": float(np.median(a)), "min_MHz": float(a.min()), "max_MHz": float(a.max()),
+                "samples": int(a.size), "source": f"driver sysfs {src} (current level, sampled every ~10 ms)"}
 
 
 def run_copy():
@@ -222,16 +291,23 @@ def main():
 
     for _ in range(args.warmup):
         step(o, lse)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the K timed steps run as WINDOWS consecutive windows, each bracketed by HIP events on
+    # the launch stream; the wall clock covers all K
+    nwin = max(1, min(WINDOWS, args.steps))
+    sizes = [args.steps // nwin + (1 if i < args.steps % nwin else 0) for i in range(nwin)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nwin + 1)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step(o, lse)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    with ClockSampler() as clocks:
+        t0 = time.perf_counter()
+        evs[0].record(stream)
+        for i, n in enumerate(sizes):
+            for _ in range(n):
+                step(o, lse)
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    win_ms = [evs[i].elapsed_time(evs[i + 1]) / n for i, n in enumerate(sizes)]
+    kernel_ms = float(np.median(win_ms))
 
     ms_per_step = wall * 1e3 / args.steps
     value = w.flops / (ms_per_step * 1e-3) / 1e12
@@ -239,7 +315,10 @@ def main():
     cdt = "e4m3" if w.fp8_block else w.dtype
     peak = PEAK_TFLOPS[cdt]
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name), "kernel_ms": round(kernel_ms, 5)}
+            "frac": round(achieved / peak, 4), "traffic": measured_traffic(w.name), "kernel_ms": round(kernel_ms, 5),
+            "kernel_ms_min": round(min(win_ms), 5), "window_ms": [round(x, 5) for x in win_ms],
+            "timing": f"median (and min) over {nwin} event-timed windows of the {args.steps} timed steps",
+            "achieved_at_min": round(w.flops / (min(win_ms) * 1e-3) / 1e12, 2)}
     if w.decode_nq:
         # decode reads every K/V element once: HBM-bound; algorithmic bytes = Q + K + V + O + lse
         el = 2
@@ -247,6 +326,7 @@ def main():
         gbps = alg / (kernel_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": 8000.0, "unit": "GB/s",
                 "frac": round(gbps / 8000.0, 4), "traffic": measured_traffic(w.name), "kernel_ms": round(kernel_ms, 5),
+                "kernel_ms_min": round(min(win_ms), 5), "window_ms": [round(x, 5) for x in win_ms],
                 "algorithmic_bytes": alg}
     out = {
         "metric": METRIC,
@@ -272,6 +352,7 @@ def main():
                       if w.sparse_density else {}),
                    **({"fp8": "block scales (64 rows, E8M0), Hadamard-rotated q/k"} if w.fp8_block else {})},
         "roofline": roof,
+        "sclk": clocks.summary(),
     }
     if quant:
         out["quantize"] = quant

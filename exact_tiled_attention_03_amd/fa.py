@@ -148,9 +148,13 @@ def fa_fwd_query(B: int, H: int, Hkv: int, N: int, d: int, causal: int, dtype: i
 def _dtype_code(t, dtype):
     import torch
     if dtype is not None:
+        if dtype not in DTYPE_NAMES:
+            raise ValueError(f"dtype must be one of {sorted(DTYPE_NAMES)}")
         return DTYPE_NAMES[dtype]
-    return {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16,
-            torch.float8_e4m3fn: FA_DTYPE_FP8_E4M3}[t.dtype]
+    codes = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16, torch.float8_e4m3fn: FA_DTYPE_FP8_E4M3}
+    if t.dtype not in codes:
+        raise ValueError(f"unsupported element type {t.dtype} (float16, bfloat16 or float8_e4m3fn)")
+    return codes[t.dtype]
 
 
 def fwd(q, k, v, causal: bool = False, scale: float | None = None, descale=None, dtype: str | None = None,
@@ -180,7 +184,13 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, descale=None,
             raise ValueError("tensors must be contiguous and on the same device")
     if tuple(k.shape) != (B, N, Hkv, d) or tuple(v.shape) != (B, N, Hkv, d):
         raise ValueError("k and v must be [B,N,Hkv,d] matching q")
-    if tuple(out.shape) != (B, N, H, d) or out.dtype != out_dtype or tuple(lse.shape) != (B, H, N):
+    _same_elem_type(q, (k, v), "q, k and v")
+    if code == FA_DTYPE_FP8_E4M3 and q.element_size() != 1:
+        raise ValueError("e4m3 inputs must be 1-byte tensors (float8_e4m3fn or uint8)")
+    if code != FA_DTYPE_FP8_E4M3 and q.dtype != {FA_DTYPE_F16: torch.float16, FA_DTYPE_BF16: torch.bfloat16}[code]:
+        raise ValueError(f"16-bit inputs must be float16 or bfloat16 matching dtype (got {q.dtype})")
+    if tuple(out.shape) != (B, N, H, d) or out.dtype != out_dtype or tuple(lse.shape) != (B, H, N) \
+            or lse.dtype != torch.float32:
         raise ValueError("out/lse have the wrong shape or type")
     if stream is None:
         stream = torch.cuda.current_stream(q.device).cuda_stream
@@ -232,12 +242,20 @@ def fwd_block_sparse(q, k, v, block_mask, causal: bool = False, scale: float | N
         raise ValueError(f"block_mask must be uint8 [1 or {H}, {nb}, {nb}]")
     if tuple(k.shape) != (B, N, Hkv, d) or tuple(v.shape) != (B, N, Hkv, d):
         raise ValueError("k and v must be [B,N,Hkv,d] matching q")
-    if tuple(out.shape) != (B, N, H, d) or out.dtype != q.dtype or tuple(lse.shape) != (B, H, N):
+    _same_elem_type(q, (k, v, out), "q, k, v and out")
+    if tuple(out.shape) != (B, N, H, d) or tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32:
         raise ValueError("out/lse have the wrong shape or type")
     _check(fa_fwd_block_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Hkv,
                                N, d, int(bool(causal)), block_mask.data_ptr(), block_mask.shape[0], scale, code,
                                _stream(q, stream)))
     return out, lse
+
+
+def _same_elem_type(ref, others, what: str):
+    """Every tensor in `others` has ref's element type (the kernels size every read from it)."""
+    for t in others:
+        if t.dtype != ref.dtype:
+            raise ValueError(f"{what} must share one element type (got {ref.dtype} and {t.dtype})")
 
 
 def _stream(t, stream):
@@ -252,6 +270,8 @@ def quantize_e4m3_block(x, signs=None, codes=None, scales=None, stream=None):
     first. Returns (codes uint8 [B,N,Hx,d], scales uint8 E8M0 [B,Hx,nb])."""
     import torch
     B, N, Hx, d = x.shape
+    if x.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError(f"x must be float16 or bfloat16 (got {x.dtype})")
     code = {torch.float16: FA_DTYPE_F16, torch.bfloat16: FA_DTYPE_BF16}[x.dtype]
     nb = (N + FP8_BLOCK_ROWS - 1) // FP8_BLOCK_ROWS
     if codes is None:
@@ -292,7 +312,11 @@ def fwd_fp8_block(q, k, v, q_scales, k_scales, v_scales, causal: bool = False, s
     if (tuple(q_scales.shape) != (B, H, nb) or tuple(k_scales.shape) != (B, Hkv, nb)
             or tuple(v_scales.shape) != (B, Hkv, nb)):
         raise ValueError("block scales must be [B,H,nb] (q) and [B,Hkv,nb] (k, v)")
-    if tuple(out.shape) != (B, N, H, d) or out.dtype != torch.bfloat16 or tuple(lse.shape) != (B, H, N):
+    for t in (q, k, v, q_scales, k_scales, v_scales):
+        if t.dtype != torch.uint8:
+            raise ValueError("codes and block scales must be uint8 tensors")
+    if tuple(out.shape) != (B, N, H, d) or out.dtype != torch.bfloat16 or tuple(lse.shape) != (B, H, N) \
+            or lse.dtype != torch.float32:
         raise ValueError("out/lse have the wrong shape or type")
     _check(fa_fwd_fp8_block(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_scales.data_ptr(), k_scales.data_ptr(),
                             v_scales.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Hkv, N, d, int(bool(causal)),
@@ -323,11 +347,13 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
     for t in (o, dout, dq):
         if tuple(t.shape) != (B, N, H, d) or t.dtype != q.dtype:
             raise ValueError("o, dout and dq must match q")
-    for t in (v, dk, dv):
+    for t in (k, v, dk, dv):
         if tuple(t.shape) != (B, N, Hkv, d) or t.dtype != q.dtype:
             raise ValueError("k, v, dk and dv must be [B,N,Hkv,d] of q's type")
     if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32:
         raise ValueError("lse must be [B,H,N] float32")
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace must hold at least {nbytes} bytes")
     _check(fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
                   dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d, int(bool(causal)), scale, code,
                   workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q, stream)))
@@ -354,10 +380,13 @@ def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_s
     for t in (q, k, v, out, lse, workspace):
         if not t.is_contiguous() or t.device != q.device:
             raise ValueError("tensors must be contiguous and on the same device")
-    if tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != d:
+    if k.dim() != 4 or tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != d:
         raise ValueError("k and v must be [B,Nk,Hkv,d] matching q")
-    if tuple(out.shape) != (B, Nq, H, d) or out.dtype != q.dtype or tuple(lse.shape) != (B, H, Nq):
+    _same_elem_type(q, (k, v, out), "q, k, v and out")
+    if tuple(out.shape) != (B, Nq, H, d) or tuple(lse.shape) != (B, H, Nq) or lse.dtype != torch.float32:
         raise ValueError("out/lse have the wrong shape or type")
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace must hold at least {nbytes} bytes")
     _check(fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Hkv, Nq, Nk,
                           d, int(bool(causal)), scale, code, num_splits, workspace.data_ptr(),
                           workspace.numel() * workspace.element_size(), _stream(q, stream)))

@@ -83,8 +83,11 @@ def load(path: str):
     lib.oracle_attn_bwd_f64.argtypes = [dp] * 7 + [ctypes.c_int] * 8 + [ctypes.c_double]
     lib.oracle_attn_bwd_f64.restype = ctypes.c_int
     lib.oracle_attn_bwd_dq_rows_f64.argtypes = [dp] * 4 + [ctypes.c_int] * 6 + [ctypes.c_double, ctypes.c_int64,
-                                                                                i64p, dp]
+                                                                                i64p, dp, dp]
     lib.oracle_attn_bwd_dq_rows_f64.restype = ctypes.c_int
+    lib.oracle_attn_bwd_dkdv_rows_f64.argtypes = [dp] * 6 + [ctypes.c_int] * 6 + [ctypes.c_double, ctypes.c_int64,
+                                                                                  i64p, dp, dp, dp]
+    lib.oracle_attn_bwd_dkdv_rows_f64.restype = ctypes.c_int
     lib.oracle_attn_fwd_kv_f64.argtypes = [dp] * 5 + [ctypes.c_int] * 7 + [ctypes.c_double]
     lib.oracle_attn_fwd_kv_f64.restype = ctypes.c_int
     lib.oracle_attn_fwd_block_f64.argtypes = ([dp, dp, dp, dp, dp] + [ctypes.c_int] * 6 +
@@ -388,18 +391,51 @@ def attn_bwd_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, 
 
 
 def attn_bwd_dq_rows_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, causal: bool,
-                         scale: float, rows: np.ndarray) -> np.ndarray:
-    """dQ of the selected rows (b, h, i) only, [R, d] (same definition as attn_bwd_f64)."""
+                         scale: float, rows: np.ndarray, with_mag: bool = False):
+    """dQ of the selected rows (b, h, i) only, [R, d] (same definition as attn_bwd_f64).
+    With with_mag, also returns [R, 2, d]: sum_j |dS_ij||k_j| and sum_j P_ij |k_j|."""
     q, k, v, dout = (np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v, dout))
     B, N, H, Hkv, d = _shape(q, k, v)
     rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
     out = np.empty((rows.shape[0], d), dtype=np.float64)
+    mag = np.empty((rows.shape[0], 2, d), dtype=np.float64) if with_mag else None
     rc = _lib().oracle_attn_bwd_dq_rows_f64(_dptr(q), _dptr(k), _dptr(v), _dptr(dout), B, H, Hkv, N, d,
                                             int(bool(causal)), float(scale), rows.shape[0],
-                                            rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _dptr(out))
+                                            rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _dptr(out),
+                                            _dptr(mag) if with_mag else None)
     if rc:
         raise ValueError(f"oracle_attn_bwd_dq_rows_f64 failed ({rc})")
-    return out
+    return (out, mag) if with_mag else out
+
+
+def attn_bwd_dkdv_rows_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray, causal: bool,
+                           scale: float, rows: np.ndarray, fwd=None, with_mag: bool = False):
+    """dK and dV of the selected key rows (b, hk, j) only (hk a key/value head), each [R, d],
+    summed over every query row that sees key j in every query head of hk's group (same
+    definition as attn_bwd_f64). `fwd` = (o, lse) from attn_fwd_f64 on the same inputs,
+    computed here when not given. With with_mag, also returns [R, 3, d]: sum_i |dS_ij||q_i|,
+    sum_i P_ij w_i |q_i| (w_i = sum_t |dO_it O_it|) and sum_i P_ij |dO_i|."""
+    q, k, v, dout = (np.ascontiguousarray(x, dtype=np.float64) for x in (q, k, v, dout))
+    B, N, H, Hkv, d = _shape(q, k, v)
+    if dout.shape != q.shape:
+        raise ValueError("dout must have q's shape")
+    o, lse = attn_fwd_f64(q, k, v, causal, scale) if fwd is None else fwd
+    o = np.ascontiguousarray(o, dtype=np.float64)
+    lse = np.ascontiguousarray(lse, dtype=np.float64)
+    if o.shape != q.shape or lse.shape != (B, H, N):
+        raise ValueError("fwd must be (o [B,N,H,d], lse [B,H,N])")
+    rows = np.ascontiguousarray(rows, dtype=np.int64).reshape(-1, 3)
+    R = rows.shape[0]
+    dk = np.empty((R, d), dtype=np.float64)
+    dv = np.empty((R, d), dtype=np.float64)
+    mag = np.empty((R, 3, d), dtype=np.float64) if with_mag else None
+    rc = _lib().oracle_attn_bwd_dkdv_rows_f64(_dptr(q), _dptr(k), _dptr(v), _dptr(dout), _dptr(o), _dptr(lse),
+                                              B, H, Hkv, N, d, int(bool(causal)), float(scale), R,
+                                              rows.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), _dptr(dk),
+                                              _dptr(dv), _dptr(mag) if with_mag else None)
+    if rc:
+        raise ValueError(f"oracle_attn_bwd_dkdv_rows_f64 failed ({rc})")
+    return (dk, dv, mag) if with_mag else (dk, dv)
 
 
 def attn_fwd_kv_f64(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: float):

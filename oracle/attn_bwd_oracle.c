@@ -111,11 +111,13 @@ int oracle_attn_bwd_f64(const double* q, const double* k, const double* v, const
 }
 
 /* dQ of selected query rows only (rows[3r..3r+2] = (b, h, i)), for checking large problems:
- * row i of dQ needs only row i of P and dP. dq_rows is [nrows][d]. */
+ * row i of dQ needs only row i of P and dP. dq_rows is [nrows][d]. mag, when not NULL, is
+ * [nrows][2][d]: sum_j |dS_ij| |k_j| and sum_j P_ij |k_j| (elementwise absolute values), the
+ * sizes that bound the rounding error of a computed dQ row. */
 int oracle_attn_bwd_dq_rows_f64(const double* q, const double* k, const double* v,
                                 const double* dout, int B, int H, int Hkv, int N, int d,
                                 int causal, double scale, int64_t nrows, const int64_t* rows,
-                                double* dq_rows) {
+                                double* dq_rows, double* mag) {
   if (B < 1 || H < 1 || Hkv < 1 || N < 1 || d < 1 || Hkv > H || H % Hkv) return 1;
   if (!q || !k || !v || !dout || !rows || !dq_rows) return 1;
   for (int64_t r = 0; r < nrows; ++r)
@@ -167,9 +169,106 @@ int oracle_attn_bwd_dq_rows_f64(const double* q, const double* k, const double* 
         const double* kj = k + (((size_t)b * N + j) * Hkv + hk) * d;
         for (int t = 0; t < d; ++t) dqi[t] += scale * ds * kj[t];
       }
+      if (mag) {
+        double* m1 = mag + (size_t)r * 2 * d;
+        double* m2 = m1 + d;
+        for (int t = 0; t < d; ++t) m1[t] = m2[t] = 0.0;
+        for (int j = jlo; j <= jhi; ++j) {
+          const double ads = fabs(p[j] * (dp[j] - D));
+          const double* kj = k + (((size_t)b * N + j) * Hkv + hk) * d;
+          for (int t = 0; t < d; ++t) {
+            m1[t] += ads * fabs(kj[t]);
+            m2[t] += p[j] * fabs(kj[t]);
+          }
+        }
+      }
     }
     free(p);
     free(dp);
   }
   return failed ? 2 : 0;
+}
+
+/* dK and dV of selected key rows only (rows[3r..3r+2] = (b, hk, j), hk a key/value head),
+ * for checking large problems. Key j's gradient sums over every query row i that sees it
+ * (i >= j under the causal mask, every i otherwise) in every query head h of its group, in
+ * ascending (h, i) order. The probabilities come from the forward's lse,
+ * P_ij = exp(s_ij - lse_i), and D_i = <dO_i, O_i> from the forward's O: both are the values
+ * oracle_attn_fwd_f64 returns for the same inputs (passed in, [B][H][N] and [B][N][H][d]),
+ * and both equal what oracle_attn_bwd_f64 forms row by row, in real arithmetic.
+ * dk_rows, dv_rows: [nrows][d]. mag, when not NULL, is [nrows][3][d]: sum_i |dS_ij| |q_i|,
+ * sum_i P_ij w_i |q_i| with w_i = sum_t |dO_it O_it|, and sum_i P_ij |dO_i|, the sizes that
+ * bound the rounding error of computed dK and dV rows. Returns 0, 1 on bad arguments,
+ * 2 if scratch allocation failed. */
+int oracle_attn_bwd_dkdv_rows_f64(const double* q, const double* k, const double* v,
+                                  const double* dout, const double* o, const double* lse,
+                                  int B, int H, int Hkv, int N, int d, int causal, double scale,
+                                  int64_t nrows, const int64_t* rows, double* dk_rows,
+                                  double* dv_rows, double* mag) {
+  if (B < 1 || H < 1 || Hkv < 1 || N < 1 || d < 1 || Hkv > H || H % Hkv) return 1;
+  if (!q || !k || !v || !dout || !o || !lse || !rows || !dk_rows || !dv_rows) return 1;
+  for (int64_t r = 0; r < nrows; ++r)
+    if (rows[3 * r] < 0 || rows[3 * r] >= B || rows[3 * r + 1] < 0 || rows[3 * r + 1] >= Hkv ||
+        rows[3 * r + 2] < 0 || rows[3 * r + 2] >= N)
+      return 1;
+  const int group = H / Hkv;
+  const size_t nq = (size_t)B * H * N;           /* D and w per (b, h, i), [B][H][N] */
+  double* D = (double*)malloc(sizeof(double) * nq);
+  double* w = (double*)malloc(sizeof(double) * nq);
+  if (!D || !w) {
+    free(D);
+    free(w);
+    return 2;
+  }
+#pragma omp parallel for schedule(static)
+  for (int64_t x = 0; x < (int64_t)nq; ++x) {
+    const int i = (int)(x % N), h = (int)((x / N) % H), b = (int)(x / ((int64_t)N * H));
+    const double* gi = dout + (((size_t)b * N + i) * H + h) * d;
+    const double* oi = o + (((size_t)b * N + i) * H + h) * d;
+    double s = 0.0, a = 0.0;
+    for (int t = 0; t < d; ++t) {
+      s += gi[t] * oi[t];
+      a += fabs(gi[t] * oi[t]);
+    }
+    D[x] = s;
+    w[x] = a;
+  }
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int b = (int)rows[3 * r], hk = (int)rows[3 * r + 1], j = (int)rows[3 * r + 2];
+    const double* kj = k + (((size_t)b * N + j) * Hkv + hk) * d;
+    const double* vj = v + (((size_t)b * N + j) * Hkv + hk) * d;
+    double* dkj = dk_rows + (size_t)r * d;
+    double* dvj = dv_rows + (size_t)r * d;
+    double* m1 = mag ? mag + (size_t)r * 3 * d : NULL;
+    for (int t = 0; t < d; ++t) dkj[t] = dvj[t] = 0.0;
+    if (m1)
+      for (int t = 0; t < 3 * d; ++t) m1[t] = 0.0;
+    for (int h = hk * group; h < (hk + 1) * group; ++h)
+      for (int i = causal ? j : 0; i < N; ++i) {
+        const double* qi = q + (((size_t)b * N + i) * H + h) * d;
+        const double* gi = dout + (((size_t)b * N + i) * H + h) * d;
+        const size_t row = ((size_t)b * H + h) * N + i;
+        double s = 0.0, dp = 0.0;
+        for (int t = 0; t < d; ++t) {
+          s += qi[t] * kj[t];
+          dp += gi[t] * vj[t];
+        }
+        const double p = exp(scale * s - lse[row]);
+        const double ds = p * (dp - D[row]);
+        for (int t = 0; t < d; ++t) {
+          dkj[t] += scale * ds * qi[t];
+          dvj[t] += p * gi[t];
+        }
+        if (m1)
+          for (int t = 0; t < d; ++t) {
+            m1[t] += fabs(ds) * fabs(qi[t]);
+            m1[d + t] += p * w[row] * fabs(qi[t]);
+            m1[2 * d + t] += p * fabs(gi[t]);
+          }
+      }
+  }
+  free(D);
+  free(w);
+  return 0;
 }

@@ -745,10 +745,134 @@ def pin_decode_rectangular():
             _close(o, ref, 1e-12, "decode vs sdpa with bottom-right mask")
 
 
+# P28 -- row selection: the single-row entry points (used to check full-size outputs one
+# row at a time) return exactly the rows of the whole-tensor functions, which the other
+# pins tie to the definition: plain, causal, key windows, block masks (shared and per-head,
+# causal, empty rows), and the stored-input entries that decode only the selected queries.
+def pin_row_selection():
+    rng = np.random.default_rng(45)
+    B, N, H, Hkv, d = 2, 70, 4, 2, 8
+    q, k, v = _qkv(rng, B, N, H, Hkv, d)
+    rows = np.array([[b, h, i] for b in range(B) for h in range(H) for i in range(N)])
+    rows = rows[rng.permutation(len(rows))[:160]]           # shuffled: output order follows rows
+    qr = q[rows[:, 0], rows[:, 2], rows[:, 1]]
+    for causal in (False, True):
+        for window in (None, (5, -1), (3, 9), (-1, 0), (0, 0), (-1, 12)):
+            o, lse = oracle.attn_fwd_f64(q, k, v, causal, 0.3, window)
+            orow, lrow = oracle.attn_rows_f64(qr, k, v, H, rows, causal, 0.3, window)
+            assert np.array_equal(orow, o[rows[:, 0], rows[:, 2], rows[:, 1]]), f"rows o causal={causal} w={window}"
+            assert np.array_equal(lrow, lse[rows[:, 0], rows[:, 1], rows[:, 2]]), f"rows lse causal={causal} w={window}"
+    nb = (N + 15) // 16
+    shared = (rng.random((1, nb, nb)) < 0.5).astype(np.uint8)
+    shared[0, 2, :] = 0                                      # an empty block row
+    per_head = (rng.random((H, nb, nb)) < 0.4).astype(np.uint8)
+    for mask in (shared, per_head):
+        for causal in (False, True):
+            o, lse = oracle.attn_fwd_block_f64(q, k, v, causal, 0.3, mask, 16)
+            orow, lrow = oracle.attn_rows_block_f64(qr, k, v, H, rows, causal, 0.3, mask, 16)
+            assert np.array_equal(orow, o[rows[:, 0], rows[:, 2], rows[:, 1]]), f"block rows o causal={causal}"
+            assert np.array_equal(lrow, lse[rows[:, 0], rows[:, 1], rows[:, 2]]), f"block rows lse causal={causal}"
+            assert np.any(np.isneginf(lse)) or mask is per_head, "the empty block row is exercised"
+    # stored-input entries (bit patterns), including the e4m3 descales
+    raw = {x: np.asarray(torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy()
+                         ).view(np.uint16) for x, a in zip("qkv", (q, k, v))}
+    for causal, window in ((False, None), (True, (6, -1))):
+        o, lse = oracle.attn_fwd(raw["q"], raw["k"], raw["v"], "bf16", causal, 0.3, window=window)
+        orow, lrow = oracle.attn_rows(raw["q"], raw["k"], raw["v"], "bf16", causal, 0.3, rows, window=window)
+        assert np.array_equal(orow, o[rows[:, 0], rows[:, 2], rows[:, 1]]), "stored-input rows"
+        assert np.array_equal(lrow, lse[rows[:, 0], rows[:, 1], rows[:, 2]]), "stored-input rows lse"
+    mask64 = (rng.random((H, 2, 2)) < 0.7).astype(np.uint8)
+    o, lse = oracle.attn_fwd_block(raw["q"], raw["k"], raw["v"], "bf16", True, 0.3, mask64)
+    orow, lrow = oracle.attn_rows_block(raw["q"], raw["k"], raw["v"], "bf16", True, 0.3, rows, mask64)
+    assert np.array_equal(orow, o[rows[:, 0], rows[:, 2], rows[:, 1]]), "stored-input block rows"
+    assert np.array_equal(lrow, lse[rows[:, 0], rows[:, 1], rows[:, 2]]), "stored-input block rows lse"
+    e8 = {x: rng.integers(0, 256, (B, N, hh, d)).astype(np.uint8) for x, hh in zip("qkv", (H, Hkv, Hkv))}
+    for x in e8:
+        e8[x][(e8[x] & 0x7F) == 0x7F] = 0                    # no NaN codes
+    ds = (0.01, 0.02, 0.5)
+    o, lse = oracle.attn_fwd(e8["q"], e8["k"], e8["v"], "e4m3", False, 0.3, ds)
+    orow, lrow = oracle.attn_rows(e8["q"], e8["k"], e8["v"], "e4m3", False, 0.3, rows, ds)
+    assert np.array_equal(orow, o[rows[:, 0], rows[:, 2], rows[:, 1]]), "e4m3 rows"
+
+
+# P29 -- block dequantisation: every value equals its code's e4m3 value (torch's
+# float8_e4m3fn decode) times 2^(byte - 127) of its 64-row block, expanded with np.repeat;
+# and a round trip through block_quantize stays within half an e4m3 step of the input
+# (after the block's power-of-two scaling), for normal and subnormal codes.
+def pin_block_dequantize():
+    rng = np.random.default_rng(46)
+    B, N, Hx, d, br = 2, 150, 3, 32, 64
+    nb = (N + br - 1) // br
+    codes = rng.integers(0, 256, (B, N, Hx, d)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x3F                     # no NaN codes
+    scales = rng.integers(100, 150, (B, Hx, nb)).astype(np.uint8)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mult = np.repeat(np.exp2(scales.astype(np.float64) - 127.0), br, axis=2)[:, :, :N]    # [B, Hx, N]
+    ref = vals * np.transpose(mult, (0, 2, 1))[..., None]
+    got = oracle.block_dequantize(codes, scales, br)
+    assert got.shape == ref.shape and np.array_equal(got, ref), "block_dequantize vs repeat expansion"
+    x = rng.standard_normal((B, N, Hx, d)) * np.exp(rng.uniform(-6, 6, (B, 1, Hx, 1)))
+    x[0, :, 0, :4] *= 1e-3                                   # values in the subnormal range of their block
+    c, sc = oracle.block_quantize(x, br)
+    y = oracle.block_dequantize(c, sc, br)
+    e = np.transpose(np.repeat(sc.astype(np.float64) - 127.0, br, axis=2)[:, :, :N], (0, 2, 1))[..., None]
+    z = np.abs(x) * np.exp2(-e)                               # scaled magnitudes, <= 448
+    assert np.all(z <= 448.0), "scaled values fit e4m3"
+    half = np.where(z >= 2.0 ** -6, np.exp2(np.floor(np.log2(np.maximum(z, 2.0 ** -6))) - 4), 2.0 ** -10)
+    err = np.abs(y - x) * np.exp2(-e)
+    assert np.all(err <= half * (1 + 1e-12)), f"round trip beyond half an e4m3 step ({(err > half).sum()})"
+    assert np.any(err > 0.9 * half), "the bound is reached (a tight check)"
+
+
+# P30 -- gradient rows: the selected-row gradient entry points (dQ rows; dK and dV of key
+# rows, which take the forward's O and lse) equal the whole-tensor gradient of
+# attn_bwd_f64, pinned by P22-P24; their absolute-value sums equal a numpy evaluation of
+# the same sums from the probability matrix.
+def pin_bwd_rows():
+    rng = np.random.default_rng(47)
+    B, N, H, Hkv, d = 2, 41, 4, 2, 8
+    q, k, v = _qkv(rng, B, N, H, Hkv, d)
+    g = rng.standard_normal((B, N, H, d))
+    g_ = H // Hkv
+    for causal in (False, True):
+        dq, dk, dv = oracle.attn_bwd_f64(q, k, v, g, causal, 0.4)
+        o, lse = oracle.attn_fwd_f64(q, k, v, causal, 0.4)
+        qrows = np.array([[b, h, i] for b in range(B) for h in range(H) for i in range(N)])[::3]
+        dqr, qmag = oracle.attn_bwd_dq_rows_f64(q, k, v, g, causal, 0.4, qrows, with_mag=True)
+        _close(dqr, dq[qrows[:, 0], qrows[:, 2], qrows[:, 1]], 1e-13, f"dq rows causal={causal}")
+        krows = np.array([[b, hk, j] for b in range(B) for hk in range(Hkv) for j in range(N)])[::-2]
+        dkr, dvr, kmag = oracle.attn_bwd_dkdv_rows_f64(q, k, v, g, causal, 0.4, krows, (o, lse), with_mag=True)
+        _close(dkr, dk[krows[:, 0], krows[:, 2], krows[:, 1]], 1e-13, f"dk rows causal={causal}")
+        _close(dvr, dv[krows[:, 0], krows[:, 2], krows[:, 1]], 1e-13, f"dv rows causal={causal}")
+        dkr2, dvr2 = oracle.attn_bwd_dkdv_rows_f64(q, k, v, g, causal, 0.4, krows)
+        assert np.array_equal(dkr, dkr2) and np.array_equal(dvr, dvr2), "fwd computed inside"
+        for b in range(B):
+            for h in range(H):
+                hk = h // g_
+                P = oracle.attn_probs_f64(q, k, b, h, causal, 0.4)
+                dS = P * (g[b, :, h] @ v[b, :, hk].T - np.sum(g[b, :, h] * o[b, :, h], axis=1)[:, None])
+                w = np.sum(np.abs(g[b, :, h] * o[b, :, h]), axis=1)
+                sel = (qrows[:, 0] == b) & (qrows[:, 1] == h)
+                i = qrows[sel, 2]
+                _close(qmag[sel, 0], np.abs(dS[i]) @ np.abs(k[b, :, hk]), 1e-12, "dq |dS||k|")
+                _close(qmag[sel, 1], P[i] @ np.abs(k[b, :, hk]), 1e-12, "dq P|k|")
+        for r, (b, hk, j) in enumerate(krows):
+            m = np.zeros((3, d))
+            for h in range(hk * g_, (hk + 1) * g_):
+                P = oracle.attn_probs_f64(q, k, b, h, causal, 0.4)
+                dS = P * (g[b, :, h] @ v[b, :, hk].T - np.sum(g[b, :, h] * o[b, :, h], axis=1)[:, None])
+                w = np.sum(np.abs(g[b, :, h] * o[b, :, h]), axis=1)
+                m[0] += np.abs(dS[:, j]) @ np.abs(q[b, :, h])
+                m[1] += (P[:, j] * w) @ np.abs(q[b, :, h])
+                m[2] += P[:, j] @ np.abs(g[b, :, h])
+            _close(kmag[r], m, 1e-12, "dk/dv magnitude sums")
+
+
 ALL_PINS = [pin_mpmath_bruteforce, pin_torch_sdpa, pin_zero_query, pin_single_key, pin_two_keys,
             pin_affine_in_v, pin_probability_rows, pin_key_permutation, pin_key_shift, pin_gqa_repeat,
             pin_causal_prefix, pin_split_merge, pin_hardmax_and_range, pin_decoders, pin_golden_fixtures,
             pin_window_bruteforce_and_sdpa, pin_window_closed_forms, pin_window_reductions,
             pin_e4m3_encode, pin_fwht, pin_block_quantize, pin_rotation_identity,
             pin_bwd_finite_differences, pin_bwd_torch_autograd, pin_bwd_invariants, pin_decode_rectangular,
-            pin_block_sparse_bruteforce_and_sdpa, pin_block_sparse_reductions]
+            pin_block_sparse_bruteforce_and_sdpa, pin_block_sparse_reductions, pin_row_selection,
+            pin_block_dequantize, pin_bwd_rows]

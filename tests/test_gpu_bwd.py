@@ -109,32 +109,38 @@ def test_bwd_gqa_equals_repeated_heads():
         assert err <= 2e-2 * (s2.abs().max().item() + 1e-6), err
 
 
-def _row_bounds(q, k, v, dout, rows, causal, scale, dtype):
-    """The bound of gpu_util.bwd_error_bound for dq of single rows (b, h, i), in numpy."""
-    u = gu.UNIT_ROUNDOFF[dtype]
-    H, Hkv = q.shape[2], k.shape[2]
-    out = []
-    for b, h, i in rows:
-        hk = h // (H // Hkv)
-        n = i + 1 if causal else k.shape[1]
-        K, V = k[b, :n, hk], v[b, :n, hk]
-        s_ = scale * (K @ q[b, i, h])
-        p = np.exp(s_ - s_.max())
-        p /= p.sum()
-        dp = V @ dout[b, i, h]
-        o = p @ V
-        ds = p * (dp - p @ dp)
-        dD = u * np.sum(np.abs(dout[b, i, h]) * np.abs(o))
-        out.append(scale * (u * np.abs(ds) @ np.abs(K) + dD * (p @ np.abs(K))))
-    return np.array(out)
+def _unit_forward(qd, kd, vd, causal, scale, units):
+    """The oracle's forward (o, lse) on the query heads of the (b, kv-head) units, placed in
+    full-size arrays (zeros elsewhere; only those rows are read)."""
+    B, N, H, d = qd.shape
+    g = H // kd.shape[2]
+    o = np.zeros_like(qd)
+    lse = np.zeros((B, H, N))
+    for b, hk in units:
+        hs = slice(hk * g, (hk + 1) * g)
+        ou, lu = oracle.attn_fwd_f64(np.ascontiguousarray(qd[b:b + 1, :, hs]), np.ascontiguousarray(kd[b:b + 1, :, hk:hk + 1]),
+                                     np.ascontiguousarray(vd[b:b + 1, :, hk:hk + 1]), causal, scale)
+        o[b, :, hs], lse[b, hs] = ou[0], lu[0]
+    return o, lse
+
+
+def _check_rows(name, got, ref, bound):
+    err = np.abs(got - ref)
+    lim = 2.0 * bound + 1e-5
+    ratio = float(np.max(err / lim)) if ref.size else 0.0
+    assert np.all(np.isfinite(got)), f"{name}: non-finite"
+    assert ratio <= 1.0, f"{name}: {int((err > lim).sum())} elements over the bound, max err/bound {ratio:.2f}"
+    return ratio
 
 
 @pytest.mark.parametrize("name", [n for n, w in synth_inputs.WORKLOADS.items() if w.backward])
 def test_bwd_workload_full_size(name):
     """The gradient workloads at full size, in the launch configuration the benchmark
-    times: whole (batch, head) slices against the oracle for the multi-head shape; for the
-    causal grouped-query shape, dq on sampled rows and, over all positions, the exact
-    identities sum_j dk_j = 0 and sum_j dv_j = sum over the group of sum_i dO_i."""
+    times, element by element against the oracle within twice the derived rounding bound
+    (gpu_util.bwd_error_bound, from the oracle's absolute-value sums): every key row of dK
+    and dV for whole (batch, K/V head) units, every row of dQ for those units' query
+    heads, and, in every (batch, head) slice, the dQ rows on both sides of each query- and
+    key-tile boundary plus random rows."""
     w = synth_inputs.WORKLOADS[name]
     _log(f"[bwd workload] {name}")
     inp = synth_inputs.workload_inputs(w)
@@ -144,30 +150,37 @@ def test_bwd_workload_full_size(name):
     o, lse = fa.fwd(q, k, v, causal=w.causal, scale=w.scale)
     dq, dk, dv = fa.bwd(q, k, v, o, lse, do, causal=w.causal, scale=w.scale)
     torch.cuda.synchronize()
-    for t in (dq, dk, dv):
-        assert bool(torch.isfinite(t.float()).all())
+    dq, dk, dv = (t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv))
+    del q, k, v, do, o, lse
+    u = gu.UNIT_ROUNDOFF[w.dtype]
     g = w.H // w.Hkv
-    if not w.causal and g == 1:
-        for b, h in ((0, 0), (w.B - 1, w.H - 1)):
-            sl = lambda a: np.ascontiguousarray(oracle.decode(a[b:b + 1, :, h:h + 1], w.dtype))
-            bounds, ref = gu.bwd_error_bound(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(dout), w.causal, w.scale,
-                                             w.dtype)
-            got = [t[b:b + 1, :, h:h + 1] for t in (dq, dk, dv)]
-            e = _check(got, ref, bounds, f"{name} b{b} h{h}")
-            _log(f"[bwd workload] b{b} h{h}: err/bound dq {e[0]:.2f} dk {e[1]:.2f} dv {e[2]:.2f}")
-        return
-    rows = gu.sample_rows(w.B, w.H, w.N, n_random=24, seed=w.seed)
     qd, kd, vd, dd = (oracle.decode(a, w.dtype) for a in (inp["q"], inp["k"], inp["v"], dout))
-    ref = oracle.attn_bwd_dq_rows_f64(qd, kd, vd, dd, w.causal, w.scale, rows)
-    bound = _row_bounds(qd, kd, vd, dd, rows, w.causal, w.scale, w.dtype)
-    got = dq[rows[:, 0], rows[:, 2], rows[:, 1]].float().cpu().numpy().astype(np.float64)
-    ratio = float(np.max(np.abs(got - ref) / (2 * bound + 1e-5)))
-    _log(f"[bwd workload] dq sampled rows: err/bound {ratio:.2f}")
-    assert ratio <= 1.0
-    dkf, dvf = dk.double(), dv.double()
-    sk = dkf.sum(dim=1).abs().max().item()
-    assert sk <= 2e-2 * dkf.abs().sum(dim=1).max().item(), f"sum_j dk_j = {sk:.3e}"
-    dos = do.double().view(w.B, w.N, w.Hkv, g, w.d).sum(dim=(1, 3))
-    sv = (dvf.sum(dim=1) - dos).abs().max().item()
-    assert sv <= 2e-2 * dvf.abs().sum(dim=1).max().item(), f"sum_j dv_j - sum_i dO_i = {sv:.3e}"
-    _log(f"[bwd workload] |sum dk| {sk:.2e}, |sum dv - sum dO| {sv:.2e}")
+    rng = np.random.default_rng(w.seed)
+    # (b, kv-head) units checked whole: one for the grouped shape (each of its keys sums over
+    # 4 x 8192 query rows), eight for the multi-head shape
+    units = [(w.B - 1, w.Hkv - 1)] if g > 1 else sorted(
+        {(0, 0), (w.B - 1, w.Hkv - 1)} | {(int(rng.integers(w.B)), int(rng.integers(w.Hkv))) for _ in range(6)})
+    fo, flse = _unit_forward(qd, kd, vd, w.causal, w.scale, units)
+    # dK, dV: every key row of each unit
+    krows = np.array([[b, hk, j] for b, hk in units for j in range(w.N)], dtype=np.int64)
+    rk, rv, mk = oracle.attn_bwd_dkdv_rows_f64(qd, kd, vd, dd, w.causal, w.scale, krows, (fo, flse), with_mag=True)
+    sel = (krows[:, 0], krows[:, 2], krows[:, 1])
+    ek = _check_rows(f"{name} dk", dk[sel], rk, w.scale * u * (mk[:, 0] + mk[:, 1]) + u * np.abs(rk))
+    ev = _check_rows(f"{name} dv", dv[sel], rv, u * mk[:, 2] + u * np.abs(rv))
+    # dQ: every row of the units' query heads, tile-boundary rows of every slice, random rows
+    edge = sorted({i for t in (gu.KEY_TILE, gu.QUERY_TILE) for x in range(0, w.N + 1, t) for i in (x - 1, x)
+                   if 0 <= i < w.N} if w.N <= 4096 else
+                  {i for x in range(0, w.N + 1, gu.QUERY_TILE) for i in (x - 1, x) if 0 <= i < w.N})
+    qrows = {(b, h, i) for b, hk in units for h in (range(hk * g, (hk + 1) * g) if g == 1 else (hk * g,))
+             for i in range(w.N)}
+    qrows |= {(b, h, i) for b in range(w.B) for h in range(w.H) for i in edge}
+    qrows |= {tuple(r) for r in gu.sample_rows(w.B, w.H, w.N, n_random=64, seed=w.seed).tolist()}
+    qrows = np.array(sorted(qrows), dtype=np.int64)
+    rq, mq = oracle.attn_bwd_dq_rows_f64(qd, kd, vd, dd, w.causal, w.scale, qrows, with_mag=True)
+    o_rows, _ = oracle.attn_rows_f64(qd[qrows[:, 0], qrows[:, 2], qrows[:, 1]], kd, vd, w.H, qrows, w.causal,
+                                     w.scale)
+    dD = u * np.sum(np.abs(dd[qrows[:, 0], qrows[:, 2], qrows[:, 1]] * o_rows), axis=1)
+    eq = _check_rows(f"{name} dq", dq[qrows[:, 0], qrows[:, 2], qrows[:, 1]], rq,
+                     w.scale * (u * mq[:, 0] + dD[:, None] * mq[:, 1]) + u * np.abs(rq))
+    _log(f"[bwd workload] {name}: {len(krows)} dK/dV rows of units {units} and {len(qrows)} dQ rows, every element; "
+         f"err/bound dq {eq:.2f} dk {ek:.2f} dv {ev:.2f}")

@@ -103,7 +103,10 @@ def test_block_attention_parity(case):
     torch.cuda.synchronize()
     o, lse = gu.host(o, lse)
     bound = gu.fp8_bound_from_values(q, k, v, causal, scale, o_ref)
-    gu.compare(o, o_ref, lse, lse_ref, "e4m3", str(case), extra_bound=bound)
+    few = gu.effective_keys(q, k, causal, scale) < gu.FEW_KEYS
+    e = gu.compare(o, o_ref, lse, lse_ref, "e4m3", str(case), extra_bound=bound, extra_rows=few)
+    _log(f"[fp8 block attn] {case}: {e[3]} of {o.size} elements within the derived bound only "
+         f"({int(few.sum())} rows with < {gu.FEW_KEYS} effective keys)")
 
 
 def test_scale_placement_is_exact():
@@ -184,7 +187,8 @@ def test_fp8_error_per_tensor_block_rotated():
 def test_block_workload_full_size():
     """The e4m3 workload's shape (B8 H16 N4096 d128, 0.1% x20 outliers) in the launch
     configuration the benchmark times: the GPU quantiser's codes and scales equal the
-    oracle's everywhere, and the block-scaled attention matches the oracle on sampled rows."""
+    oracle's everywhere, and the block-scaled attention matches the oracle over every
+    output element (6e-2 * max(1, |O|) outside rows with few effective keys)."""
     w = synth_inputs.WORKLOADS["fp8_block_hadamard_b8_h16_n4096_d128"]
     _log(f"[fp8 block workload] {w.name}")
     inp = synth_inputs.workload_inputs(w)
@@ -204,10 +208,11 @@ def test_block_workload_full_size():
     o, lse = fa.fwd_fp8_block(dev_codes["q"][0], dev_codes["k"][0], dev_codes["v"][0], dev_codes["q"][1],
                               dev_codes["k"][1], dev_codes["v"][1], causal=w.causal, scale=scale)
     torch.cuda.synchronize()
-    rows = gu.sample_rows(w.B, w.H, w.N, n_random=40, seed=w.seed)
+    o_g, l_g = gu.host(o, lse)
+    del o, lse
     q, k, v = (oracle.block_dequantize(*ref[n]) for n in "qkv")
-    o_ref, lse_ref = oracle.attn_rows_f64(q[rows[:, 0], rows[:, 2], rows[:, 1]], k, v, w.H, rows, w.causal, scale)
-    o_g = o[rows[:, 0], rows[:, 2], rows[:, 1]].float().cpu().numpy().astype(np.float64)
-    l_g = lse[rows[:, 0], rows[:, 1], rows[:, 2]].cpu().numpy().astype(np.float64)
-    e = gu.compare(o_g, o_ref, l_g, lse_ref, "e4m3", w.name)
-    _log(f"[fp8 block workload] max scaled dO {e[0]:.2e}, max |dO| {e[1]:.2e}, max dlse {e[2]:.2e}")
+    o_ref, lse_ref = oracle.attn_fwd_f64(q, k, v, w.causal, scale)
+    bound, few = gu.fp8_failing_rows_bound_values(q, k, v, w.causal, scale, o_g, o_ref)
+    e = gu.compare(o_g, o_ref, l_g, lse_ref, "e4m3", w.name, extra_bound=bound, extra_rows=few)
+    _log(f"[fp8 block workload] every element: max scaled dO {e[0]:.2e}, max |dO| {e[1]:.2e}, "
+         f"max dlse {e[2]:.2e}; {e[3]} elements within the derived bound only")

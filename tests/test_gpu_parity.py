@@ -50,26 +50,22 @@ def test_small_full_parity(case):
 
 
 @pytest.mark.parametrize("name", [n for n, w in synth_inputs.WORKLOADS.items()
-                                  if w.dtype != "e4m3" and not w.fp8_block and not w.backward and not w.decode_nq])
-def test_workload_sampled_parity(name):
+                                  if w.dtype != "e4m3" and not w.fp8_block and not w.backward and not w.decode_nq
+                                  and not w.sparse_density])
+def test_workload_full_parity(name):
+    """Each 16-bit forward workload at full size, in the launch configuration the benchmark
+    times, against the oracle over every output element."""
     w = synth_inputs.WORKLOADS[name]
     _log(f"[workload] {name}")
     inp = synth_inputs.workload_inputs(w)
     o_d, lse_d = gu.run(inp, w.dtype, w.causal, w.scale, w.window)
-    assert bool(torch.isfinite(o_d.float()).all()) and bool(torch.isfinite(lse_d).all())
-    if w.N <= 128:
-        o_ref, lse_ref = oracle.attn_fwd(inp["q"], inp["k"], inp["v"], w.dtype, w.causal, w.scale,
-                                         window=w.window)
-        o_g, l_g = gu.host(o_d, lse_d)
-        gu.compare(o_g, o_ref, l_g, lse_ref, w.dtype, name)
-        return
-    rows = gu.sample_rows(w.B, w.H, w.N, n_random=40, seed=w.seed)
-    o_ref, lse_ref = oracle.attn_rows(inp["q"], inp["k"], inp["v"], w.dtype, w.causal, w.scale, rows,
-                                      window=w.window)
-    o_g = o_d[rows[:, 0], rows[:, 2], rows[:, 1]].float().cpu().numpy().astype(np.float64)
-    l_g = lse_d[rows[:, 0], rows[:, 1], rows[:, 2]].cpu().numpy().astype(np.float64)
+    o_g, l_g = gu.host(o_d, lse_d)
+    del o_d, lse_d
+    o_ref, lse_ref = oracle.attn_fwd(inp["q"], inp["k"], inp["v"], w.dtype, w.causal, w.scale, window=w.window)
     e = gu.compare(o_g, o_ref, l_g, lse_ref, w.dtype, name)
-    _log(f"[workload] {name}: max scaled dO {e[0]:.2e}, max |dO| {e[1]:.2e}, max dlse {e[2]:.2e}")
+    big = int((np.abs(o_ref) > 1).sum())
+    _log(f"[workload] {name}: every element of O {o_ref.shape} and lse {lse_ref.shape}: max scaled dO {e[0]:.2e}, "
+         f"max |dO| {e[1]:.2e}, max dlse {e[2]:.2e}; {big} elements with |O_ref| > 1")
 
 
 def _dev(x, dtype):
@@ -159,9 +155,11 @@ FP8_SMALL = [
 @pytest.mark.parametrize("case", FP8_SMALL, ids=lambda c: "-".join(map(str, c)))
 def test_fp8_small_full_parity(case):
     """e4m3 on small shapes, including causal rows that see only a few keys: there the error
-    of e4m3 probabilities is not averaged out, so an element passes either the stated
-    6e-2 * max(1, |O|) bound or the probability-rounding bound derived in
-    gpu_util.fp8_quantization_bound (lse stays within 1e-3 everywhere)."""
+    of e4m3 probabilities is not averaged out. Every element of a row with at least
+    FEW_KEYS effective keys (1 / sum of squared softmax weights) is held to the stated
+    6e-2 * max(1, |O|); an element of a row with fewer may instead pass the
+    probability-rounding bound derived in gpu_util.fp8_quantization_bound, and the number
+    that needed it is logged (lse stays within 1e-3 everywhere)."""
     B, H, Hkv, N, d, causal = case
     _log(f"[fp8 small] {case}")
     scale = 1.0 / np.sqrt(d)
@@ -169,7 +167,12 @@ def test_fp8_small_full_parity(case):
     o, lse = gu.host(*gu.run(inp, "e4m3", causal, scale))
     o_ref, lse_ref = oracle.attn_fwd(inp["q"], inp["k"], inp["v"], "e4m3", causal, scale, inp["descale"])
     bound = gu.fp8_quantization_bound(inp, causal, scale, o_ref)
-    gu.compare(o, o_ref, lse, lse_ref, "e4m3", str(case), extra_bound=bound)
+    dq, dk, _ = inp["descale"]
+    few = gu.effective_keys(oracle.decode(inp["q"], "e4m3", dq), oracle.decode(inp["k"], "e4m3", dk), causal,
+                            scale) < gu.FEW_KEYS
+    e = gu.compare(o, o_ref, lse, lse_ref, "e4m3", str(case), extra_bound=bound, extra_rows=few)
+    _log(f"[fp8 small] {case}: max scaled dO {e[0]:.2e}, {e[3]} of {o.size} elements within the derived bound "
+         f"only ({int(few.sum())} of {few.size} rows with < {gu.FEW_KEYS} effective keys)")
 
 
 def test_fp8_constant_values_exact():
@@ -185,17 +188,21 @@ def test_fp8_constant_values_exact():
         assert np.max(np.abs(o - ref) / np.maximum(1e-30, np.abs(ref))) <= 2.0 ** -8
 
 
-def test_fp8_workload_sampled_parity():
+def test_fp8_workload_full_parity():
+    """The e4m3 workload (B8 H16 N4096 d128, 0.1% x20 outliers, per-tensor scales) at full
+    size against the oracle over every element. Every element is held to 6e-2 *
+    max(1, |O|) except in rows with fewer than FEW_KEYS effective keys, where the
+    probability-rounding bound may apply instead; those elements are counted."""
     w = synth_inputs.WORKLOADS["fp8_e4m3_b8_h16_n4096_d128"]
     _log(f"[workload] {w.name}")
     inp = synth_inputs.workload_inputs(w)
     o_d, lse_d = gu.run(inp, w.dtype, w.causal, w.scale)
     assert o_d.dtype == torch.bfloat16
-    assert bool(torch.isfinite(o_d.float()).all()) and bool(torch.isfinite(lse_d).all())
-    rows = gu.sample_rows(w.B, w.H, w.N, n_random=40, seed=w.seed)
-    o_ref, lse_ref = oracle.attn_rows(inp["q"], inp["k"], inp["v"], w.dtype, w.causal, w.scale, rows,
-                                      inp["descale"])
-    o_g = o_d[rows[:, 0], rows[:, 2], rows[:, 1]].float().cpu().numpy().astype(np.float64)
-    l_g = lse_d[rows[:, 0], rows[:, 1], rows[:, 2]].cpu().numpy().astype(np.float64)
-    e = gu.compare(o_g, o_ref, l_g, lse_ref, "e4m3", w.name)
-    _log(f"[workload] {w.name}: max scaled dO {e[0]:.2e}, max |dO| {e[1]:.2e}, max dlse {e[2]:.2e}")
+    o_g, l_g = gu.host(o_d, lse_d)
+    del o_d, lse_d
+    o_ref, lse_ref = oracle.attn_fwd(inp["q"], inp["k"], inp["v"], w.dtype, w.causal, w.scale, inp["descale"])
+    bound, few = gu.fp8_failing_rows_bound(inp, w.causal, w.scale, o_g, o_ref)
+    e = gu.compare(o_g, o_ref, l_g, lse_ref, "e4m3", w.name, extra_bound=bound, extra_rows=few)
+    _log(f"[workload] {w.name}: every element: max scaled dO {e[0]:.2e}, max |dO| {e[1]:.2e}, max dlse {e[2]:.2e}; "
+         f"{e[3]} of {o_g.size} elements within the derived bound only ({int(few.sum())} rows with < "
+         f"{gu.FEW_KEYS} effective keys)")

@@ -56,6 +56,18 @@ MUTANTS = {
     "block_causal_ignored": ("!= 0 && (!causal || j <= i);", "!= 0;"),
     "block_empty_row_unguarded": ("if (m == -INFINITY) {                      /* no visible key */",
                                   "if (0) {"),
+    # the single-row entry points
+    "rows_window_dropped": ("key_range(i, N, causal, left, right, &jlo, &jhi);\n      attn_row(qi, k, v, Hkv, N, d, "
+                            "jlo, jhi, scale, b, h / group, s, o_rows",
+                            "key_range(i, N, causal, -1, -1, &jlo, &jhi);\n      attn_row(qi, k, v, Hkv, N, d, "
+                            "jlo, jhi, scale, b, h / group, s, o_rows"),
+    "rows_gqa_modulo": ("jlo, jhi, scale, b, h / group, s, o_rows", "jlo, jhi, scale, b, h % Hkv, s, o_rows"),
+    "rows_gathered_query_reversed": ("q_is_rows ? q + (size_t)r * d :", "q_is_rows ? q + (size_t)(nrows - 1 - r) * d :"),
+    "rows_lse_slot_shifted": ("lse_rows + r);", "lse_rows + (r + 1) % nrows);"),
+    "block_rows_causal_dropped": ("block_keep(mask, mask_heads, block, N, causal, h, i, keep);\n      "
+                                  "attn_row_keep(qi, k, v, Hkv, N, d, keep, scale, b, h / group, s, o_rows",
+                                  "block_keep(mask, mask_heads, block, N, 0, h, i, keep);\n      "
+                                  "attn_row_keep(qi, k, v, Hkv, N, d, keep, scale, b, h / group, s, o_rows"),
 }
 
 # mutants of the block-quantisation oracle (fp8_quant_oracle.c)
@@ -89,6 +101,17 @@ BMUTANTS = {
                       "const double* vj = k + (((size_t)b * N + j) * Hkv + hk) * d;"),
     "bwd_window_left_off_by_one": ("if (left >= 0 && i - left > lo) lo = i - left;",
                                    "if (left >= 0 && i - left + 1 > lo) lo = i - left + 1;"),
+    # the key-row gradient and the absolute-value sums
+    "dkdv_rows_causal_from_zero": ("for (int i = causal ? j : 0; i < N; ++i) {", "for (int i = 0; i < N; ++i) {"),
+    "dkdv_rows_causal_skips_diagonal": ("for (int i = causal ? j : 0; i < N; ++i) {",
+                                        "for (int i = causal ? j + 1 : 0; i < N; ++i) {"),
+    "dkdv_rows_lse_unscaled": ("const double p = exp(scale * s - lse[row]);", "const double p = exp(s - lse[row]);"),
+    "dkdv_rows_D_dropped": ("const double ds = p * (dp - D[row]);", "const double ds = p * dp;"),
+    "dkdv_rows_one_head": ("for (int h = hk * group; h < (hk + 1) * group; ++h)", "for (int h = hk * group; h == hk * group; ++h)"),
+    "dkdv_rows_dv_from_q": ("dvj[t] += p * gi[t];", "dvj[t] += p * qi[t];"),
+    "dkdv_mag_signed": ("m1[t] += fabs(ds) * fabs(qi[t]);", "m1[t] += ds * fabs(qi[t]);"),
+    "dkdv_mag_weight_dropped": ("m1[d + t] += p * w[row] * fabs(qi[t]);", "m1[d + t] += p * fabs(qi[t]);"),
+    "dq_mag_p_signed_k": ("m2[t] += p[j] * fabs(kj[t]);", "m2[t] += p[j] * kj[t];"),
 }
 
 ALL = {**{n: (SRC,) + m for n, m in MUTANTS.items()}, **{n: (QSRC,) + m for n, m in QMUTANTS.items()},
