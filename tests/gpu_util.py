@@ -122,9 +122,9 @@ def sample_rows(B: int, H: int, N: int, n_random: int, seed: int, br: int = QUER
     """Rows (b, h, i) to spot-check: first and last positions, both sides of query-tile
     (workgroup) and key-tile boundaries, and random rows."""
     rng = np.random.default_rng(seed)
-    fixed_i = sorted({0, 1, N - 1, N - 2, min(63, N - 1), min(64, N - 1), min(br - 1, N - 1), min(br, N - 1),
-                      min(br + 31, N - 1), min(br + 32, N - 1),
-                      N // 2, (N // br) * br - 1 if N > br else 0, (N // br) * br if N > br else 0})
+    last = (N // br) * br
+    fixed_i = sorted({min(max(i, 0), N - 1) for i in (0, 1, N - 1, N - 2, 63, 64, br - 1, br, br + 31, br + 32,
+                                                      N // 2, last - 1, last)})
     rows = []
     for i in fixed_i:
         rows.append((int(rng.integers(B)), int(rng.integers(H)), max(0, i)))
