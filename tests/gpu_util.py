@@ -35,9 +35,9 @@ def host(o: torch.Tensor, lse: torch.Tensor):
 
 def compare(o, o_ref, lse, lse_ref, dtype: str, what: str = "", extra_bound=None, extra_rows=None):
     """Assert the parity bound; return (max scaled dO, max |dO|, max |dlse|, n_extra). With
-    `extra_bound` (an elementwise array), an element whose row is flagged in `extra_rows`
-    (a boolean array over o's leading axes; every row when None) also passes when |dO| is
-    within it; n_extra counts the elements that pass only that way."""
+    `extra_bound` (an elementwise array), an element flagged in `extra_rows` (a boolean
+    array like o; every element when None) also passes when |dO| is within it; n_extra
+    counts the elements that pass only that way."""
     assert np.all(np.isfinite(o)), f"{what}: non-finite output"
     assert np.all(np.isfinite(lse)), f"{what}: non-finite lse"
     err = np.abs(o - o_ref)
@@ -52,28 +52,50 @@ def compare(o, o_ref, lse, lse_ref, dtype: str, what: str = "", extra_bound=None
         main_ok = scaled <= TOL[dtype]
         alt_ok = err <= extra_bound
         if extra_rows is not None:
-            alt_ok &= np.asarray(extra_rows, dtype=bool)[..., None]
+            alt_ok &= np.asarray(extra_rows, dtype=bool)
         ok = main_ok | alt_ok
         n_extra = int((~main_ok & alt_ok).sum())
-        assert np.all(ok), f"{what}: {int((~ok).sum())} elements outside both bounds (max scaled {e_o:.3e})"
+        if not np.all(ok):
+            idx = np.argwhere(~ok)[:8]
+            detail = "; ".join(f"{tuple(int(x) for x in ix)}: got {o[tuple(ix)]:.4f} ref {o_ref[tuple(ix)]:.4f} "
+                               f"bound {np.broadcast_to(extra_bound, o.shape)[tuple(ix)]:.4f}" for ix in idx)
+            raise AssertionError(f"{what}: {int((~ok).sum())} elements outside both bounds (max scaled {e_o:.3e}): "
+                                 f"{detail}")
     assert e_l <= LSE_TOL, f"{what}: max |dlse| {e_l:.3e} > {LSE_TOL}"
     return e_o, e_abs, e_l, n_extra
 
 
-# rows that see fewer effective keys than this may use the e4m3 probability-rounding bound
-FEW_KEYS = 64
+# The stated e4m3 tolerance (6e-2 * max(1, |O|)) is for outputs averaged over many keys of
+# unit-scale V. Rounding each probability to e4m3 (relative error d_j, |d_j| <= u = 2^-4,
+# taken as independent and uniform) moves element (i, t) of O by sum_j w_ij d_j
+# (v_jt - O_it), whose standard deviation is (u / sqrt 3) rho_it with
+# rho_it = sqrt(sum_j w_ij^2 (v_jt - O_it)^2). An element is inside the regime of the stated
+# tolerance when four of those standard deviations fit in it, rho_it <= RHO_MAX; that holds
+# for N(0,1) V once a row has about six effective keys. Elsewhere -- rows dominated by a
+# few keys, or x20 outlier values of V that carry weight -- an element may instead pass the
+# worst-case probability-rounding bound of fp8_bound_from_values; tests count them.
+RHO_MAX = TOL["e4m3"] * 3.0 ** 0.5 / (4 * 2.0 ** -4)
 
 
-def effective_keys(q: np.ndarray, k: np.ndarray, causal: bool, scale: float, window=None) -> np.ndarray:
-    """1 / sum_j w_ij^2 of every row's softmax weights (its effective number of visible
-    keys), [B, N, H], from the oracle's probabilities (small shapes)."""
+def _rho(wts: np.ndarray, vrows: np.ndarray, o_row: np.ndarray) -> np.ndarray:
+    """rho of one row: softmax weights wts [n] over key rows vrows [n, d], output o_row [d]."""
+    return np.sqrt((wts * wts) @ (vrows - o_row[None, :]) ** 2)
+
+
+def fp8_exempt_elements(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: float,
+                        o_ref: np.ndarray, window=None) -> np.ndarray:
+    """Elements outside the regime of the stated e4m3 tolerance (rho > RHO_MAX), like
+    o_ref, from the oracle's probabilities (small shapes; exact fp64 inputs)."""
     import oracle
     B, N, H, _ = q.shape
-    out = np.empty((B, N, H))
+    g = H // k.shape[2]
+    out = np.zeros(o_ref.shape, dtype=bool)
     for b in range(B):
         for h in range(H):
-            w = oracle.attn_probs_f64(q, k, b, h, causal, scale, window)
-            out[b, :, h] = 1.0 / np.sum(w * w, axis=1)
+            w = oracle.attn_probs_f64(q, k, b, h, causal, scale, window)            # [N, N]
+            vh = v[b, :, h // g, :]
+            dev2 = (vh[None, :, :] - o_ref[b, :, h, None, :]) ** 2                  # [N(i), N(j), d]
+            out[b, :, h] = np.sqrt(np.einsum("ij,ijt->it", w * w, dev2)) > RHO_MAX
     return out
 
 
@@ -184,13 +206,13 @@ def fp8_failing_rows_bound(inp: dict, causal: bool, scale: float, o: np.ndarray,
 def fp8_failing_rows_bound_values(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool, scale: float,
                                   o: np.ndarray, o_ref: np.ndarray, window=None):
     """For a full-size e4m3 output: the probability-rounding bound of
-    fp8_bound_from_values and the few-effective-keys flag, evaluated only on the rows that
-    have an element outside 6e-2 * max(1, |O_ref|) (elsewhere the bound is 0 and the flag
-    False), from each such row's oracle softmax weights (q, k, v: exact fp64 input values).
-    Returns (bound like o, flags [B, N, H])."""
+    fp8_bound_from_values and the outside-the-regime flag (rho > RHO_MAX) of every element,
+    evaluated only on the rows that have an element outside 6e-2 * max(1, |O_ref|)
+    (elsewhere the bound is 0 and the flag False), from each such row's oracle softmax
+    weights (q, k, v: exact fp64 input values). Returns (bound, flags), both like o."""
     bad = np.any(np.abs(o - o_ref) > TOL["e4m3"] * np.maximum(1.0, np.abs(o_ref)), axis=-1)   # [B, N, H]
     bound = np.zeros_like(o_ref)
-    few = np.zeros(bad.shape, dtype=bool)
+    few = np.zeros(o_ref.shape, dtype=bool)
     H, Hkv = q.shape[2], k.shape[2]
     u = 2.0 ** -4
     for b, i, h in zip(*np.nonzero(bad)):
@@ -206,7 +228,7 @@ def fp8_failing_rows_bound_values(q: np.ndarray, k: np.ndarray, v: np.ndarray, c
         s = scale * (kb @ q[b, i, h])
         wts = np.exp(s - s.max())
         wts /= wts.sum()
-        few[b, i, h] = 1.0 / np.sum(wts * wts) < FEW_KEYS
+        few[b, i, h] = _rho(wts, vb, o_ref[b, i, h]) > RHO_MAX
         dev = np.abs(vb - o_ref[b, i, h][None, :])
         bound[b, i, h] = (2 * u / (1 - u)) * (wts @ dev) + 2.0 ** -8 * np.abs(o_ref[b, i, h]) + 2e-3
     return bound, few
