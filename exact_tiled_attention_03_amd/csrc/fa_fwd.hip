@@ -1288,10 +1288,11 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported configuration";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
+    case FA_ERR_SCRATCH: return "FA_ERR_SCRATCH: the request needs more than the library's static scratch";
   }
   return "unknown fa_status";
 }
 
-int fa_version(void) { return 10200; }
+int fa_version(void) { return 10300; }
 
 }  // extern "C"

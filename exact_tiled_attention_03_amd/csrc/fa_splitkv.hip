@@ -22,6 +22,8 @@
 // softmax is lane-local (one query row per lane pair).
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include <cmath>
 #include <cstdint>
 
@@ -364,39 +366,24 @@ fa_status dispatch_rb(const SkvArgs& args, int causal, hipStream_t s) {
   return causal ? launch_partial<Ops, D, 2, true>(args, s) : launch_partial<Ops, D, 2, false>(args, s);
 }
 
-}  // namespace
+// The workspace of one call: every partial output and lse is written by the partial kernel
+// before the merge kernel reads it, so the buffer's previous contents never matter.
+size_t splitkv_bytes(int B, int H, int Nq, int d, int S) { return (size_t)S * B * H * Nq * (d + 1) * sizeof(float); }
 
-extern "C" {
-
-size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, int num_splits) {
-  if (B < 1 || H < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return 0;
-  int S, L;
-  plan(B, Hkv, Nk, num_splits, &S, &L);
-  return (size_t)S * B * H * Nq * (d + 1) * sizeof(float);
-}
-
-fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                         int Hkv, int Nq, int Nk, int d, int causal, float scale, fa_dtype dtype,
-                         int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
-  fa_status st = check_splitkv(B, H, Hkv, Nq, Nk, d, causal, dtype);
-  if (st != FA_OK) return st;
-  if (!q || !k || !v || !o || !lse || !workspace) return FA_ERR_INVALID_ARG;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 4) || !aligned(lse, 4) ||
-      !aligned(workspace, 16))
-    return FA_ERR_INVALID_ARG;
-  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+fa_status splitkv_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
+                       int Nq, int Nk, int d, int causal, float scale, fa_dtype dtype, int num_splits,
+                       float* workspace, size_t workspace_bytes, hipStream_t s) {
   SkvArgs args;
   plan(B, Hkv, Nk, num_splits, &args.S, &args.L);
-  const size_t need = (size_t)args.S * B * H * Nq * (d + 1) * sizeof(float);
-  if (workspace_bytes < need) return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < splitkv_bytes(B, H, Nq, d, args.S)) return FA_ERR_INVALID_ARG;
   if ((long long)B * Hkv * args.S > 0x7fffffffLL - 3) return FA_ERR_INVALID_ARG;
   args.q = q;
   args.k = k;
   args.v = v;
   args.o = o;
   args.lse = lse;
-  args.part_o = (float*)workspace;
-  args.part_lse = (float*)workspace + (size_t)args.S * B * H * Nq * d;
+  args.part_o = workspace;
+  args.part_lse = workspace + (size_t)args.S * B * H * Nq * d;
   args.B = B;
   args.H = H;
   args.Hkv = Hkv;
@@ -406,9 +393,79 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
   args.rows = args.group * Nq;
   args.units = B * Hkv * args.S;
   args.c = (float)((double)scale * 1.4426950408889634);
-  hipStream_t s = (hipStream_t)stream;
   if (dtype == FA_DTYPE_BF16) return d == 128 ? dispatch_rb<Bf16, 128>(args, causal, s) : dispatch_rb<Bf16, 64>(args, causal, s);
   return d == 128 ? dispatch_rb<F16, 128>(args, causal, s) : dispatch_rb<F16, 64>(args, causal, s);
+}
+
+fa_status splitkv_checks(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv,
+                         int Nq, int Nk, int d, int causal, float scale, fa_dtype dtype) {
+  fa_status st = check_splitkv(B, H, Hkv, Nq, Nk, d, causal, dtype);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 4) || !aligned(lse, 4))
+    return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+// Library-owned scratch for fa_fwd_splitkv_static: one copy of this array per GPU, held
+// until the process ends. Host code never passes the array's name to a kernel (in host
+// code it is a host-side stand-in, not a device address); it uses the device address that
+// hipGetSymbolAddress returns on each device, looked up once per device on that device's
+// first call.
+constexpr size_t kStaticScratchBytes = FA_SPLITKV_STATIC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// this device's address of `scratch` (nullptr if the lookup failed)
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d, int num_splits) {
+  if (B < 1 || H < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1) return 0;
+  int S, L;
+  plan(B, Hkv, Nk, num_splits, &S, &L);
+  return splitkv_bytes(B, H, Nq, d, S);
+}
+
+fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                         int Hkv, int Nq, int Nk, int d, int causal, float scale, fa_dtype dtype,
+                         int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  fa_status st = splitkv_checks(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!workspace || !aligned(workspace, 16)) return FA_ERR_INVALID_ARG;
+  return splitkv_impl(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal, scale, dtype, num_splits, (float*)workspace,
+                      workspace_bytes, (hipStream_t)stream);
+}
+
+fa_status fa_fwd_splitkv_static(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                int Hkv, int Nq, int Nk, int d, int causal, float scale, fa_dtype dtype,
+                                int num_splits, void* stream) {
+  fa_status st = splitkv_checks(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  int S, L;
+  plan(B, Hkv, Nk, num_splits, &S, &L);
+  if (splitkv_bytes(B, H, Nq, d, S) > kStaticScratchBytes) return FA_ERR_SCRATCH;
+  void* ws = scratch_on_current_device();
+  if (!ws) return FA_ERR_LAUNCH;
+  return splitkv_impl(q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, causal, scale, dtype, num_splits, (float*)ws,
+                      kStaticScratchBytes, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -12,7 +12,8 @@ import threading
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libfa.so")
 
-FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH = 0, 1, 2, 3
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_LAUNCH, FA_ERR_SCRATCH = 0, 1, 2, 3, 4
+SPLITKV_STATIC_SCRATCH_BYTES = 32 << 20   # FA_SPLITKV_STATIC_SCRATCH_BYTES
 FP8_BLOCK_ROWS = 64      # FA_FP8_BLOCK_ROWS
 FA_DTYPE_F16, FA_DTYPE_BF16, FA_DTYPE_FP8_E4M3 = 0, 1, 2
 DTYPE_NAMES = {"f16": FA_DTYPE_F16, "bf16": FA_DTYPE_BF16, "e4m3": FA_DTYPE_FP8_E4M3}
@@ -57,6 +58,8 @@ def lib() -> ctypes.CDLL:
             L.fa_fwd_splitkv_workspace_bytes.restype = ctypes.c_size_t
             L.fa_fwd_splitkv.argtypes = [vp] * 5 + [c_int] * 7 + [c_float, c_int, c_int, vp, ctypes.c_size_t, vp]
             L.fa_fwd_splitkv.restype = c_int
+            L.fa_fwd_splitkv_static.argtypes = [vp] * 5 + [c_int] * 7 + [c_float, c_int, c_int, vp]
+            L.fa_fwd_splitkv_static.restype = c_int
             L.fa_fwd_query.argtypes = [c_int] * 7 + [szp] * 5
             L.fa_fwd_query.restype = c_int
             L.fa_status_string.argtypes = [c_int]
@@ -136,6 +139,14 @@ def fa_fwd_splitkv(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int,
     """Direct call of fa_fwd_splitkv with raw pointers; returns the status code."""
     return int(lib().fa_fwd_splitkv(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Hkv, Nq, Nk, d, int(causal),
                                     float(scale), int(dtype), int(num_splits), ws_ptr, int(ws_bytes), stream))
+
+
+def fa_fwd_splitkv_static(q_ptr: int, k_ptr: int, v_ptr: int, o_ptr: int, lse_ptr: int, B: int, H: int, Hkv: int,
+                          Nq: int, Nk: int, d: int, causal: int, scale: float, dtype: int, num_splits: int,
+                          stream: int = 0) -> int:
+    """Direct call of fa_fwd_splitkv_static (no workspace, no allocation); returns the status code."""
+    return int(lib().fa_fwd_splitkv_static(q_ptr, k_ptr, v_ptr, o_ptr, lse_ptr, B, H, Hkv, Nq, Nk, d, int(causal),
+                                           float(scale), int(dtype), int(num_splits), stream))
 
 
 def fa_fwd_query(B: int, H: int, Hkv: int, N: int, d: int, causal: int, dtype: int) -> dict:
@@ -358,6 +369,29 @@ def bwd(q, k, v, o, lse, dout, causal: bool = False, scale: float | None = None,
                   dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, N, d, int(bool(causal)), scale, code,
                   workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream(q, stream)))
     return dq, dk, dv
+
+
+def fwd_splitkv_static(q, k, v, out, lse, causal: bool = False, scale: float | None = None, num_splits: int = 0,
+                       stream=None):
+    """fwd_splitkv into caller-provided out [B,Nq,H,d] and lse [B,H,Nq] with the library's
+    static scratch instead of a workspace: allocates nothing (for graph capture and serving
+    loops). Calls that overlap on one GPU race. Returns (out, lse)."""
+    code = _dtype_code(q, None)
+    B, Nq, H, d = q.shape
+    Hkv = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    for t in (q, k, v, out, lse):
+        if not t.is_contiguous() or t.device != q.device:
+            raise ValueError("tensors must be contiguous and on the same device")
+    if k.dim() != 4 or tuple(v.shape) != tuple(k.shape) or k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k and v must be [B,Nk,Hkv,d] matching q")
+    _same_elem_type(q, (k, v, out), "q, k, v and out")
+    if tuple(out.shape) != (B, Nq, H, d) or tuple(lse.shape) != (B, H, Nq) or str(lse.dtype) != "torch.float32":
+        raise ValueError("out/lse have the wrong shape or type")
+    _check(fa_fwd_splitkv_static(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Hkv,
+                                 Nq, k.shape[1], d, int(bool(causal)), scale, code, num_splits, _stream(q, stream)))
+    return out, lse
 
 
 def fwd_splitkv(q, k, v, causal: bool = False, scale: float | None = None, num_splits: int = 0, out=None, lse=None,

@@ -54,7 +54,8 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1,   /* null/misaligned pointer, bad size, bad flag, bad scale */
   FA_ERR_UNSUPPORTED = 2,   /* valid request the kernels do not implement (e.g. d) */
-  FA_ERR_LAUNCH = 3         /* the HIP runtime rejected the launch */
+  FA_ERR_LAUNCH = 3,        /* the HIP runtime rejected the launch */
+  FA_ERR_SCRATCH = 4        /* the request needs more than the library's static scratch */
 } fa_status;
 
 typedef enum {
@@ -221,6 +222,25 @@ fa_status fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, f
                          void* stream);
 
 /*
+ * fa_fwd_splitkv without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation. Same arguments (minus workspace and workspace_bytes), semantics, kernels and
+ * results as fa_fwd_splitkv with the same num_splits. The partial outputs go to a scratch
+ * array of FA_SPLITKV_STATIC_SCRATCH_BYTES bytes that the library holds on each GPU it
+ * runs on until the process ends; requests whose fa_fwd_splitkv_workspace_bytes exceeds
+ * that size return FA_ERR_SCRATCH (use fa_fwd_splitkv with a caller workspace). The call
+ * allocates nothing. Every call on one GPU shares that GPU's array: calls that overlap on
+ * one GPU (concurrent streams, or threads) race and must be serialised by the caller.
+ * Nothing in the array needs to start at zero: each call writes every partial it reads.
+ * The array's device address is looked up on a device's first call (FA_ERR_LAUNCH if the
+ * lookup fails).
+ */
+#define FA_SPLITKV_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
+fa_status fa_fwd_splitkv_static(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                int H, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                                fa_dtype dtype, int num_splits, void* stream);
+
+/*
  * Shape query: byte sizes of every buffer fa_fwd reads or writes for these arguments,
  * after the same size checks fa_fwd makes. Any output pointer may be NULL.
  * workspace_bytes is always 0 (no scratch memory). Pure host function.
@@ -232,7 +252,7 @@ fa_status fa_fwd_query(int B, int H, int Hkv, int N, int d, int causal, fa_dtype
 /* Static, human-readable text for a status code. */
 const char* fa_status_string(fa_status s);
 
-/* Library version, encoded as major * 10000 + minor * 100 + patch (10200: fa_fwd_block_sparse). */
+/* Library version, encoded as major * 10000 + minor * 100 + patch (10300: fa_fwd_splitkv_static). */
 int fa_version(void);
 
 #ifdef __cplusplus

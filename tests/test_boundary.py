@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     assert fa.version() >= 100
-    for s in range(4):
+    for s in range(5):
         assert fa.status_string(s).startswith("FA_")
     assert "unknown" in fa.status_string(99)
 
@@ -247,6 +247,31 @@ def test_splitkv_rejects_before_launch(over, status):
     a.update(over)
     st = fa.fa_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"],
                            a["d"], a["causal"], a["scale"], a["dtype"], a["splits"], a["ws"], a["ws_bytes"])
+    assert st == status
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(q=0), fa.FA_ERR_INVALID_ARG),
+    (dict(o=0), fa.FA_ERR_INVALID_ARG),
+    (dict(q=FAKE + 8), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=10, Nk=5), fa.FA_ERR_INVALID_ARG),
+    (dict(H=16, Hkv=2, Nq=9), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=fa.FA_DTYPE_FP8_E4M3), fa.FA_ERR_UNSUPPORTED),
+    (dict(scale=-1.0), fa.FA_ERR_INVALID_ARG),
+    # partials of 4096 splits x 32 heads x 129 floats = 67.6 MB > the 32 MiB static scratch
+    (dict(B=1, H=32, Hkv=8, Nq=1, Nk=1 << 17, splits=4096), fa.FA_ERR_SCRATCH),
+])
+def test_splitkv_static_rejects_before_launch(over, status):
+    """fa_fwd_splitkv_static makes the same host checks as fa_fwd_splitkv, and refuses a
+    request whose partials exceed its static scratch, before any HIP call."""
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, H=4, Hkv=2, Nq=1, Nk=64, d=128, causal=0, scale=0.1,
+             dtype=fa.FA_DTYPE_BF16, splits=0)
+    a.update(over)
+    if status == fa.FA_ERR_SCRATCH:
+        need = fa.fa_fwd_splitkv_workspace_bytes(a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"], a["d"], a["splits"])
+        assert need > fa.SPLITKV_STATIC_SCRATCH_BYTES
+    st = fa.fa_fwd_splitkv_static(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["Hkv"], a["Nq"], a["Nk"],
+                                  a["d"], a["causal"], a["scale"], a["dtype"], a["splits"])
     assert st == status
 
 
