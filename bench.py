@@ -255,7 +255,8 @@ def main():
         (qc, qs), (kc, ks), (vc, vs) = qz
 
         def step(o=None, lse=None):
-            return fa.fwd_fp8_block(qc, kc, vc, qs, ks, vs, causal=w.causal, scale=w.scale / w.d, out=o, lse=lse)
+            return fa.fwd_fp8_block(qc, kc, vc, qs, ks, vs, causal=w.causal, scale=w.scale / w.d, out=o, lse=lse,
+                                    qk_e4m3=True)
     elif w.decode_nq:
         # split-KV decode: a step is one fa_fwd_splitkv call (partials + merge)
         nbytes = fa.fa_fwd_splitkv_workspace_bytes(w.B, w.H, w.Hkv, w.decode_nq, w.N, w.d, 0)
@@ -350,7 +351,8 @@ def main():
                                         "kept_blocks": round(float(synth_inputs.workload_block_mask(w).mean()), 4),
                                         "pattern": "local + global + random key blocks per 256-query group"}}
                       if w.sparse_density else {}),
-                   **({"fp8": "block scales (64 rows, E8M0), Hadamard-rotated q/k"} if w.fp8_block else {})},
+                   **({"fp8": "block scales (64 rows, E8M0), Hadamard-rotated q/k, Q K^T on the e4m3 MFMA"}
+                      if w.fp8_block else {})},
         "roofline": roof,
         "sclk": clocks.summary(),
     }

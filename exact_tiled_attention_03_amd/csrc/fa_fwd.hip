@@ -241,6 +241,8 @@ using ic = std::integral_constant<int, V>;
 // after the barrier that ended the last read of that slot.
 // s_waitcnt operand: vmcnt <= 8, expcnt and lgkmcnt not waited for
 constexpr int kVmcnt8 = 0x8 | (0x7 << 4) | (0xF << 8);
+// s_waitcnt operand: vmcnt <= 4, expcnt and lgkmcnt not waited for
+constexpr int kVmcnt4 = 0x4 | (0x7 << 4) | (0xF << 8);
 
 // one 16-byte-per-lane buffer load into LDS: lane i writes dst + 16 i
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, lds_byte* dst, unsigned voffset) {
@@ -1072,6 +1074,390 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
   }
 }
 
+// ---- the forward kernel for e4m3 inputs on fp8 MFMAs -----------------------------------
+// Both products on the e4m3 MFMA v_mfma_scale_f32_32x32x64_f8f6f4 (four times the bf16
+// MFMA's k per instruction, at the same cycle count per 32 x 32 output block):
+//   * S^T = K Q^T: A = a K tile row (64 dims of one key, 32 bytes per lane), B = the Q row
+//     (the same 64 dims of one query); any pairing of dims between A and B bytes gives the
+//     same sum, so each lane holds 32 consecutive bytes of its row. Q and K block scales
+//     (E8M0) go into the instruction's scale operands and are applied exactly;
+//   * O^T += V^T P^T as in the kernel above (one MFMA per 32 dims covers the tile's 64 keys),
+//     with the sum of the stored probabilities from one more MFMA against all-ones.
+// K tiles go from global memory straight into LDS (LDS DMA) as e4m3 bytes; V passes through
+// registers and is transposed into V^T there (4 x 4 byte transposes). The workgroup and
+// schedule follow the 16-bit kernel: 8 wavefronts of 32 query rows in lockstep, two K and two
+// V^T slots, one barrier per key tile. Because one P.V MFMA consumes all 64 keys of P, P.V
+// of tile j is deferred to step j+1, where it runs beside the MFMAs of S(j+2) and the softmax
+// of tile j+1, so the softmax is spread over all nine MFMAs of a step.
+// The running maximum moves only when a tile's maximum exceeds it by more than kTau (the
+// maximum is taken in the step before the tile's exponentials); probabilities are stored as
+// e4m3 times 2^kOff, p <= 2^(kTau + kOff) = 2^8.5 < 448, so the bulk of them lies in
+// e4m3's normal range. O is normalised by the sum of the stored probabilities (O is a
+// convex combination of V rows); lse uses the float32 sum of the unrounded ones.
+// K tile in LDS: row r (key) of D bytes, 16-byte chunk c at c ^ k8swz(r), so that 16
+// consecutive rows read at one logical chunk hit 16 different 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int k8swz(int r) {
+  return D == 128 ? (r >> 1) & 7 : (r >> 2) & 3;
+}
+constexpr int kMaxScaleTiles = 2048;            // block-scaled e4m3: N <= 131072
+
+template <int D, int MASK, bool BLOCK>
+__global__ __launch_bounds__(kThreads) void fa_fwd_e4m3qk_kernel(FwdArgs a) {
+  constexpr bool CAUSAL = MASK == kMaskCausal;
+  constexpr bool BAND = MASK == kMaskBand;
+  constexpr float kTau = 2.5f;
+  constexpr float kOff = 6.0f;
+  constexpr int kKsteps = D / 64;                 // 64-dim k-steps of S^T
+  constexpr int kDblocks = D / 32;                // 32-row blocks of O^T
+  constexpr int kKb = kBc / 32;                   // 32-key blocks per tile
+  constexpr int kChunks = D / 16;                 // 16-byte chunks per K row
+  constexpr int kTileK = kBc * D;                 // e4m3 K tile
+  constexpr int kTileV = D * kBc;                 // e4m3 V^T tile
+  constexpr int kVBase = 2 * kTileK;
+  constexpr int kOnesBase = kVBase + 2 * kTileV;  // 32 x 64 e4m3 ones: A operand of the probability sum
+  constexpr int kSOps = kKsteps * kKb;            // S^T MFMAs per tile
+  static_assert(kBc == 64 && FA_FP8_BLOCK_ROWS == kBc, "one P.V MFMA and one block scale per key tile");
+
+  // K slot 0, K slot 1, V^T slot 0, V^T slot 1, ones
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kTileK + 2 * kTileV + 32 * kBc];
+  // block scales of the K and V tiles of this (batch, K/V head), two entries of 127 (2^0)
+  // past the end
+  __shared__ unsigned char kscale[BLOCK ? kMaxScaleTiles + 4 : 1];
+  __shared__ unsigned char vscale[BLOCK ? kMaxScaleTiles + 4 : 1];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const TileCoord tc = tile_of_workgroup(a, blockIdx.x, MASK != kMaskNone);
+  const int b = tc.b, h = tc.h, qt = tc.qt;
+  const int hk = h / a.group;
+  const int N = a.N;
+  const int q0 = qt * kBr;
+  const int qw0 = q0 + wave * 32;
+  const int qi = qw0 + l32;
+  const int kv0 = BAND ? max(0, q0 - a.wl) / kBc * kBc : 0;
+  const int nk = N - kv0;
+  const size_t q_row_stride = (size_t)a.H * D;    // bytes
+  const size_t kv_row_stride = (size_t)a.Hkv * D;
+  const uint8_t* qp = (const uint8_t*)a.q + ((size_t)b * N) * q_row_stride + (size_t)h * D;
+  const uint8_t* kp = (const uint8_t*)a.k + ((size_t)b * N + kv0) * kv_row_stride + (size_t)hk * D;
+  const uint8_t* vp = (const uint8_t*)a.v + ((size_t)b * N + kv0) * kv_row_stride + (size_t)hk * D;
+
+  // Q^T operand: lane holds q[qi][64 ks + 32 hi .. + 31] for k-step ks. The wavefront's 32
+  // queries lie in one scale block.
+  const int qi_ld = min(qi, N - 1);
+  int q_sc = 0;
+  if constexpr (BLOCK) q_sc = a.q_scales[((size_t)b * a.H + h) * a.nb + min(qw0, N - 1) / FA_FP8_BLOCK_ROWS];
+  i32x8 qreg[kKsteps];
+#pragma unroll
+  for (int ks = 0; ks < kKsteps; ++ks) {
+    const u32x4 x0 = *(const u32x4*)(qp + (size_t)qi_ld * q_row_stride + ks * 64 + hi * 32);
+    const u32x4 x1 = *(const u32x4*)(qp + (size_t)qi_ld * q_row_stride + ks * 64 + hi * 32 + 16);
+    qreg[ks] = i32x8{(int)x0[0], (int)x0[1], (int)x0[2], (int)x0[3], (int)x1[0], (int)x1[1], (int)x1[2], (int)x1[3]};
+  }
+
+  const int kv_end = BAND ? min(N, q0 + kBr + a.wr) : CAUSAL ? min(N, q0 + kBr) : N;
+  const int ntiles = (kv_end - kv0 + kBc - 1) / kBc;
+  if constexpr (BLOCK) {
+    const size_t sc0 = ((size_t)b * a.Hkv + hk) * a.nb + kv0 / kBc;
+    for (int t = tid; t < ntiles + 4; t += kThreads) {
+      const bool in = t < ntiles && kv0 / kBc + t < a.nb;
+      kscale[t] = in ? a.k_scales[sc0 + t] : (unsigned char)127;
+      vscale[t] = in ? a.v_scales[sc0 + t] : (unsigned char)127;
+    }
+  }
+
+  // S^T operand reads: key l32 of 32-key block kb, chunks 4 ks + 2 hi and + 1
+  int koff[kKsteps][2];
+#pragma unroll
+  for (int ks = 0; ks < kKsteps; ++ks)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) koff[ks][x] = l32 * D + (((4 * ks + 2 * hi + x) ^ k8swz<D>(l32)) << 4);
+  constexpr int kKbStride = 32 * D;               // bytes between the 32-key blocks of a K tile
+  int voff[kDblocks][2];
+#pragma unroll
+  for (int db = 0; db < kDblocks; ++db)
+#pragma unroll
+    for (int x = 0; x < 2; ++x) voff[db][x] = kVBase + vt8_byte(db * 32 + l32, hi * 32 + x * 16);
+
+  // ---- staging ------------------------------------------------------------------------
+  //   K: kTileK / 1 KiB DMA instructions per tile, one per wavefront w < kTileK / 1024; lane
+  //      i writes row 1024 w / D + i / kChunks at chunk position i % kChunks and loads the
+  //      logical chunk that position holds (rows past the end of the sequence read zeros);
+  //   V: wavefront w stages keys [8w, 8w+8): lane l -> keys 8w + 4hi + 0..3, dims
+  //      4(l % 32) .. + 3 (lanes past D/4 repeat the last dims), a 4 x 4 byte transpose into
+  //      V^T; rows past the end of the sequence read as zeros (their keys are masked).
+  constexpr int kKDma = kTileK / 1024;
+  constexpr int kKRowsPerDma = 1024 / D;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const unsigned row_bytes = (unsigned)kv_row_stride;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, (int)(row_bytes * (unsigned)nk), kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vp, 0, (int)(row_bytes * (unsigned)nk), kBufferWord3);
+  const int k_row_in_dma = lane / kChunks;
+  const unsigned k_lane_off = (unsigned)(k_row_in_dma * row_bytes) +
+      (unsigned)(((lane % kChunks) ^ k8swz<D>(kKRowsPerDma * wv + k_row_in_dma)) * 16);
+  auto dma_k = [&](int k0, int slot) __attribute__((always_inline)) {   // k0: first key of the tile
+    if constexpr (kKDma < kWaves) {
+      if (wv >= kKDma) return;
+    }
+    const unsigned row0 = (unsigned)(k0 + kKRowsPerDma * wv);
+    lds_byte* dst = lds_dma_dst(lds + slot * kTileK + kKRowsPerDma * wv * D);
+    dma16(krs, dst, row0 * row_bytes + k_lane_off);
+  };
+  const int v_dq = min(l32, D / 4 - 1);
+  const unsigned v_lane_off = (unsigned)v_dq * 4u + (unsigned)(4 * hi) * row_bytes;
+  unsigned vst[4];
+  auto load_v = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      vst[r] = __builtin_amdgcn_raw_buffer_load_b32(vrs, (unsigned)(k0 + 8 * wv + r) * row_bytes + v_lane_off, 0, 0);
+  };
+  // keys k0..k0+3 of a lane (k0 = 8w + 4hi, tile-relative) are bytes 32hs + e0 .. +3 of
+  // each V^T row
+  const int v_k0 = 8 * wv + 4 * hi;
+  const int v_hs = ((v_k0 & 31) & 7) >> 2, v_e0 = (v_k0 >> 5) * 16 + ((v_k0 & 31) >> 3) * 4;
+  auto store_v = [&](int slot) __attribute__((always_inline)) {
+    // 4x4 byte transpose: out[dd] = bytes (key r = 0..3) of dim 4 v_dq + dd
+    const unsigned t0 = __builtin_amdgcn_perm(vst[1], vst[0], 0x05010400u);
+    const unsigned t1 = __builtin_amdgcn_perm(vst[1], vst[0], 0x07030602u);
+    const unsigned t2 = __builtin_amdgcn_perm(vst[3], vst[2], 0x05010400u);
+    const unsigned t3 = __builtin_amdgcn_perm(vst[3], vst[2], 0x07030602u);
+    const unsigned out[4] = {__builtin_amdgcn_perm(t2, t0, 0x05040100u), __builtin_amdgcn_perm(t2, t0, 0x07060302u),
+                             __builtin_amdgcn_perm(t3, t1, 0x05040100u), __builtin_amdgcn_perm(t3, t1, 0x07060302u)};
+    unsigned char* vt = lds + kVBase + slot * kTileV;
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd) *(unsigned*)(vt + vt8_byte(4 * v_dq + dd, v_hs * 32 + v_e0)) = out[dd];
+  };
+
+  // ---- per-wavefront state ------------------------------------------------------------
+  f32x16 oacc[kDblocks];
+#pragma unroll
+  for (int i = 0; i < kDblocks; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[i][e] = 0.0f;
+  f32x16 lacc;       // sum of the stored probabilities (every element holds the lane's sum)
+#pragma unroll
+  for (int e = 0; e < 16; ++e) lacc[e] = 0.0f;
+  f32x16 sA[kKb], sB[kKb];
+  u32x4 pc[2], pn[2];        // e4m3 probabilities of the tile whose P.V is pending, and of the next
+  pc[0] = pc[1] = pn[0] = pn[1] = u32x4{0u, 0u, 0u, 0u};
+  const u32x4 ones = {0x38383838u, 0x38383838u, 0x38383838u, 0x38383838u};  // e4m3 1.0
+  // the all-ones A operand of the probability sum, read from LDS (the same 32 bytes for every
+  // lane), so that no registers hold it across the loop
+  auto psum_mfma = [&](const u32x4 (&pp)[2], const f32x16& c) __attribute__((always_inline)) {
+    const lds_byte* ob = (const lds_byte*)lds + kOnesBase;
+    return mfma_fp8(lds_load<u32x4>(ob, lane * 32), lds_load<u32x4>(ob, lane * 32 + 16), pp[0], pp[1], c);
+  };
+  float m_run = -__FLT_MAX__;
+  float l_run = 0.0f;        // float32 sum of the unrounded probabilities (for lse)
+  float mx_cur;              // maximum of the tile whose exponentials come next
+
+  // S^T MFMA i (k-step i / kKb, 32-key block i % kKb) on the K slot at ks_
+  auto s_op = [&](const lds_byte* ks_, int i, const f32x16& c, int k_sc) __attribute__((always_inline)) {
+    const int ks = i / kKb, kb = i % kKb;
+    const u32x4 a0 = lds_load<u32x4>(ks_, koff[ks][0] + kb * kKbStride);
+    const u32x4 a1 = lds_load<u32x4>(ks_, koff[ks][1] + kb * kKbStride);
+    const i32x8 av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    if constexpr (BLOCK) return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qreg[ks], c, 0, 0, 0, k_sc, 0, q_sc);
+    else return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, qreg[ks], c, 0, 0, 0, 0, 0, 0);
+  };
+  auto pv_mfma = [&](const u32x4& a0, const u32x4& a1, const u32x4 (&pp)[2], const f32x16& c, int v_sc)
+      __attribute__((always_inline)) {
+    if constexpr (BLOCK) return mfma_fp8_scaled(a0, a1, pp[0], pp[1], c, v_sc);
+    else return mfma_fp8(a0, a1, pp[0], pp[1], c);
+  };
+  auto tile_needs_mask = [&](int k0r) __attribute__((always_inline)) {
+    const int k0 = kv0 + k0r;
+    bool need = (k0 + kBc > N) || (CAUSAL && k0 + kBc - 1 > qw0);
+    if constexpr (BAND) need = need || k0 + kBc - 1 > qw0 + a.wr || k0 < qw0 + 31 - a.wl;
+    return need;
+  };
+  auto mask_tile = [&](f32x16 (&s)[kKb], int k0r) __attribute__((always_inline)) {
+    const int k0 = kv0 + k0r;
+    if (tile_needs_mask(k0r)) {
+#pragma unroll
+      for (int kb = 0; kb < kKb; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + kb * 32 + (e >> 2) * 8 + hi * 4 + (e & 3);
+          bool dead = key >= N || (CAUSAL && key > qi);
+          if constexpr (BAND) dead = dead || key > qi + a.wr || key < qi - a.wl;
+          s[kb][e] = dead ? -INFINITY : s[kb][e];
+        }
+    }
+  };
+  auto tile_max = [&](const f32x16 (&s)[kKb]) __attribute__((always_inline)) {
+    return pair_max(tree_max<kKb>(s)) * a.c;
+  };
+  // exponentials of a tile in place (float32, for lse) and their e4m3 codes into pn: dword w
+  // of the operand holds bytes e = 4w .. 4w+3 (key order of the S^T accumulator)
+  auto exponentials = [&](f32x16 (&s)[kKb]) __attribute__((always_inline)) {
+    const float shift = kOff - m_run;
+#pragma unroll
+    for (int kb = 0; kb < kKb; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) s[kb][e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], a.c, shift));
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int kb = w >> 2, i = (w & 3) * 4;
+      // both halves are written: the previous word only fills the operand
+      int d = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][i], s[kb][i + 1], (int)pn[w >> 2][w & 3], false);
+      d = __builtin_amdgcn_cvt_pk_fp8_f32(s[kb][i + 2], s[kb][i + 3], d, true);
+      pn[w >> 2][w & 3] = (unsigned)d;
+    }
+  };
+  // P.V and the probability sum of the pending tile (V^T slot vslot, V scale v_sc)
+  auto pending_pv = [&](int vslot, int v_sc) __attribute__((always_inline)) {
+    const lds_byte* vs_ = (const lds_byte*)lds + vslot * kTileV;   // voff holds kVBase
+#pragma unroll
+    for (int db = 0; db < kDblocks; ++db)
+      oacc[db] = pv_mfma(lds_load<u32x4>(vs_, voff[db][0]), lds_load<u32x4>(vs_, voff[db][1]), pc, oacc[db], v_sc);
+    lacc = psum_mfma(pc, lacc);
+  };
+
+  // One step, for tile j (scores S(j) in sc, maximum mx_cur): the rescale decision for tile
+  // j (the rare path first adds the pending P(j-1).V(j-1) under the old maximum and clears
+  // P(j-1)), then one scheduling region: the MFMAs of S(j+1) = K(j+1) Q^T, then those of
+  // P(j-1).V(j-1) and its sum, beside the exponentials and e4m3 packing of P(j), its float32
+  // row sum, the mask (MASKED_C: whether tile j+1 needs one) and maximum of S(j+1), the LDS
+  // stores of V(j) and the global loads of V(j+1). The DMA of K(j+2) goes out first.
+  auto step = [&](f32x16 (&sc)[kKb], f32x16 (&sn)[kKb], auto par_c, int j, auto masked_c)
+      __attribute__((always_inline)) {
+    constexpr int par = decltype(par_c)::value;   // j & 1
+    constexpr bool kMasked = decltype(masked_c)::value;
+    dma_k((j + 2) * kBc, par);   // K slot j&1 was last read by S(j), before the previous barrier
+    const int k_sc = BLOCK ? (int)kscale[j + 1] : 0;
+    const int v_sc = BLOCK ? (int)vscale[max(j - 1, 0)] : 0;
+    if (__builtin_amdgcn_ballot_w64(mx_cur > m_run + kTau) != 0) {
+      pending_pv(par ^ 1, v_sc);
+      pc[0] = pc[1] = u32x4{0u, 0u, 0u, 0u};
+      const float m_new = fmaxf(m_run, mx_cur);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // 0 while m_run = -FLT_MAX
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < kDblocks; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) lacc[e] *= alpha;
+    }
+    const lds_byte* ks_ = (const lds_byte*)lds + (par ^ 1) * kTileK;
+    const lds_byte* vs_ = (const lds_byte*)lds + (par ^ 1) * kTileV;    // V^T of tile j-1; voff holds kVBase
+#pragma unroll
+    for (int kb = 0; kb < kKb; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sn[kb][e] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kSOps; ++i) sn[i % kKb] = s_op(ks_, i, sn[i % kKb], k_sc);
+    exponentials(sc);
+#pragma unroll
+    for (int db = 0; db < kDblocks; ++db)
+      oacc[db] = pv_mfma(lds_load<u32x4>(vs_, voff[db][0]), lds_load<u32x4>(vs_, voff[db][1]), pc, oacc[db], v_sc);
+    lacc = psum_mfma(pc, lacc);
+    l_run += tree_sum<kKb>(sc);
+    if constexpr (kMasked) mask_tile(sn, (j + 1) * kBc);
+    mx_cur = tile_max(sn);
+    store_v(par);
+    load_v((j + 1) * kBc);
+    pc[0] = pn[0];
+    pc[1] = pn[1];
+    // MFMAs in program order, the operand reads two MFMAs ahead, the VALU work spread
+    // between them
+    constexpr int kSReads = 2;                     // LDS operand reads per S^T MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kSReads, 0);
+#pragma unroll
+    for (int i = 0; i < kSOps; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kSReads, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 80 / kSOps, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kDblocks + 1; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < kDblocks - 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 70 / (kDblocks + 1), 0);
+    }
+    // the K DMA of this step is complete (only the V loads just issued may be pending)
+    // before the barrier that publishes it
+    __builtin_amdgcn_s_waitcnt(kVmcnt4);
+  };
+
+  // prologue: K(0), K(1) in LDS, V(0) in registers, the V^T slot of the (absent) tile -1
+  // zero, S(0) computed, masked and its maximum taken
+  dma_k(0, 0);
+  dma_k(kBc, 1);
+  load_v(0);
+  {
+    unsigned char* vz = lds + kVBase + kTileV;   // slot 1: read by step 0 with P = 0
+    for (int i = tid; i < kTileV / 16; i += kThreads) *(u32x4*)(vz + i * 16) = u32x4{0u, 0u, 0u, 0u};
+    unsigned char* one = lds + kOnesBase;
+    for (int i = tid; i < 32 * kBc / 16; i += kThreads) *(u32x4*)(one + i * 16) = ones;
+  }
+  __builtin_amdgcn_s_waitcnt(kVmcnt4);
+  __syncthreads();
+  {
+    const int k_sc0 = BLOCK ? (int)kscale[0] : 0;
+    const lds_byte* ks_ = (const lds_byte*)lds;
+#pragma unroll
+    for (int kb = 0; kb < kKb; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sA[kb][e] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kSOps; ++i) sA[i % kKb] = s_op(ks_, i, sA[i % kKb], k_sc0);
+    mask_tile(sA, 0);
+    mx_cur = tile_max(sA);
+  }
+  __syncthreads();   // every wavefront has read K slot 0 before K(2) replaces it
+
+  // Tiles go in pairs of steps (an odd count gets one more, fully masked tile). Step j masks
+  // tile j+1: a pair (j, j+1) runs the unmasked body while tiles j+1 and j+2 are seen whole
+  // by every wavefront (in range and, under the causal mask, at or before the workgroup's
+  // first query), a prefix of the loop; the rest runs the masked body.
+  int clear_tiles = 0;
+  if constexpr (!BAND) {
+    const int in_range = (N - kv0) / kBc;
+    clear_tiles = CAUSAL ? min(in_range, (q0 + 1 - kv0) / kBc) : in_range;
+  }
+  int j = 0;
+  for (; j + 2 < clear_tiles; j += 2) {
+    step(sA, sB, ic<0>(), j, std::false_type{});
+    __syncthreads();
+    step(sB, sA, ic<1>(), j + 1, std::false_type{});
+    __syncthreads();
+  }
+  for (; j < ntiles; j += 2) {
+    step(sA, sB, ic<0>(), j, std::true_type{});
+    __syncthreads();
+    step(sB, sA, ic<1>(), j + 1, std::true_type{});
+    __syncthreads();
+  }
+  // the last tile's P.V (its V^T was stored by the last step, before its barrier)
+  pending_pv((j - 1) & 1, BLOCK ? (int)vscale[j - 1] : 0);
+
+  // epilogue: O = O_acc * v_descale / (sum of stored probabilities) in bf16; lse from the
+  // float32 sum of the unrounded probabilities, undoing the 2^kOff shift
+  const float l_tot = pair_sum(l_run);
+  if (qi < N) {
+    const float inv = lacc[0] > 0.0f ? a.v_scale / lacc[0] : 0.0f;
+    uint16_t* op = (uint16_t*)a.o + ((size_t)b * N + qi) * ((size_t)a.H * D) + (size_t)h * D;
+#pragma unroll
+    for (int db = 0; db < kDblocks; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dim = db * 32 + g * 8 + hi * 4;
+        u32x2 w;
+        w[0] = Bf16Ops::pack2(oacc[db][g * 4 + 0] * inv, oacc[db][g * 4 + 1] * inv);
+        w[1] = Bf16Ops::pack2(oacc[db][g * 4 + 2] * inv, oacc[db][g * 4 + 3] * inv);
+        *(u32x2*)(op + dim) = w;
+      }
+    if (hi == 0) a.lse[((size_t)b * a.H + h) * N + qi] = (m_run - kOff + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  }
+}
+
 // ---- host side -------------------------------------------------------------------------
 bool aligned(const void* p, size_t n) { return ((uintptr_t)p % n) == 0; }
 
@@ -1099,9 +1485,13 @@ fa_status launch(const FwdArgs& args, hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-template <int D, int MASK, bool BLOCK = false>
+template <int D, int MASK, bool BLOCK = false, bool QK8 = false>
 fa_status launch_fp8(const FwdArgs& args, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, MASK, BLOCK>), dim3(args.total), dim3(kThreads), 0, stream, args);
+  if constexpr (QK8) {
+    hipLaunchKernelGGL((fa_fwd_e4m3qk_kernel<D, MASK, BLOCK>), dim3(args.total), dim3(kThreads), 0, stream, args);
+  } else {
+    hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, MASK, BLOCK>), dim3(args.total), dim3(kThreads), 0, stream, args);
+  }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -1248,13 +1638,15 @@ fa_status fa_fwd_block_sparse(const void* q, const void* k, const void* v, void*
 fa_status fa_fwd_fp8_block(const void* q, const void* k, const void* v, const unsigned char* q_scales,
                            const unsigned char* k_scales, const unsigned char* v_scales, void* o,
                            float* lse, int B, int H, int Hkv, int N, int d, int causal, float scale,
-                           void* stream) {
+                           int qk_e4m3, void* stream) {
   fa_status st = check_sizes(B, H, Hkv, N, d, causal, FA_DTYPE_FP8_E4M3);
   if (st != FA_OK) return st;
   if (!q || !k || !v || !o || !lse || !q_scales || !k_scales || !v_scales) return FA_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(lse, 4))
     return FA_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  if (qk_e4m3 != 0 && qk_e4m3 != 1) return FA_ERR_INVALID_ARG;
+  if ((N + kBc - 1) / kBc > kMaxScaleTiles) return FA_ERR_UNSUPPORTED;
   FwdArgs args;
   fill_common(args, q, k, v, o, lse, B, H, Hkv, N);
   args.c = (float)((double)scale * 1.4426950408889634);
@@ -1264,6 +1656,10 @@ fa_status fa_fwd_fp8_block(const void* q, const void* k, const void* v, const un
   args.k_scales = k_scales;
   args.v_scales = v_scales;
   hipStream_t s = (hipStream_t)stream;
+  if (qk_e4m3) {
+    if (d == 128) return causal ? launch_fp8<128, kMaskCausal, true, true>(args, s) : launch_fp8<128, kMaskNone, true, true>(args, s);
+    return causal ? launch_fp8<64, kMaskCausal, true, true>(args, s) : launch_fp8<64, kMaskNone, true, true>(args, s);
+  }
   if (d == 128) return causal ? launch_fp8<128, kMaskCausal, true>(args, s) : launch_fp8<128, kMaskNone, true>(args, s);
   return causal ? launch_fp8<64, kMaskCausal, true>(args, s) : launch_fp8<64, kMaskNone, true>(args, s);
 }

@@ -48,7 +48,7 @@ def lib() -> ctypes.CDLL:
             L.fa_fwd_block_sparse.restype = c_int
             L.fa_quantize_e4m3_block.argtypes = [vp, c_int, c_int, c_int, c_int, c_int, vp, vp, vp, vp]
             L.fa_quantize_e4m3_block.restype = c_int
-            L.fa_fwd_fp8_block.argtypes = [vp] * 8 + [c_int] * 6 + [c_float, vp]
+            L.fa_fwd_fp8_block.argtypes = [vp] * 8 + [c_int] * 6 + [c_float, c_int, vp]
             L.fa_fwd_fp8_block.restype = c_int
             L.fa_bwd_workspace_bytes.argtypes = [c_int] * 3
             L.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -111,10 +111,10 @@ def fa_quantize_e4m3_block(x_ptr: int, in_dtype: int, B: int, N: int, Hx: int, d
 
 def fa_fwd_fp8_block(q_ptr: int, k_ptr: int, v_ptr: int, qs_ptr: int, ks_ptr: int, vs_ptr: int, o_ptr: int,
                      lse_ptr: int, B: int, H: int, Hkv: int, N: int, d: int, causal: int, scale: float,
-                     stream: int = 0) -> int:
+                     qk_e4m3: int = 0, stream: int = 0) -> int:
     """Direct call of fa_fwd_fp8_block with raw pointers; returns the status code."""
     return int(lib().fa_fwd_fp8_block(q_ptr, k_ptr, v_ptr, qs_ptr, ks_ptr, vs_ptr, o_ptr, lse_ptr, B, H, Hkv,
-                                      N, d, int(causal), float(scale), stream))
+                                      N, d, int(causal), float(scale), int(qk_e4m3), stream))
 
 
 def fa_bwd_workspace_bytes(B: int, H: int, N: int) -> int:
@@ -302,9 +302,11 @@ def quantize_e4m3_block(x, signs=None, codes=None, scales=None, stream=None):
 
 
 def fwd_fp8_block(q, k, v, q_scales, k_scales, v_scales, causal: bool = False, scale: float | None = None,
-                  out=None, lse=None, stream=None):
+                  out=None, lse=None, stream=None, qk_e4m3: bool = False):
     """Attention forward on block-quantised e4m3 inputs (uint8 code tensors q [B,N,H,d],
-    k and v [B,N,Hkv,d], with their E8M0 block scales). Returns (o bfloat16, lse)."""
+    k and v [B,N,Hkv,d], with their E8M0 block scales). qk_e4m3: Q K^T on the e4m3 MFMA,
+    for Q and K rotated by quantize_e4m3_block with signs (else exact bf16 products).
+    Returns (o bfloat16, lse)."""
     import torch
     B, N, H, d = q.shape
     Hkv = k.shape[2]
@@ -331,7 +333,7 @@ def fwd_fp8_block(q, k, v, q_scales, k_scales, v_scales, causal: bool = False, s
         raise ValueError("out/lse have the wrong shape or type")
     _check(fa_fwd_fp8_block(q.data_ptr(), k.data_ptr(), v.data_ptr(), q_scales.data_ptr(), k_scales.data_ptr(),
                             v_scales.data_ptr(), out.data_ptr(), lse.data_ptr(), B, H, Hkv, N, d, int(bool(causal)),
-                            scale, _stream(q, stream)))
+                            scale, int(bool(qk_e4m3)), _stream(q, stream)))
     return out, lse
 
 

@@ -159,15 +159,23 @@ fa_status fa_quantize_e4m3_block(const void* x, fa_dtype in_dtype, int B, int N,
  * times 2^(scale byte - 127) of block n / FA_FP8_BLOCK_ROWS of that (b, head).
  *   q_scales  device pointer, [B][H][nb] bytes; k_scales, v_scales [B][Hkv][nb] bytes,
  *             nb = ceil(N / FA_FP8_BLOCK_ROWS).
- * Q and K scales are applied exactly when their codes are widened to bf16 for the
- * Q K^T product; V scales are the per-tile scale operand of the scaled e4m3 P.V MFMA.
- * o is bfloat16. Otherwise as fa_fwd with dtype FP8_E4M3 (no descale argument; when Q
- * and K were rotated by the quantiser, pass scale / d).
+ *   qk_e4m3   0: Q K^T runs on the bf16 MFMA after an exact widening of the codes (times
+ *             their block scales); exact products, float32 sums, for any codes.
+ *             1: Q K^T runs on the e4m3 MFMA with the Q and K block scales as its scale
+ *             operands (about 1.2x faster). That unit sums each 64-term product with
+ *             limited internal precision, so a score moves by an amount that grows with
+ *             the largest products of its row: fine after incoherent processing (Q and K
+ *             rotated by fa_quantize_e4m3_block with signs, which spreads outliers), not
+ *             on raw codes with outliers. Any other value is FA_ERR_INVALID_ARG.
+ * V scales are the per-tile scale operand of the scaled e4m3 P.V MFMA. o is bfloat16.
+ * N <= 131072 (FA_ERR_UNSUPPORTED beyond). Otherwise as fa_fwd with dtype FP8_E4M3 (no
+ * descale argument; when Q and K were rotated by the quantiser, pass scale / d).
  */
 fa_status fa_fwd_fp8_block(const void* q, const void* k, const void* v,
                            const unsigned char* q_scales, const unsigned char* k_scales,
                            const unsigned char* v_scales, void* o, float* lse, int B, int H,
-                           int Hkv, int N, int d, int causal, float scale, void* stream);
+                           int Hkv, int N, int d, int causal, float scale, int qk_e4m3,
+                           void* stream);
 
 /*
  * Gradient of the attention forward (fa_fwd) for an upstream gradient dout of o. The

@@ -179,13 +179,16 @@ def test_quantize_rejects_before_launch(over, status):
     (dict(causal=3), fa.FA_ERR_INVALID_ARG),
     (dict(Hkv=3), fa.FA_ERR_INVALID_ARG),
     (dict(d=256), fa.FA_ERR_UNSUPPORTED),
+    (dict(qk=2), fa.FA_ERR_INVALID_ARG),
+    (dict(N=131073), fa.FA_ERR_UNSUPPORTED),                 # more key tiles than the scale cache holds
+    (dict(N=131073, qk=1), fa.FA_ERR_UNSUPPORTED),
 ])
 def test_fwd_fp8_block_rejects_before_launch(over, status):
     a = dict(q=FAKE, k=FAKE, v=FAKE, qs=FAKE, ks=FAKE, vs=FAKE, o=FAKE, lse=FAKE, B=1, H=4, Hkv=2, N=64, d=128,
-             causal=0, scale=0.1)
+             causal=0, scale=0.1, qk=0)
     a.update(over)
     st = fa.fa_fwd_fp8_block(a["q"], a["k"], a["v"], a["qs"], a["ks"], a["vs"], a["o"], a["lse"], a["B"], a["H"],
-                             a["Hkv"], a["N"], a["d"], a["causal"], a["scale"])
+                             a["Hkv"], a["N"], a["d"], a["causal"], a["scale"], a["qk"])
     assert st == status
 
 

@@ -84,12 +84,16 @@ ATTN_CASES = [
 ]
 
 
+@pytest.mark.parametrize("qk_e4m3", [False, True], ids=["qk-bf16", "qk-e4m3"])
 @pytest.mark.parametrize("case", ATTN_CASES, ids=lambda c: "-".join(map(str, c)))
-def test_block_attention_parity(case):
+def test_block_attention_parity(case, qk_e4m3):
     """Block-scaled attention on oracle-quantised codes against the oracle on their exact
-    values (e4m3 tolerance, or the derived probability-rounding bound)."""
+    values (e4m3 tolerance, or the derived probability-rounding bound), with Q K^T on the
+    bf16 MFMA (any codes) and, for Hadamard-rotated Q and K, on the e4m3 MFMA."""
     B, H, Hkv, N, d, causal, rotate = case
-    _log(f"[fp8 block attn] {case}")
+    if qk_e4m3 and not rotate:
+        pytest.skip("Q K^T on the e4m3 MFMA is specified for incoherently processed (rotated) Q and K only")
+    _log(f"[fp8 block attn] {case} qk_e4m3={qk_e4m3}")
     inp = synth_inputs.make_inputs(B, H, Hkv, N, d, "bf16", seed=1300 + N, outlier_frac=1e-3)
     signs = synth_inputs.random_signs(d, 78) if rotate else None
     scale = 1.0 / np.sqrt(d) / (d if rotate else 1)
@@ -99,7 +103,8 @@ def test_block_attention_parity(case):
     q, k, v = (oracle.block_dequantize(c, s_) for c, s_ in ((qc, qs), (kc, ks), (vc, vs)))
     o_ref, lse_ref = oracle.attn_fwd_f64(q, k, v, causal, scale)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    o, lse = fa.fwd_fp8_block(dev(qc), dev(kc), dev(vc), dev(qs), dev(ks), dev(vs), causal=causal, scale=scale)
+    o, lse = fa.fwd_fp8_block(dev(qc), dev(kc), dev(vc), dev(qs), dev(ks), dev(vs), causal=causal, scale=scale,
+                              qk_e4m3=qk_e4m3)
     torch.cuda.synchronize()
     o, lse = gu.host(o, lse)
     bound = gu.fp8_bound_from_values(q, k, v, causal, scale, o_ref)
@@ -109,11 +114,13 @@ def test_block_attention_parity(case):
          f"({int(few.sum())} elements outside the stated regime)")
 
 
-def test_scale_placement_is_exact():
+@pytest.mark.parametrize("qk_e4m3", [False, True], ids=["qk-bf16", "qk-e4m3"])
+def test_scale_placement_is_exact(qk_e4m3):
     """Moving a power of two between a tensor's codes and its block scales leaves the
-    output unchanged bit for bit (the scales are applied exactly), for Q, K and V."""
+    output unchanged bit for bit (the scales are applied exactly), for Q, K and V, with
+    either Q K^T product."""
     B, H, Hkv, N, d = 1, 2, 2, 256, 128
-    _log("[fp8 block attn] scale placement")
+    _log(f"[fp8 block attn] scale placement, qk_e4m3={qk_e4m3}")
     inp = synth_inputs.make_inputs(B, H, Hkv, N, d, "bf16", seed=1400)
     cs = []
     for n in "qkv":
@@ -122,7 +129,8 @@ def test_scale_placement_is_exact():
         c = np.where(np.abs(vals) < 2.0 ** -5, np.uint8(0), c)     # so that halving every value is exact
         cs.append((c, s_))
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    run = lambda pairs: fa.fwd_fp8_block(*(dev(x) for x, _ in pairs), *(dev(y) for _, y in pairs), scale=0.088)
+    run = lambda pairs: fa.fwd_fp8_block(*(dev(x) for x, _ in pairs), *(dev(y) for _, y in pairs), scale=0.088,
+                                         qk_e4m3=qk_e4m3)
     base = run(cs)
     for which in range(3):
         c, s_ = cs[which]
@@ -170,7 +178,8 @@ def test_fp8_error_per_tensor_block_rotated():
         qc, qs = fa.quantize_e4m3_block(qd, sg)
         kc, ks = fa.quantize_e4m3_block(kd, sg)
         vc, vs = fa.quantize_e4m3_block(vd, None)
-        o, lse = fa.fwd_fp8_block(qc, kc, vc, qs, ks, vs, scale=scale / (d if sg is not None else 1))
+        o, lse = fa.fwd_fp8_block(qc, kc, vc, qs, ks, vs, scale=scale / (d if sg is not None else 1),
+                                  qk_e4m3=sg is not None)
         results[name] = pick(o, lse)
     torch.cuda.synchronize()
     err = {}
@@ -186,7 +195,7 @@ def test_fp8_error_per_tensor_block_rotated():
 
 def test_block_workload_full_size():
     """The e4m3 workload's shape (B8 H16 N4096 d128, 0.1% x20 outliers) in the launch
-    configuration the benchmark times: the GPU quantiser's codes and scales equal the
+    configuration the benchmark times (Q K^T on the e4m3 MFMA): the GPU quantiser's codes and scales equal the
     oracle's everywhere, and the block-scaled attention matches the oracle over every
     output element (6e-2 * max(1, |O|), or the probability-rounding bound in rows outside
     the regime of that tolerance, gpu_util.RHO_MAX)."""
@@ -207,7 +216,7 @@ def test_block_workload_full_size():
         dev_codes[n] = (c, s_)
     scale = w.scale / w.d
     o, lse = fa.fwd_fp8_block(dev_codes["q"][0], dev_codes["k"][0], dev_codes["v"][0], dev_codes["q"][1],
-                              dev_codes["k"][1], dev_codes["v"][1], causal=w.causal, scale=scale)
+                              dev_codes["k"][1], dev_codes["v"][1], causal=w.causal, scale=scale, qk_e4m3=True)
     torch.cuda.synchronize()
     o_g, l_g = gu.host(o, lse)
     del o, lse
