@@ -39,6 +39,7 @@
 
 namespace {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
@@ -1082,23 +1083,35 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
 //     same sum, so each lane holds 32 consecutive bytes of its row. Q and K block scales
 //     (E8M0) go into the instruction's scale operands and are applied exactly;
 //   * O^T += V^T P^T as in the kernel above (one MFMA per 32 dims covers the tile's 64 keys),
-//     with the sum of the stored probabilities from one more MFMA against all-ones.
+//     with the sum of the stored probabilities from one 16x16x128 e4m3 MFMA of P against a
+//     0/1 selector (half the cycles of a 32x32x64 one, four accumulator registers).
 // K tiles go from global memory straight into LDS (LDS DMA) as e4m3 bytes; V passes through
 // registers and is transposed into V^T there (4 x 4 byte transposes). The workgroup and
 // schedule follow the 16-bit kernel: 8 wavefronts of 32 query rows in lockstep, two K and two
 // V^T slots, one barrier per key tile. Because one P.V MFMA consumes all 64 keys of P, P.V
 // of tile j is deferred to step j+1, where it runs beside the MFMAs of S(j+2) and the softmax
-// of tile j+1, so the softmax is spread over all nine MFMAs of a step.
+// of tile j+1, so the softmax is spread over all the MFMAs of a step.
 // The running maximum moves only when a tile's maximum exceeds it by more than kTau (the
 // maximum is taken in the step before the tile's exponentials); probabilities are stored as
 // e4m3 times 2^kOff, p <= 2^(kTau + kOff) = 2^8.5 < 448, so the bulk of them lies in
 // e4m3's normal range. O is normalised by the sum of the stored probabilities (O is a
 // convex combination of V rows); lse uses the float32 sum of the unrounded ones.
-// K tile in LDS: row r (key) of D bytes, 16-byte chunk c at c ^ k8swz(r), so that 16
-// consecutive rows read at one logical chunk hit 16 different 16-byte bank groups.
+// K tile in LDS: row r (key) of D bytes, 16-byte chunk c at c ^ k8swz(r). Any 8
+// consecutive rows read at one logical chunk hit 8 different 16-byte units of a 128-byte
+// bank window, and any 16 consecutive rows 16 different units of a 256-byte window, so the
+// S^T operand reads are free of bank conflicts whether the LDS serves 8 or 16 lanes of a
+// 16-byte read per cycle.
 template <int D>
 __device__ __forceinline__ int k8swz(int r) {
-  return D == 128 ? (r >> 1) & 7 : (r >> 2) & 3;
+  if constexpr (D == 128) return (r ^ ((r >> 3) & 3)) & 7;
+  else return ((((r >> 2) ^ (r >> 3)) & 1) << 1) | (((r >> 1) ^ (r >> 3)) & 1);
+}
+// V^T tile in LDS for the same kernel: row dim of 64 bytes, 16-byte chunk c of a row at
+// c ^ (((dim >> 1) ^ (dim >> 3)) & 3). The P.V operand reads (32 consecutive dims at one
+// chunk) are conflict-free under both lane groupings above, and so are the 4-byte stores of
+// the staging below, where each lane rotates which of its four dims it writes per store.
+__device__ __forceinline__ int vt8q_byte(int dim, int pos) {
+  return dim * 64 + ((((pos >> 4) ^ (((dim >> 1) ^ (dim >> 3)) & 3))) << 4) + (pos & 15);
 }
 constexpr int kMaxScaleTiles = 2048;            // block-scaled e4m3: N <= 131072
 
@@ -1115,12 +1128,12 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_e4m3qk_kernel(FwdArgs a) {
   constexpr int kTileK = kBc * D;                 // e4m3 K tile
   constexpr int kTileV = D * kBc;                 // e4m3 V^T tile
   constexpr int kVBase = 2 * kTileK;
-  constexpr int kOnesBase = kVBase + 2 * kTileV;  // 32 x 64 e4m3 ones: A operand of the probability sum
+  constexpr int kOnesBase = kVBase + 2 * kTileV;  // 32 bytes of e4m3 ones, 32 of zeros: A operands of the probability sum
   constexpr int kSOps = kKsteps * kKb;            // S^T MFMAs per tile
   static_assert(kBc == 64 && FA_FP8_BLOCK_ROWS == kBc, "one P.V MFMA and one block scale per key tile");
 
   // K slot 0, K slot 1, V^T slot 0, V^T slot 1, ones
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kTileK + 2 * kTileV + 32 * kBc];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kTileK + 2 * kTileV + 64];
   // block scales of the K and V tiles of this (batch, K/V head), two entries of 127 (2^0)
   // past the end
   __shared__ unsigned char kscale[BLOCK ? kMaxScaleTiles + 4 : 1];
@@ -1177,19 +1190,23 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_e4m3qk_kernel(FwdArgs a) {
 #pragma unroll
     for (int x = 0; x < 2; ++x) koff[ks][x] = l32 * D + (((4 * ks + 2 * hi + x) ^ k8swz<D>(l32)) << 4);
   constexpr int kKbStride = 32 * D;               // bytes between the 32-key blocks of a K tile
-  int voff[kDblocks][2];
+  // P.V operand reads: dim 32 db + l32, bytes 32 hi + 16 x .. + 15; the chunk swizzle of a
+  // dim does not depend on db (bits 1.. 3 of 32 db are zero), so blocks differ by 2 KiB
+  int voff[2];
 #pragma unroll
-  for (int db = 0; db < kDblocks; ++db)
-#pragma unroll
-    for (int x = 0; x < 2; ++x) voff[db][x] = kVBase + vt8_byte(db * 32 + l32, hi * 32 + x * 16);
+  for (int x = 0; x < 2; ++x) voff[x] = kVBase + vt8q_byte(l32, hi * 32 + x * 16);
+  constexpr int kVdbStride = 32 * kBc;
 
   // ---- staging ------------------------------------------------------------------------
   //   K: kTileK / 1 KiB DMA instructions per tile, one per wavefront w < kTileK / 1024; lane
   //      i writes row 1024 w / D + i / kChunks at chunk position i % kChunks and loads the
   //      logical chunk that position holds (rows past the end of the sequence read zeros);
-  //   V: wavefront w stages keys [8w, 8w+8): lane l -> keys 8w + 4hi + 0..3, dims
-  //      4(l % 32) .. + 3 (lanes past D/4 repeat the last dims), a 4 x 4 byte transpose into
-  //      V^T; rows past the end of the sequence read as zeros (their keys are masked).
+  //   V: the tile is 16 groups of 4 keys by D/64 halves of 64 dims. Wavefront w stages dim
+  //      half w % (D/64) of four groups (set s = w / (D/64) < 4; wavefronts past 4 D/64 stage
+  //      nothing): lane l takes group g = 8(s >> 1) + (s & 1) + 2(l & 3), whose keys lie in
+  //      one 16-byte chunk of each V^T row at word l & 3, and dims 64 half + 4(l >> 2) .. + 3.
+  //      A 4 x 4 byte transpose turns its four 4-byte loads into four 4-byte V^T stores; rows
+  //      past the end of the sequence read as zeros (their keys are masked).
   constexpr int kKDma = kTileK / 1024;
   constexpr int kKRowsPerDma = 1024 / D;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -1207,29 +1224,43 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_e4m3qk_kernel(FwdArgs a) {
     lds_byte* dst = lds_dma_dst(lds + slot * kTileK + kKRowsPerDma * wv * D);
     dma16(krs, dst, row0 * row_bytes + k_lane_off);
   };
-  const int v_dq = min(l32, D / 4 - 1);
-  const unsigned v_lane_off = (unsigned)v_dq * 4u + (unsigned)(4 * hi) * row_bytes;
+  constexpr int kVHalves = D / 64;
+  const bool v_stager = 4 * kVHalves >= kWaves || wv < 4 * kVHalves;   // wavefront-uniform
+  const int v_set = (wv / kVHalves) & 3, v_half = wv % kVHalves;
+  const int v_grp = 8 * (v_set >> 1) + (v_set & 1) + 2 * (lane & 3);
+  const int v_dq = lane >> 2;                     // dims 64 v_half + 4 v_dq .. + 3
+  const unsigned v_lane_off = (unsigned)(64 * v_half + 4 * v_dq) + (unsigned)(4 * v_grp) * row_bytes;
   unsigned vst[4];
   auto load_v = [&](int k0) __attribute__((always_inline)) {
+    if (!v_stager) return;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
-      vst[r] = __builtin_amdgcn_raw_buffer_load_b32(vrs, (unsigned)(k0 + 8 * wv + r) * row_bytes + v_lane_off, 0, 0);
+      vst[r] = __builtin_amdgcn_raw_buffer_load_b32(vrs, (unsigned)(k0 + r) * row_bytes + v_lane_off, 0, 0);
   };
-  // keys k0..k0+3 of a lane (k0 = 8w + 4hi, tile-relative) are bytes 32hs + e0 .. +3 of
-  // each V^T row
-  const int v_k0 = 8 * wv + 4 * hi;
-  const int v_hs = ((v_k0 & 31) & 7) >> 2, v_e0 = (v_k0 >> 5) * 16 + ((v_k0 & 31) >> 3) * 4;
+  // The keys 4g .. 4g+3 of group g are bytes 32(g & 1) + 16(g >> 3) + 4((g >> 1) & 3) .. +3
+  // of each V^T row (the key order of the P operand). Store t writes dim 4 v_dq + (t ^ rot),
+  // rot = (v_dq >> 2) & 3: the first transpose stage takes each load's bytes in that order,
+  // through per-lane byte selectors, and the address of store t is that of store 0 with bits
+  // 4..7 flipped by 64 t + 16 (t >> 1) (the dim's low bits and its chunk swizzle; the tile
+  // bases are multiples of 256).
+  const int v_rot = (v_dq >> 2) & 3;
+  const int v_pos = 32 * (v_grp & 1) + 16 * (v_grp >> 3) + 4 * ((v_grp >> 1) & 3);
+  const unsigned v_sel_lo = (unsigned)(v_rot | (4 + v_rot) << 8 | (v_rot ^ 1) << 16 | (4 + (v_rot ^ 1)) << 24);
+  const int v_st0 = vt8q_byte(64 * v_half + 4 * v_dq + v_rot, v_pos);
+  static_assert(kVBase % 256 == 0 && kTileV % 256 == 0, "V^T store addresses are formed by xor");
   auto store_v = [&](int slot) __attribute__((always_inline)) {
-    // 4x4 byte transpose: out[dd] = bytes (key r = 0..3) of dim 4 v_dq + dd
-    const unsigned t0 = __builtin_amdgcn_perm(vst[1], vst[0], 0x05010400u);
-    const unsigned t1 = __builtin_amdgcn_perm(vst[1], vst[0], 0x07030602u);
-    const unsigned t2 = __builtin_amdgcn_perm(vst[3], vst[2], 0x05010400u);
-    const unsigned t3 = __builtin_amdgcn_perm(vst[3], vst[2], 0x07030602u);
+    if (!v_stager) return;
+    // 4x4 byte transpose: out[t] = bytes (key r = 0..3) of dim 4 v_dq + (t ^ rot)
+    const unsigned v_sel_hi = v_sel_lo ^ 0x02020202u;        // dims rot ^ 2, rot ^ 3
+    const unsigned t0 = __builtin_amdgcn_perm(vst[1], vst[0], v_sel_lo);
+    const unsigned t1 = __builtin_amdgcn_perm(vst[1], vst[0], v_sel_hi);
+    const unsigned t2 = __builtin_amdgcn_perm(vst[3], vst[2], v_sel_lo);
+    const unsigned t3 = __builtin_amdgcn_perm(vst[3], vst[2], v_sel_hi);
     const unsigned out[4] = {__builtin_amdgcn_perm(t2, t0, 0x05040100u), __builtin_amdgcn_perm(t2, t0, 0x07060302u),
                              __builtin_amdgcn_perm(t3, t1, 0x05040100u), __builtin_amdgcn_perm(t3, t1, 0x07060302u)};
     unsigned char* vt = lds + kVBase + slot * kTileV;
 #pragma unroll
-    for (int dd = 0; dd < 4; ++dd) *(unsigned*)(vt + vt8_byte(4 * v_dq + dd, v_hs * 32 + v_e0)) = out[dd];
+    for (int t = 0; t < 4; ++t) *(unsigned*)(vt + (v_st0 ^ (64 * t + 16 * (t >> 1)))) = out[t];
   };
 
   // ---- per-wavefront state ------------------------------------------------------------
@@ -1238,18 +1269,27 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_e4m3qk_kernel(FwdArgs a) {
   for (int i = 0; i < kDblocks; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[i][e] = 0.0f;
-  f32x16 lacc;       // sum of the stored probabilities (every element holds the lane's sum)
+  f32x4 lacc;        // sum of the stored probabilities (every element holds the lane's sum)
 #pragma unroll
-  for (int e = 0; e < 16; ++e) lacc[e] = 0.0f;
+  for (int e = 0; e < 4; ++e) lacc[e] = 0.0f;
   f32x16 sA[kKb], sB[kKb];
   u32x4 pc[2], pn[2];        // e4m3 probabilities of the tile whose P.V is pending, and of the next
   pc[0] = pc[1] = pn[0] = pn[1] = u32x4{0u, 0u, 0u, 0u};
   const u32x4 ones = {0x38383838u, 0x38383838u, 0x38383838u, 0x38383838u};  // e4m3 1.0
-  // the all-ones A operand of the probability sum, read from LDS (the same 32 bytes for every
-  // lane), so that no registers hold it across the loop
-  auto psum_mfma = [&](const u32x4 (&pp)[2], const f32x16& c) __attribute__((always_inline)) {
-    const lds_byte* ob = (const lds_byte*)lds + kOnesBase;
-    return mfma_fp8(lds_load<u32x4>(ob, lane * 32), lds_load<u32x4>(ob, lane * 32 + 16), pp[0], pp[1], c);
+  // The probability sum runs on a 16x16x128 MFMA. Its B operand is the P operand itself:
+  // lane l (k-group G = l >> 4, column l & 15) holds the keys of query l & 31 from half l >> 5,
+  // so k-groups G and G ^ 2 of column n belong to query n + 16 (G & 1). The A operand selects
+  // k-group G for the output rows m with (m >> 2) & 1 == G & 1 (A lane l: row l & 15, k-group
+  // l >> 4, all ones or all zeros), which puts the sum of query l & 31 in the four outputs of
+  // lane l. Both kinds of A operand are read from LDS (32 bytes of ones, then 32 of zeros).
+  const int psel_off = kOnesBase + ((((lane >> 4) ^ (lane >> 2)) & 1) << 5);
+  auto psum_mfma = [&](const u32x4 (&pp)[2], const f32x4& c) __attribute__((always_inline)) {
+    const lds_byte* ob = (const lds_byte*)lds;
+    const u32x4 a0 = lds_load<u32x4>(ob, psel_off), a1 = lds_load<u32x4>(ob, psel_off + 16);
+    const i32x8 av = {(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    const i32x8 bv = {(int)pp[0][0], (int)pp[0][1], (int)pp[0][2], (int)pp[0][3],
+                      (int)pp[1][0], (int)pp[1][1], (int)pp[1][2], (int)pp[1][3]};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 0, 0, 0, 0, 0, 0);
   };
   float m_run = -__FLT_MAX__;
   float l_run = 0.0f;        // float32 sum of the unrounded probabilities (for lse)
@@ -1314,7 +1354,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_e4m3qk_kernel(FwdArgs a) {
     const lds_byte* vs_ = (const lds_byte*)lds + vslot * kTileV;   // voff holds kVBase
 #pragma unroll
     for (int db = 0; db < kDblocks; ++db)
-      oacc[db] = pv_mfma(lds_load<u32x4>(vs_, voff[db][0]), lds_load<u32x4>(vs_, voff[db][1]), pc, oacc[db], v_sc);
+      oacc[db] = pv_mfma(lds_load<u32x4>(vs_, voff[0] + db * kVdbStride), lds_load<u32x4>(vs_, voff[1] + db * kVdbStride), pc, oacc[db], v_sc);
     lacc = psum_mfma(pc, lacc);
   };
 
@@ -1343,7 +1383,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_e4m3qk_kernel(FwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) lacc[e] *= alpha;
+      for (int e = 0; e < 4; ++e) lacc[e] *= alpha;
     }
     const lds_byte* ks_ = (const lds_byte*)lds + (par ^ 1) * kTileK;
     const lds_byte* vs_ = (const lds_byte*)lds + (par ^ 1) * kTileV;    // V^T of tile j-1; voff holds kVBase
@@ -1356,7 +1396,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_e4m3qk_kernel(FwdArgs a) {
     exponentials(sc);
 #pragma unroll
     for (int db = 0; db < kDblocks; ++db)
-      oacc[db] = pv_mfma(lds_load<u32x4>(vs_, voff[db][0]), lds_load<u32x4>(vs_, voff[db][1]), pc, oacc[db], v_sc);
+      oacc[db] = pv_mfma(lds_load<u32x4>(vs_, voff[0] + db * kVdbStride), lds_load<u32x4>(vs_, voff[1] + db * kVdbStride), pc, oacc[db], v_sc);
     lacc = psum_mfma(pc, lacc);
     l_run += tree_sum<kKb>(sc);
     if constexpr (kMasked) mask_tile(sn, (j + 1) * kBc);
@@ -1395,7 +1435,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_e4m3qk_kernel(FwdArgs a) {
     unsigned char* vz = lds + kVBase + kTileV;   // slot 1: read by step 0 with P = 0
     for (int i = tid; i < kTileV / 16; i += kThreads) *(u32x4*)(vz + i * 16) = u32x4{0u, 0u, 0u, 0u};
     unsigned char* one = lds + kOnesBase;
-    for (int i = tid; i < 32 * kBc / 16; i += kThreads) *(u32x4*)(one + i * 16) = ones;
+    if (tid < 4) *(u32x4*)(one + tid * 16) = tid < 2 ? ones : u32x4{0u, 0u, 0u, 0u};
   }
   __builtin_amdgcn_s_waitcnt(kVmcnt4);
   __syncthreads();
