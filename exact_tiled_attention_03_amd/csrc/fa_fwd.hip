@@ -755,8 +755,12 @@ __device__ __forceinline__ f32x16 mfma_fp8_scaled(u32x4 a0, u32x4 a1, u32x4 b0, 
 __device__ __forceinline__ float e8m0_to_f32(unsigned byte) {
   return __uint_as_float(byte ? byte << 23 : 0x00400000u);
 }
-__device__ __forceinline__ int vt8_byte(int dim, int pos) {      // V^T tile: byte pos of a row
-  return dim * 64 + ((((pos >> 4) ^ ((dim >> 2) & 3))) << 4) + (pos & 15);
+// V^T tile of the e4m3 kernels in LDS: row dim of 64 bytes, 16-byte chunk c of a row at
+// c ^ (((dim >> 1) ^ (dim >> 3)) & 3). The P.V operand reads (32 consecutive dims at one
+// chunk) are conflict-free under both lane groupings above, and so are the 4-byte stores of
+// the staging below, where each lane rotates which of its four dims it writes per store.
+__device__ __forceinline__ int vt8q_byte(int dim, int pos) {
+  return dim * 64 + ((((pos >> 4) ^ (((dim >> 1) ^ (dim >> 3)) & 3))) << 4) + (pos & 15);
 }
 
 template <int D, int MASK, bool BLOCK>
@@ -771,9 +775,10 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
   constexpr int kTileK = kBc * D * 2;             // bf16 K tile in the layout of k_byte
   constexpr int kTileV = D * 64;                  // e4m3 V^T tile
   constexpr int kStageBytes = kTileK + kTileV;
+  constexpr int kOnesBase = 2 * kStageBytes;      // 32 bytes of e4m3 ones, 32 of zeros: A operands of the probability sum
   static_assert(kBc == 64, "one P.V MFMA covers the 64 keys of a tile");
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * kStageBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kOnesBase + 64];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -814,15 +819,20 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
   int koff[kKsteps];
 #pragma unroll
   for (int ks = 0; ks < kKsteps; ++ks) koff[ks] = k_byte<D>(l32, ks * 16 + hi * 8);
-  int voff[kDblocks][2];
+  // P.V operand reads: dim 32 db + l32, bytes 32 hi + 16 x .. + 15 of its V^T row; the
+  // chunk swizzle of a dim does not depend on db, so the blocks differ by 2 KiB
+  int voff[2];
 #pragma unroll
-  for (int db = 0; db < kDblocks; ++db)
-#pragma unroll
-    for (int x = 0; x < 2; ++x) voff[db][x] = kTileK + vt8_byte(db * 32 + l32, hi * 32 + x * 16);
+  for (int x = 0; x < 2; ++x) voff[x] = kTileK + vt8q_byte(l32, hi * 32 + x * 16);
+  constexpr int kVdbStride = 32 * kBc;
 
-  // staging: wavefront w stages keys [8w, 8w+8) of a tile
+  // staging: wavefront w stages keys [8w, 8w+8) of K, and a quarter of V
   //   K: lane l -> key 8w + l/(D/16), 16 e4m3 codes (dims 16(l%(D/16)) ..), stored as bf16;
-  //   V: lane l -> keys 8w + 4hi + 0..3, dims 4(l%32) .. +3 (4x4 bytes, transposed)
+  //   V: the tile is 16 groups of 4 keys by D/64 halves of 64 dims. Wavefront w stages dim
+  //      half w % (D/64) of four groups (set s = w / (D/64) < 4; wavefronts past 4 D/64 stage
+  //      nothing): lane l takes group g = 8(s >> 1) + (s & 1) + 2(l & 3), whose keys lie in
+  //      one 16-byte chunk of each V^T row at word l & 3, and dims 64 half + 4(l >> 2) .. + 3,
+  //      a 4 x 4 byte transpose into four 4-byte V^T stores
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const unsigned row_bytes = (unsigned)kv_row_stride;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, (int)(row_bytes * (unsigned)nk), kBufferWord3);
@@ -830,8 +840,11 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
   constexpr int kKLanes = 8 * (D / 16);           // lanes with 16 K codes
   const bool k_lane = lane < kKLanes;
   const int k_key = min(lane / (D / 16), 7), k_chunk = lane % (D / 16);
-  const bool v_lane = (l32 * 4) < D;
-  const int v_dq = min(l32, D / 4 - 1);
+  constexpr int kVHalves = D / 64;
+  const bool v_stager = 4 * kVHalves >= kWaves || wv < 4 * kVHalves;   // wavefront-uniform
+  const int v_set = (wv / kVHalves) & 3, v_half = wv % kVHalves;
+  const int v_grp = 8 * (v_set >> 1) + (v_set & 1) + 2 * (lane & 3);
+  const int v_dq = lane >> 2;                     // dims 64 v_half + 4 v_dq .. + 3
   u32x4 kst;
   unsigned vst[4];
   // block scales of the staged tiles (key tile = scale block, both FA_FP8_BLOCK_ROWS = kBc
@@ -848,24 +861,38 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
     kst = __builtin_amdgcn_raw_buffer_load_b128(krs, (unsigned)key * row_bytes + k_chunk * 16u, 0, 0);
     if constexpr (BLOCK) k_sc = a.k_scales[kv_sc0 + j];
   };
-  // the row offset of a full tile is wavefront-uniform (scalar operand), the lane's half
-  // (4 hi rows) rides in the per-lane offset; a ragged tile clamps rows per lane
-  const unsigned v_lane_off = (unsigned)v_dq * 4u + (unsigned)(4 * hi) * row_bytes;
+  // the row offset of a full tile is wavefront-uniform (scalar operand), the lane's group
+  // rides in the per-lane offset; a ragged tile clamps rows per lane
+  const unsigned v_col = (unsigned)(64 * v_half + 4 * v_dq);
+  const unsigned v_lane_off = v_col + (unsigned)(4 * v_grp) * row_bytes;
   auto load_v = [&](int j) __attribute__((always_inline)) {
     const int j0 = j * kBc;
-    if (j0 + kBc <= nk) {
+    if (v_stager) {
+      if (j0 + kBc <= nk) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vst[r] = __builtin_amdgcn_raw_buffer_load_b32(vrs, v_lane_off, (j0 + 8 * wv + r) * (int)row_bytes, 0);
-    } else {
+        for (int r = 0; r < 4; ++r)
+          vst[r] = __builtin_amdgcn_raw_buffer_load_b32(vrs, v_lane_off, (j0 + r) * (int)row_bytes, 0);
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = min(j0 + 8 * wv + 4 * hi + r, nk - 1);
-        vst[r] = __builtin_amdgcn_raw_buffer_load_b32(vrs, (unsigned)v_dq * 4u + (unsigned)key * row_bytes, 0, 0);
+        for (int r = 0; r < 4; ++r) {
+          const int key = min(j0 + 4 * v_grp + r, nk - 1);
+          vst[r] = __builtin_amdgcn_raw_buffer_load_b32(vrs, v_col + (unsigned)key * row_bytes, 0, 0);
+        }
       }
     }
     if constexpr (BLOCK) v_sc_next = a.v_scales[kv_sc0 + j];
   };
+  // The keys 4g .. 4g+3 of group g are bytes 32(g & 1) + 16(g >> 3) + 4((g >> 1) & 3) .. +3
+  // of each V^T row (the key order of the P operand). Store t writes dim 4 v_dq + (t ^ rot),
+  // rot = (v_dq >> 2) & 3: the first transpose stage takes each load's bytes in that order,
+  // through per-lane byte selectors, and the address of store t is that of store 0 with bits
+  // 4..7 flipped by 64 t + 16 (t >> 1) (the dim's low bits and its chunk swizzle; the tile
+  // bases are multiples of 256).
+  const int v_rot = (v_dq >> 2) & 3;
+  const int v_pos = 32 * (v_grp & 1) + 16 * (v_grp >> 3) + 4 * ((v_grp >> 1) & 3);
+  const unsigned v_sel_lo = (unsigned)(v_rot | (4 + v_rot) << 8 | (v_rot ^ 1) << 16 | (4 + (v_rot ^ 1)) << 24);
+  const int v_st0 = vt8q_byte(64 * v_half + 4 * v_dq + v_rot, v_pos);
+  static_assert(kTileK % 256 == 0 && kStageBytes % 256 == 0, "V^T store addresses are formed by xor");
   auto store_k = [&](int buf) __attribute__((always_inline)) {
     if (!k_lane) return;
     const float k_mult = BLOCK ? e8m0_to_f32(k_sc) : 1.0f;
@@ -878,21 +905,18 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
   };
   auto store_v = [&](int buf) __attribute__((always_inline)) {
     if constexpr (BLOCK) v_sc = v_sc_next;
-    if (!v_lane) return;
-    // 4x4 byte transpose: out[dd] = bytes (key r = 0..3) of dim 4 v_dq + dd
-    const unsigned t0 = __builtin_amdgcn_perm(vst[1], vst[0], 0x05010400u);
-    const unsigned t1 = __builtin_amdgcn_perm(vst[1], vst[0], 0x07030602u);
-    const unsigned t2 = __builtin_amdgcn_perm(vst[3], vst[2], 0x05010400u);
-    const unsigned t3 = __builtin_amdgcn_perm(vst[3], vst[2], 0x07030602u);
+    if (!v_stager) return;
+    // 4x4 byte transpose: out[t] = bytes (key r = 0..3) of dim 4 v_dq + (t ^ rot)
+    const unsigned v_sel_hi = v_sel_lo ^ 0x02020202u;        // dims rot ^ 2, rot ^ 3
+    const unsigned t0 = __builtin_amdgcn_perm(vst[1], vst[0], v_sel_lo);
+    const unsigned t1 = __builtin_amdgcn_perm(vst[1], vst[0], v_sel_hi);
+    const unsigned t2 = __builtin_amdgcn_perm(vst[3], vst[2], v_sel_lo);
+    const unsigned t3 = __builtin_amdgcn_perm(vst[3], vst[2], v_sel_hi);
     const unsigned out[4] = {__builtin_amdgcn_perm(t2, t0, 0x05040100u), __builtin_amdgcn_perm(t2, t0, 0x07060302u),
                              __builtin_amdgcn_perm(t3, t1, 0x05040100u), __builtin_amdgcn_perm(t3, t1, 0x07060302u)};
-    // keys k0..k0+3 (k0 = 8w + 4hi, tile-relative) are bytes 32hs + e0 .. +3 of each row
-    const int k0 = 8 * wv + 4 * hi;
-    const int kb = k0 >> 5, rem = k0 & 31;
-    const int hs = (rem & 7) >> 2, e0 = kb * 16 + (rem >> 3) * 4;
     unsigned char* vt = lds + buf * kStageBytes + kTileK;
 #pragma unroll
-    for (int dd = 0; dd < 4; ++dd) *(unsigned*)(vt + vt8_byte(4 * v_dq + dd, hs * 32 + e0)) = out[dd];
+    for (int t = 0; t < 4; ++t) *(unsigned*)(vt + (v_st0 ^ (64 * t + 16 * (t >> 1)))) = out[t];
   };
 
   f32x16 oacc[kDblocks];
@@ -904,12 +928,13 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
   u32x4 p[2];                // 32 e4m3 probabilities: bytes e = 0..31 as in kfp8
   p[0] = u32x4{0u, 0u, 0u, 0u};
   p[1] = u32x4{0u, 0u, 0u, 0u};
-  // sum of the stored probabilities, by the P.V MFMA against an all-ones A operand; every
-  // element holds the lane's sum
-  f32x16 lacc;
+  // sum of the stored probabilities, from a 16x16x128 MFMA of P against a 0/1 selector (as
+  // in the kernel below, psum_mfma); every element holds the lane's sum
+  f32x4 lacc;
 #pragma unroll
-  for (int e = 0; e < 16; ++e) lacc[e] = 0.0f;
+  for (int e = 0; e < 4; ++e) lacc[e] = 0.0f;
   const u32x4 ones = {0x38383838u, 0x38383838u, 0x38383838u, 0x38383838u};  // e4m3 1.0
+  const int psel_off = kOnesBase + ((((lane >> 4) ^ (lane >> 2)) & 1) << 5);
   float m_run = -__FLT_MAX__;   // as in the 16-bit kernel
   float l_run = 0.0f;        // float32 sum of the unrounded probabilities (for lse)
   auto wave_active = [&](int j) __attribute__((always_inline)) {
@@ -944,20 +969,26 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
     u32x4 a0[kDblocks], a1[kDblocks];
 #pragma unroll
     for (int db = 0; db < 2 && db < kDblocks; ++db) {
-      a0[db] = lds_load<u32x4>(st, voff[db][0]);
-      a1[db] = lds_load<u32x4>(st, voff[db][1]);
+      a0[db] = lds_load<u32x4>(st, voff[0] + db * kVdbStride);
+      a1[db] = lds_load<u32x4>(st, voff[1] + db * kVdbStride);
     }
 #pragma unroll
     for (int db = 0; db < kDblocks; ++db) {
       if (db + 2 < kDblocks) {
-        a0[db + 2] = lds_load<u32x4>(st, voff[db + 2][0]);
-        a1[db + 2] = lds_load<u32x4>(st, voff[db + 2][1]);
+        a0[db + 2] = lds_load<u32x4>(st, voff[0] + (db + 2) * kVdbStride);
+        a1[db + 2] = lds_load<u32x4>(st, voff[1] + (db + 2) * kVdbStride);
       }
       if constexpr (BLOCK) oacc[db] = mfma_fp8_scaled(a0[db], a1[db], p[0], p[1], oacc[db], v_sc);
       else oacc[db] = mfma_fp8(a0[db], a1[db], p[0], p[1], oacc[db]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    lacc = mfma_fp8(ones, ones, p[0], p[1], lacc);
+    {
+      const lds_byte* ob = (const lds_byte*)lds;
+      const u32x4 s0 = lds_load<u32x4>(ob, psel_off), s1 = lds_load<u32x4>(ob, psel_off + 16);
+      const i32x8 av = {(int)s0[0], (int)s0[1], (int)s0[2], (int)s0[3], (int)s1[0], (int)s1[1], (int)s1[2], (int)s1[3]};
+      const i32x8 bv = {(int)p[0][0], (int)p[0][1], (int)p[0][2], (int)p[0][3], (int)p[1][0], (int)p[1][1], (int)p[1][2], (int)p[1][3]};
+      lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, lacc, 0, 0, 0, 0, 0, 0);
+    }
   };
   auto mfma_block = [&](auto buf_c, int j) __attribute__((always_inline)) {
     constexpr int buf = decltype(buf_c)::value;
@@ -994,7 +1025,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[i][e] *= alpha;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) lacc[e] *= alpha;
+      for (int e = 0; e < 4; ++e) lacc[e] *= alpha;
     }
     const float shift = kOff - m_run;
     f32x16 pe[kKb];
@@ -1019,6 +1050,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
   {  // the V^T region of slot 0 (no tile -1) is zero, so step 0's P.V adds 0 * 0
     unsigned char* vz = lds + kTileK;
     for (int i = tid; i < kTileV / 16; i += kThreads) *(u32x4*)(vz + i * 16) = u32x4{0u, 0u, 0u, 0u};
+    unsigned char* one = lds + kOnesBase;
+    if (tid < 4) *(u32x4*)(one + tid * 16) = tid < 2 ? ones : u32x4{0u, 0u, 0u, 0u};
   }
   __builtin_amdgcn_s_waitcnt(0);
   if (1 < ntiles) load_k(1);
@@ -1105,13 +1138,6 @@ template <int D>
 __device__ __forceinline__ int k8swz(int r) {
   if constexpr (D == 128) return (r ^ ((r >> 3) & 3)) & 7;
   else return ((((r >> 2) ^ (r >> 3)) & 1) << 1) | (((r >> 1) ^ (r >> 3)) & 1);
-}
-// V^T tile in LDS for the same kernel: row dim of 64 bytes, 16-byte chunk c of a row at
-// c ^ (((dim >> 1) ^ (dim >> 3)) & 3). The P.V operand reads (32 consecutive dims at one
-// chunk) are conflict-free under both lane groupings above, and so are the 4-byte stores of
-// the staging below, where each lane rotates which of its four dims it writes per store.
-__device__ __forceinline__ int vt8q_byte(int dim, int pos) {
-  return dim * 64 + ((((pos >> 4) ^ (((dim >> 1) ^ (dim >> 3)) & 3))) << 4) + (pos & 15);
 }
 constexpr int kMaxScaleTiles = 2048;            // block-scaled e4m3: N <= 131072
 
