@@ -756,11 +756,11 @@ __device__ __forceinline__ float e8m0_to_f32(unsigned byte) {
   return __uint_as_float(byte ? byte << 23 : 0x00400000u);
 }
 // V^T tile of the e4m3 kernels in LDS: row dim of 64 bytes, 16-byte chunk c of a row at
-// c ^ (((dim >> 1) ^ (dim >> 3)) & 3). The P.V operand reads (32 consecutive dims at one
-// chunk) are conflict-free under both lane groupings above, and so are the 4-byte stores of
-// the staging below, where each lane rotates which of its four dims it writes per store.
+// c ^ ((dim >> 2) & 3). The P.V operand reads (32 consecutive dims at one chunk) take the
+// conflict-free time of a 16-byte read, as measured, and so do the 4-byte stores of the
+// staging below, where each lane rotates which of its four dims it writes per store.
 __device__ __forceinline__ int vt8q_byte(int dim, int pos) {
-  return dim * 64 + ((((pos >> 4) ^ (((dim >> 1) ^ (dim >> 3)) & 3))) << 4) + (pos & 15);
+  return dim * 64 + ((((pos >> 4) ^ ((dim >> 2) & 3))) << 4) + (pos & 15);
 }
 
 template <int D, int MASK, bool BLOCK>
@@ -886,8 +886,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
   // of each V^T row (the key order of the P operand). Store t writes dim 4 v_dq + (t ^ rot),
   // rot = (v_dq >> 2) & 3: the first transpose stage takes each load's bytes in that order,
   // through per-lane byte selectors, and the address of store t is that of store 0 with bits
-  // 4..7 flipped by 64 t + 16 (t >> 1) (the dim's low bits and its chunk swizzle; the tile
-  // bases are multiples of 256).
+  // 6..7 flipped by t (the dim's low bits; the chunk swizzle is the same for the four dims,
+  // and the tile bases are multiples of 256).
   const int v_rot = (v_dq >> 2) & 3;
   const int v_pos = 32 * (v_grp & 1) + 16 * (v_grp >> 3) + 4 * ((v_grp >> 1) & 3);
   const unsigned v_sel_lo = (unsigned)(v_rot | (4 + v_rot) << 8 | (v_rot ^ 1) << 16 | (4 + (v_rot ^ 1)) << 24);
@@ -916,7 +916,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_fp8_kernel(FwdArgs a) {
                              __builtin_amdgcn_perm(t3, t1, 0x05040100u), __builtin_amdgcn_perm(t3, t1, 0x07060302u)};
     unsigned char* vt = lds + buf * kStageBytes + kTileK;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) *(unsigned*)(vt + (v_st0 ^ (64 * t + 16 * (t >> 1)))) = out[t];
+    for (int t = 0; t < 4; ++t) *(unsigned*)(vt + (v_st0 ^ (64 * t))) = out[t];
   };
 
   f32x16 oacc[kDblocks];
@@ -1267,8 +1267,8 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_e4m3qk_kernel(FwdArgs a) {
   // of each V^T row (the key order of the P operand). Store t writes dim 4 v_dq + (t ^ rot),
   // rot = (v_dq >> 2) & 3: the first transpose stage takes each load's bytes in that order,
   // through per-lane byte selectors, and the address of store t is that of store 0 with bits
-  // 4..7 flipped by 64 t + 16 (t >> 1) (the dim's low bits and its chunk swizzle; the tile
-  // bases are multiples of 256).
+  // 6..7 flipped by t (the dim's low bits; the chunk swizzle is the same for the four dims,
+  // and the tile bases are multiples of 256).
   const int v_rot = (v_dq >> 2) & 3;
   const int v_pos = 32 * (v_grp & 1) + 16 * (v_grp >> 3) + 4 * ((v_grp >> 1) & 3);
   const unsigned v_sel_lo = (unsigned)(v_rot | (4 + v_rot) << 8 | (v_rot ^ 1) << 16 | (4 + (v_rot ^ 1)) << 24);
@@ -1286,7 +1286,7 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_e4m3qk_kernel(FwdArgs a) {
                              __builtin_amdgcn_perm(t3, t1, 0x05040100u), __builtin_amdgcn_perm(t3, t1, 0x07060302u)};
     unsigned char* vt = lds + kVBase + slot * kTileV;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) *(unsigned*)(vt + (v_st0 ^ (64 * t + 16 * (t >> 1)))) = out[t];
+    for (int t = 0; t < 4; ++t) *(unsigned*)(vt + (v_st0 ^ (64 * t))) = out[t];
   };
 
   // ---- per-wavefront state ------------------------------------------------------------
