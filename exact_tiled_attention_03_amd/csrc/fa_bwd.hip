@@ -51,6 +51,7 @@
 #include <type_traits>
 
 #include "fa.h"
+#include "fa_env.h"
 
 namespace {
 
@@ -845,16 +846,19 @@ template <typename Ops, int D, bool CAUSAL>
 fa_status launch_bwd(BwdArgs args, hipStream_t s) {
   const int rows = args.B * args.N * args.H;
   const int per_block = kThreads / (D / 8);
+  fa_env::log_launch("bwd_delta_kernel", __PRETTY_FUNCTION__, (rows + per_block - 1) / per_block, kThreads);
   hipLaunchKernelGGL((bwd_delta_kernel<Ops, D>), dim3((rows + per_block - 1) / per_block), dim3(kThreads), 0, s, args);
   if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
   BwdArgs kv = args;
   kv.tiles = (args.N + kKeysPerWaveKV * kWavesKV - 1) / (kKeysPerWaveKV * kWavesKV);
   kv.total = kv.tiles * args.Hkv * args.B;
+  fa_env::log_launch("bwd_dkdv_kernel", __PRETTY_FUNCTION__, kv.total, 64 * kWavesKV);
   hipLaunchKernelGGL((bwd_dkdv_kernel<Ops, D, CAUSAL>), dim3(kv.total), dim3(64 * kWavesKV), 0, s, kv);
   if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
   BwdArgs qa = args;
   qa.tiles = (args.N + 32 * kWavesQ - 1) / (32 * kWavesQ);
   qa.total = qa.tiles * args.H * args.B;
+  fa_env::log_launch("bwd_dq_kernel", __PRETTY_FUNCTION__, qa.total, 64 * kWavesQ);
   hipLaunchKernelGGL((bwd_dq_kernel<Ops, D, CAUSAL>), dim3(qa.total), dim3(64 * kWavesQ), 0, s, qa);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

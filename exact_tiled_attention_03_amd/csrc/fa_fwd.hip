@@ -36,6 +36,7 @@
 #include <type_traits>
 
 #include "fa.h"
+#include "fa_env.h"
 
 namespace {
 
@@ -1547,6 +1548,7 @@ fa_status check_sizes(int B, int H, int Hkv, int N, int d, int causal, fa_dtype 
 
 template <typename Ops, int D, int MASK>
 fa_status launch(const FwdArgs& args, hipStream_t stream) {
+  fa_env::log_launch("fa_fwd_overlap_kernel", __PRETTY_FUNCTION__, args.total, kThreads);
   hipLaunchKernelGGL((fa_fwd_overlap_kernel<Ops, D, MASK>), dim3(args.total), dim3(kThreads), 0, stream, args);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
@@ -1554,8 +1556,10 @@ fa_status launch(const FwdArgs& args, hipStream_t stream) {
 template <int D, int MASK, bool BLOCK = false, bool QK8 = false>
 fa_status launch_fp8(const FwdArgs& args, hipStream_t stream) {
   if constexpr (QK8) {
+    fa_env::log_launch("fa_fwd_e4m3qk_kernel", __PRETTY_FUNCTION__, args.total, kThreads);
     hipLaunchKernelGGL((fa_fwd_e4m3qk_kernel<D, MASK, BLOCK>), dim3(args.total), dim3(kThreads), 0, stream, args);
   } else {
+    fa_env::log_launch("fa_fwd_fp8_kernel", __PRETTY_FUNCTION__, args.total, kThreads);
     hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, MASK, BLOCK>), dim3(args.total), dim3(kThreads), 0, stream, args);
   }
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
@@ -1713,6 +1717,7 @@ fa_status fa_fwd_fp8_block(const void* q, const void* k, const void* v, const un
   if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
   if (qk_e4m3 != 0 && qk_e4m3 != 1) return FA_ERR_INVALID_ARG;
   if ((N + kBc - 1) / kBc > kMaxScaleTiles) return FA_ERR_UNSUPPORTED;
+  if (fa_env::forced_fp8_block_qk() >= 0) qk_e4m3 = fa_env::forced_fp8_block_qk();
   FwdArgs args;
   fill_common(args, q, k, v, o, lse, B, H, Hkv, N);
   args.c = (float)((double)scale * 1.4426950408889634);

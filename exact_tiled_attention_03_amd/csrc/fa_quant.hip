@@ -26,6 +26,7 @@
 #include <cstdint>
 
 #include "fa.h"
+#include "fa_env.h"
 
 namespace {
 
@@ -156,6 +157,7 @@ __global__ __launch_bounds__(kThreads) void quantize_e4m3_block_kernel(QuantArgs
 
 template <int D, bool BF16, bool ROTATE>
 fa_status launch_quant(const QuantArgs& args, int grid, hipStream_t s) {
+  fa_env::log_launch("quantize_e4m3_block_kernel", __PRETTY_FUNCTION__, grid, kThreads);
   hipLaunchKernelGGL((quantize_e4m3_block_kernel<D, BF16, ROTATE>), dim3(grid), dim3(kThreads), 0, s, args);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

@@ -28,6 +28,7 @@
 #include <cstdint>
 
 #include "fa.h"
+#include "fa_env.h"
 
 namespace {
 
@@ -353,9 +354,11 @@ fa_status check_splitkv(int B, int H, int Hkv, int Nq, int Nk, int d, int causal
 
 template <typename Ops, int D, int RB, bool CAUSAL>
 fa_status launch_partial(const SkvArgs& args, hipStream_t s) {
+  fa_env::log_launch("splitkv_partial_kernel", __PRETTY_FUNCTION__, (args.units + 3) / 4, kThreads);
   hipLaunchKernelGGL((splitkv_partial_kernel<Ops, D, RB, CAUSAL>), dim3((args.units + 3) / 4), dim3(kThreads), 0, s, args);
   if (hipGetLastError() != hipSuccess) return FA_ERR_LAUNCH;
   const int rows = args.B * args.H * args.Nq;
+  fa_env::log_launch("splitkv_merge_kernel", __PRETTY_FUNCTION__, (rows + 3) / 4, kThreads);
   hipLaunchKernelGGL((splitkv_merge_kernel<Ops, D>), dim3((rows + 3) / 4), dim3(kThreads), 0, s, args);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

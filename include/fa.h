@@ -38,6 +38,13 @@
  * must not overlap q, k, v or each other. No workspace is needed: memory use is linear
  * in N. The library keeps no state and may be called from several threads.
  *
+ * Environment (read once, on first use):
+ *   FA_LOG=1                    every launch prints "fa: <kernel> [<template arguments>]
+ *                               grid <workgroups> block <threads>" to stderr;
+ *   FA_FORCE_VARIANT=fp8_block_qk=bf16 | fp8_block_qk=e4m3
+ *                               overrides the qk_e4m3 argument of fa_fwd_fp8_block after
+ *                               its validation (for A/B runs of the two Q K^T paths).
+ *
  * Errors. Every precondition is checked on the host before any HIP call; on error
  * nothing is enqueued and the outputs are untouched.
  */
