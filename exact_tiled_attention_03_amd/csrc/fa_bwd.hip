@@ -323,12 +323,14 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
   // one tile of lead left the staging waiting on them)
   u32x4 rows[2][kUpt][4];
   float lse_st[2] = {0.0f, 0.0f};
-  // query tiles from the last one down, so that the workgroups of one K/V head (which
-  // start at different tiles under the causal mask) read the same Q/dO tile at about the
-  // same time and share it in L2
+  // query tiles from the last one down, the heads of the group interleaved (head fastest),
+  // so that the workgroups of one K/V head read the same Q/dO tile of the same head at
+  // about the same time and share it in L2: under the causal mask they stop at different
+  // tiles, and a head-major walk put them on different heads' rows (16 MiB per K/V head
+  // at N = 8192, four times an XCD's L2)
   auto tile_coords = [&](int t, int& h, int& q0) __attribute__((always_inline)) {
-    h = hk * a.group + t / per_head;
-    q0 = (nqt - 1 - t % per_head) * kBq;
+    h = hk * a.group + t % a.group;
+    q0 = (nqt - 1 - t / a.group) * kBq;
   };
   auto load_tile = [&](int t, auto set_c) __attribute__((always_inline)) {
     constexpr int st = decltype(set_c)::value;
