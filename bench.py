@@ -199,14 +199,26 @@ class ClockSampler:
 
 
 def run_copy():
+    """A plain device copy of known size: the reference for the HBM counters' scale, and
+    the copy rate this machine reaches, the practical ceiling of the HBM-bound kernels."""
     n = 1 << 28  # 2^28 float32 = 1 GiB read, 1 GiB written per copy
     x = torch.ones(n, device="cuda", dtype=torch.float32)
     y = torch.empty_like(x)
     for _ in range(5):
         y.copy_(x)
     torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    timed = 20
+    e0.record(stream)
+    for _ in range(timed):
+        y.copy_(x)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    s = e0.elapsed_time(e1) / timed * 1e-3
     print(json.dumps({"mode": "copy", "bytes_read_per_launch": n * 4, "bytes_written_per_launch": n * 4,
-                      "launches": 5}), flush=True)
+                      "launches": 5 + timed, "ms_per_copy": s * 1e3,
+                      "TBps_moved": 2 * n * 4 / s / 1e12}), flush=True)
 
 
 def main():

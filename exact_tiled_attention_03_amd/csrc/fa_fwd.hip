@@ -176,9 +176,13 @@ __device__ __forceinline__ int vt_byte(int g, int dim, int c) {
   return g * (D * 32) + dim * 32 + ((c ^ ((dim >> 3) & 1)) << 4);
 }
 
+// Maxima here use the NaN-propagating maximum (v_maximum3_f32 on gfx950): fmaxf's NaN
+// rule makes the compiler quiet each MFMA result with an extra v_max before v_max3, while
+// the two agree on every non-NaN input (masked scores are -inf, never NaN).
+__device__ __forceinline__ float max_nan(float x, float y) { return __builtin_elementwise_maximum(x, y); }
 __device__ __forceinline__ float pair_max(float x) {  // max over lanes l and l^32
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float pair_sum(float x) {  // sum over lanes l and l^32
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -201,10 +205,10 @@ __device__ __forceinline__ float tree_max(const f32x16 (&x)[KB]) {
     if (n <= 1) break;
     int m = 0;
 #pragma unroll
-    for (int i = 0; i + 2 < n; i += 3) t[m++] = fmaxf(fmaxf(t[i], t[i + 1]), t[i + 2]);
+    for (int i = 0; i + 2 < n; i += 3) t[m++] = max_nan(max_nan(t[i], t[i + 1]), t[i + 2]);
     const int rem = n % 3;
     if (rem == 1) t[m++] = t[n - 1];
-    if (rem == 2) t[m++] = fmaxf(t[n - 2], t[n - 1]);
+    if (rem == 2) t[m++] = max_nan(t[n - 2], t[n - 1]);
     n = m;
   }
   return t[0];
