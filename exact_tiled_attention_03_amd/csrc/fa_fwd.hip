@@ -630,11 +630,12 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
   // tiles go in pairs; an odd count gets one more tile, past kv_end, whose keys are all
   // masked for every query of the workgroup (probability 0)
   // Pairs of tiles that every wavefront of the workgroup sees whole (all keys in range
-  // and, under the causal mask, at or before the workgroup's first query) run the
-  // unmasked body: a prefix of the loop for the dense masks, pairs chosen at run time
+  // and, under the causal mask, at or before the workgroup's first query; under the band
+  // mask, inside every query's band) run the unmasked body: a prefix of the loop for the
+  // plain and causal masks, a middle range for the band, pairs chosen at run time
   // (uniformly for the workgroup) from the block-sparse list. The rest (the ragged end,
-  // the causal diagonal, the band, tiles some query block does not keep) run the masked
-  // one. A choice per wavefront measured 2% slower than this uniform split.
+  // the causal diagonal, the band's edges, tiles some query block does not keep) run the
+  // masked one. A choice per wavefront measured 2% slower than this uniform split.
   int j = 0;
   int e[4];
   if constexpr (BLOCKS) {
@@ -667,12 +668,29 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
     }
   } else {
     pair_entries(0, e);
-    int clear_pairs = 0;
-    if constexpr (!BAND) {
+    // tile pairs [clear_begin, clear_end) run the unmasked body
+    int clear_begin = 0, clear_end = 0;
+    if constexpr (BAND) {
+      // a tile is clear when its keys are in range and inside the band of every query of
+      // the workgroup: first key >= the last query - wl, last key <= the first query + wr
+      const int q_last = min(q0 + kBr, N) - 1;
+      const int lo = q_last - a.wl - kv0;          // offsets from kv0
+      const int hi = min(q0 + a.wr, N - 1) - kv0;
+      const int jb = lo <= 0 ? 0 : (lo + kBc - 1) / kBc;
+      const int je = hi < kBc - 1 ? 0 : (hi - (kBc - 1)) / kBc + 1;
+      clear_begin = (jb + 1) & ~1;
+      clear_end = max(clear_begin, je & ~1);
+    } else {
       const int in_range = (N - kv0) / kBc;
-      clear_pairs = (CAUSAL ? min(in_range, (q0 + 1 - kv0) / kBc) : in_range) & ~1;
+      clear_end = (CAUSAL ? min(in_range, (q0 + 1 - kv0) / kBc) : in_range) & ~1;
     }
-    for (; j < clear_pairs; j += 2) {
+    for (; j < clear_begin; j += 2) {   // the band's left edge
+      step(sA, sB, ic<0>(), j, std::true_type{}, e[0], e[2]);
+      __syncthreads();
+      step(sB, sA, ic<1>(), j + 1, std::true_type{}, e[1], e[3]);
+      __syncthreads();
+    }
+    for (; j < clear_end; j += 2) {
       step(sA, sB, ic<0>(), j, std::false_type{}, e[0], e[2]);
       __syncthreads();
       step(sB, sA, ic<1>(), j + 1, std::false_type{}, e[1], e[3]);
