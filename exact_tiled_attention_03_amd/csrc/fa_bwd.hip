@@ -392,9 +392,9 @@ __global__ __launch_bounds__(64 * kWavesKV) void bwd_dkdv_kernel(BwdArgs a) {
   };
 
   // Each 64-query tile runs as six phases whose MFMAs hide the next phase's LDS reads
-  // and the previous phase's softmax arithmetic (one wavefront per SIMD, so nothing else
-  // would): S(c,h) are the S/dP MFMAs of 16-query block h of 32-query chunk c, E(c,h) its
-  // probabilities and dS, V(c) the dV/dK MFMAs of chunk c:
+  // and the previous phase's softmax arithmetic (the other wavefront of the SIMD covers
+  // only what these leave exposed): S(c,h) are the S/dP MFMAs of 16-query block h of
+  // 32-query chunk c, E(c,h) its probabilities and dS, V(c) the dV/dK MFMAs of chunk c:
   //   S(0,0) | S(0,1) E(0,0) | S(1,0) E(0,1) | S(1,1) E(1,0) | V(0) E(1,1) | V(1) staging
   // Read bases (a tile's buffer offset plus these, formed per tile): the swizzles are XORs
   // on bits that the block offsets leave clear, so
