@@ -597,13 +597,15 @@ __global__ __launch_bounds__(kThreads) void fa_fwd_overlap_kernel(FwdArgs a) {
     pv_mfma(par);
     store_v(par ^ 1);
     load_v(k0n);
-    // P.V operand reads kLead ahead, the V staging spread between the MFMAs
+    // P.V operand reads kLeadB ahead (8 measured 0.3-0.7% faster than 4 or 6), the V
+    // staging spread between the MFMAs
     constexpr int kPOps = kDblocks * 2 * kKb;
-    __builtin_amdgcn_sched_group_barrier(0x100, kLead, 0);
+    constexpr int kLeadB = 8;
+    __builtin_amdgcn_sched_group_barrier(0x100, kLeadB, 0);
 #pragma unroll
     for (int i = 0; i < kPOps; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < kPOps - kLead) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (i < kPOps - kLeadB) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
       if (i >= 8 && i < 12) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
       if (i >= 8) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
