@@ -48,6 +48,12 @@ CASES = [
     ("bf16", 1, 2, 2, 2, 128, False, (0, 0)),
     ("bf16", 1, 2, 2, 3, 64, False, (1, 0)),
     ("bf16", 1, 2, 2, 129, 128, False, (0, 64)),
+    # windows wide enough that workgroups have a masked left edge, a range of tiles inside
+    # every query's band (the unmasked step body) and a masked right edge or diagonal
+    ("bf16", 1, 2, 2, 1300, 128, False, (300, 300)),
+    ("bf16", 1, 2, 1, 1217, 128, True, (700, -1)),
+    ("f16", 1, 2, 1, 1100, 64, True, (700, -1)),
+    ("f16", 1, 2, 2, 1000, 128, False, (450, 200)),
 ]
 
 
