@@ -81,6 +81,12 @@ ATTN_CASES = [
     (2, 4, 2, 513, 128, False, True),
     (1, 2, 1, 200, 64, True, False),
     (1, 4, 4, 129, 64, False, True),
+    # rotated shapes for the e4m3 Q K^T kernel as well: causal GQA 4:1 over several
+    # 256-query workgroups with a ragged end, d = 64 under the causal mask, a single row
+    (1, 8, 2, 1100, 128, True, True),
+    (1, 4, 2, 700, 64, True, True),
+    (2, 2, 1, 65, 64, True, True),
+    (1, 2, 2, 1, 128, False, True),
 ]
 
 
