@@ -35,6 +35,9 @@ SMALL = [
     ("f16", 1, 2, 1, 300, 128, False),
     ("bf16", 1, 8, 2, 1024, 128, True),
     ("bf16", 1, 4, 4, 640, 128, False),
+    # several 256-query workgroups with a ragged end, d = 64 and GQA
+    ("f16", 1, 8, 2, 777, 64, True),
+    ("bf16", 2, 6, 3, 513, 64, False),
 ] + [("bf16", 1, 2, 2, n, d, c) for n in (1, 2, 3, 17, 100, 129) for d in (64, 128) for c in (False, True)]
 
 
@@ -149,6 +152,7 @@ FP8_SMALL = [
     (1, 3, 1, 333, 64, False),
     (1, 3, 1, 333, 64, True),
     (1, 8, 2, 1024, 128, True),
+    (1, 4, 2, 600, 64, True),
 ] + [(1, 2, 2, n, 128, c) for n in (1, 2, 17, 100, 129) for c in (False, True)]
 
 
